@@ -1,0 +1,114 @@
+"""fp64 CPU oracle for the Gated Delta Rule-2 operator -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The HIP library never uses it, and the
+two share no code.
+
+The arithmetic lives in ``gdr2_oracle.c`` (plain C, fp64, OpenMP over the B*H
+sequences); this module only compiles it with gcc and marshals numpy arrays.
+What it computes is the token-by-token recurrence of "Gated DeltaNet-2:
+Decoupling Erase and Write in Linear Attention" (anthology record LIT-802,
+"Key takeaways", first bullet; paper Sec. 3.1 Eqs. 8-10):
+
+    S_t = (I - k_t (b_t * k_t)^T) diag(exp g_t) S_{t-1} + k_t (w_t * v_t)^T
+    o_t = S_t^T q_t          (readout after the update; a reading, see C file)
+
+and the hand-derived back-propagation through that loop.
+
+Parity status: every function here is pinned by tests in
+``tests/test_oracle_pins.py`` (reductions to KDA / Gated DeltaNet / DeltaNet
+stated on the pages, closed forms, invariants, brute force, finite
+differences).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdr2_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle into ``oracle/liboracle.so`` with gcc (-O2, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
+               "-shared", "-std=c11", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i = ctypes.c_int
+        lib.gdr2_oracle_fwd.argtypes = [i, i, i, i, i] + [dp] * 9
+        lib.gdr2_oracle_fwd.restype = None
+        lib.gdr2_oracle_bwd.argtypes = [i, i, i, i, i] + [dp] * 16
+        lib.gdr2_oracle_bwd.restype = None
+        lib.gdr2_oracle_num_threads.argtypes = []
+        lib.gdr2_oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64(a):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor
+        a = a.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def num_threads() -> int:
+    return int(_load().gdr2_oracle_num_threads())
+
+
+def fwd(q, k, v, g, b, w, h0=None):
+    """Forward recurrence in fp64.
+
+    q, k, g, b: [B, T, H, DK]; v, w: [B, T, H, DV]; h0: [B, H, DK, DV] or None.
+    Returns (o [B, T, H, DV], ht [B, H, DK, DV]).
+    """
+    q, k, v, g, b, w, h0 = (_f64(x) for x in (q, k, v, g, b, w, h0))
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    o = np.zeros((B, T, H, DV))
+    ht = np.zeros((B, H, DK, DV))
+    _load().gdr2_oracle_fwd(B, T, H, DK, DV, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
+                            _ptr(h0), _ptr(o), _ptr(ht))
+    return o, ht
+
+
+def bwd(q, k, v, g, b, w, h0, do, dht=None):
+    """Backward pass in fp64 (back-propagation through the token loop).
+
+    Returns dict with dq, dk, dv, dg, db, dw (input shapes) and dh0 [B, H, DK, DV].
+    """
+    q, k, v, g, b, w, h0, do, dht = (_f64(x) for x in (q, k, v, g, b, w, h0, do, dht))
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    out = {n: np.zeros_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("db", b), ("dw", w))}
+    out["dh0"] = np.zeros((B, H, DK, DV))
+    _load().gdr2_oracle_bwd(B, T, H, DK, DV, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
+                            _ptr(h0), _ptr(do), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]),
+                            _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["db"]), _ptr(out["dw"]),
+                            _ptr(out["dh0"]))
+    return out
