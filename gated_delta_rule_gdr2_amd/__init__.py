@@ -1,1 +1,197 @@
-"""MI355X-native Gated Delta Rule-2 operator (placeholder; binding added with the HIP library)."""
+"""MI355X-native Gated Delta Rule-2 operator: thin Python binding of libgdr2.
+
+The operator ("Gated DeltaNet-2: Decoupling Erase and Write in Linear
+Attention", anthology record LIT-802, takeaway 1; paper Sec. 3.1 Eqs. 8-10)
+
+    S_t = (I - k_t (b_t * k_t)^T) diag(exp g_t) S_{t-1} + k_t (w_t * v_t)^T
+    o_t = S_t^T q_t
+
+runs entirely in the HIP kernels of ``libgdr2.so`` (built from ``csrc/`` by
+``python -m gated_delta_rule_gdr2_amd.build``); see ``include/gdr2.h`` for the
+C ABI. This module only marshals torch tensors (device memory and the current
+HIP stream) into those calls. There is no fallback: if the library is missing
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["gdr2_fwd", "gdr2_bwd", "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes",
+           "gdr2_strerror", "gdr2_version", "GDR2Function", "library_path", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdr2.so")
+_lib = None
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+_DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
+EXPORTED = ["gdr2_fwd", "gdr2_bwd", "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes",
+            "gdr2_strerror", "gdr2_version"]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgdr2.so (raises RuntimeError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libgdr2.so not found at %s; build it with "
+                           "`python -m gated_delta_rule_gdr2_amd.build`" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.gdr2_fwd_workspace_bytes.argtypes = [i] * 8
+    lib.gdr2_fwd_workspace_bytes.restype = sz
+    lib.gdr2_bwd_workspace_bytes.argtypes = [i] * 7
+    lib.gdr2_bwd_workspace_bytes.restype = sz
+    lib.gdr2_fwd.argtypes = [vp] * 9 + [i] * 8 + [vp, sz, vp, vp]
+    lib.gdr2_fwd.restype = i
+    lib.gdr2_bwd.argtypes = [vp] * 16 + [i] * 8 + [vp, sz, vp, vp]
+    lib.gdr2_bwd.restype = i
+    lib.gdr2_strerror.argtypes = [i]
+    lib.gdr2_strerror.restype = ctypes.c_char_p
+    lib.gdr2_version.argtypes = []
+    lib.gdr2_version.restype = i
+    _lib = lib
+    return lib
+
+
+def gdr2_strerror(status: int) -> str:
+    return load_library().gdr2_strerror(int(status)).decode()
+
+
+def gdr2_version() -> int:
+    return int(load_library().gdr2_version())
+
+
+def gdr2_fwd_workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=DTYPE_BF16, save_for_bwd=False) -> int:
+    return int(load_library().gdr2_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype, int(bool(save_for_bwd))))
+
+
+def gdr2_bwd_workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=DTYPE_BF16) -> int:
+    return int(load_library().gdr2_bwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, shape):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _raise(status, what):
+    if status != 0:
+        raise RuntimeError("%s failed: %s (status %d)" % (what, gdr2_strerror(status), status))
+
+
+def _dims(q, v):
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if q.dtype not in _DT:
+        raise ValueError("unsupported dtype %s" % q.dtype)
+    return B, T, H, dk, dv, _DT[q.dtype]
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def workspace(B, T, H, dk, dv, dtype, train, device="cuda"):
+    """Allocate a workspace tensor (uint8) big enough for gdr2_fwd(save_for_bwd=train) / gdr2_bwd."""
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else dtype
+    n = gdr2_bwd_workspace_bytes(B, T, H, dk, dv, 64, dt) if train else \
+        gdr2_fwd_workspace_bytes(B, T, H, dk, dv, 64, dt, False)
+    if n == 0:
+        raise ValueError("unsupported shape/dtype for gdr2: B=%d T=%d H=%d dk=%d dv=%d" % (B, T, H, dk, dv))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def gdr2_fwd(q, k, v, g, b, w, h0=None, *, chunk=64, save_for_bwd=False, ws=None, o=None,
+             output_final_state=True, stream=None, stage_events=None):
+    """Forward pass. q, k, g, b: [B,T,H,dk]; v, w: [B,T,H,dv] (bf16 or fp32, same dtype);
+    h0: [B,H,dk,dv] fp32 or None. Returns (o, ht or None, ws). Pass ``ws`` back to
+    gdr2_bwd(..., fwd_saved=True) when save_for_bwd is set. ``stage_events``: optional
+    ctypes array of hipEvent_t handles recorded around the kernels (see include/gdr2.h)."""
+    lib = load_library()
+    B, T, H, dk, dv, dt = _dims(q, v)
+    for t, n, shp in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)), (g, "g", (B, T, H, dk)),
+                      (b, "b", (B, T, H, dk)), (v, "v", (B, T, H, dv)), (w, "w", (B, T, H, dv))):
+        _check(t, n, q.dtype, shp)
+    _check(h0, "h0", torch.float32, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty(B, T, H, dv, dtype=q.dtype, device=q.device)
+    _check(o, "o", q.dtype, (B, T, H, dv))
+    ht = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device) if output_final_state else None
+    if ws is None:
+        ws = workspace(B, T, H, dk, dv, dt, save_for_bwd, q.device)
+    st = lib.gdr2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(h0), _ptr(o), _ptr(ht),
+                      B, T, H, dk, dv, chunk, dt, int(bool(save_for_bwd)), _ptr(ws), ws.numel(), _stream(stream),
+                      stage_events)
+    _raise(st, "gdr2_fwd")
+    return o, ht, ws
+
+
+def gdr2_bwd(q, k, v, g, b, w, h0, dout, dht=None, *, chunk=64, ws=None, fwd_saved=False,
+             need_dh0=True, grads=None, stream=None, stage_events=None):
+    """Backward pass. Returns a dict with dq, dk, dv, dg, db, dw (input dtype) and dh0 (fp32 or None).
+    With fwd_saved=True, ``ws`` must be the workspace of a gdr2_fwd(..., save_for_bwd=True) call on
+    the same inputs."""
+    lib = load_library()
+    B, T, H, dk, dv, dt = _dims(q, v)
+    for t, n, shp in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)), (g, "g", (B, T, H, dk)),
+                      (b, "b", (B, T, H, dk)), (v, "v", (B, T, H, dv)), (w, "w", (B, T, H, dv)),
+                      (dout, "dout", (B, T, H, dv))):
+        _check(t, n, q.dtype, shp)
+    _check(h0, "h0", torch.float32, (B, H, dk, dv))
+    _check(dht, "dht", torch.float32, (B, H, dk, dv))
+    if grads is None:
+        grads = {n: torch.empty_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("db", b),
+                                                     ("dw", w))}
+    grads["dh0"] = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device) if need_dh0 else None
+    if ws is None:
+        if fwd_saved:
+            raise ValueError("fwd_saved=True needs the forward's workspace")
+        ws = workspace(B, T, H, dk, dv, dt, True, q.device)
+    st = lib.gdr2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(h0), _ptr(dout), _ptr(dht),
+                      _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dg"]),
+                      _ptr(grads["db"]), _ptr(grads["dw"]), _ptr(grads["dh0"]), B, T, H, dk, dv, chunk, dt,
+                      int(bool(fwd_saved)), _ptr(ws), ws.numel(), _stream(stream), stage_events)
+    _raise(st, "gdr2_bwd")
+    return grads
+
+
+class GDR2Function(torch.autograd.Function):
+    """Autograd wrapper: forward saves the per-chunk states in the workspace, backward reuses them."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, b, w, h0=None):
+        o, ht, ws = gdr2_fwd(q, k, v, g, b, w, h0, save_for_bwd=True)
+        ctx.save_for_backward(q, k, v, g, b, w, h0, ws)
+        ctx.has_h0 = h0 is not None
+        return o, ht
+
+    @staticmethod
+    def backward(ctx, do, dht):
+        q, k, v, g, b, w, h0, ws = ctx.saved_tensors
+        gr = gdr2_bwd(q, k, v, g, b, w, h0, do.contiguous(),
+                      None if dht is None else dht.contiguous(), ws=ws, fwd_saved=True,
+                      need_dh0=ctx.has_h0)
+        return gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["db"], gr["dw"], gr["dh0"]

@@ -1,0 +1,132 @@
+// C ABI of libgdr2: argument validation (host only, before any HIP call),
+// workspace sizing and kernel dispatch. See include/gdr2.h for the contract.
+#include "../../include/gdr2.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdr2_kernels.hpp"
+
+namespace {
+
+bool supported(int dk, int dv, int chunk, int dtype) {
+    if (chunk != 64) return false;
+    if (dtype == GDR2_DTYPE_BF16) return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
+    if (dtype == GDR2_DTYPE_F32) return dk == 64 && dv == 64;
+    return false;
+}
+
+int esize(int dtype) { return dtype == GDR2_DTYPE_BF16 ? 2 : 4; }
+
+bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
+    if (B < 1 || T < 1 || H < 1) return GDR2_ERR_SHAPE;
+    if (!supported(dk, dv, chunk, dtype)) return GDR2_ERR_UNSUPPORTED;
+    // element counts must fit comfortably in 64-bit offsets and the grid in 32 bits
+    const long long NT = (T + 63) / 64;
+    const long long nc = (long long)B * H * NT;
+    if (nc > 0x7fffffffLL || (long long)B * T * H > (1LL << 40)) return GDR2_ERR_SHAPE;
+    return GDR2_OK;
+}
+
+gdr2::Layout layout_for(int B, int T, int H, int dk, int dv, int dtype) {
+    const long long NT = (T + 63) / 64;
+    return gdr2::make_layout((long long)B * H * NT, dk, dv, esize(dtype));
+}
+
+void fill_common(gdr2::Args& a, int B, int T, int H, int dk, int dv, int dtype, void* ws) {
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.NT = (T + 63) / 64;
+    a.NC = (long long)B * H * a.NT;
+    a.L = layout_for(B, T, H, dk, dv, dtype);
+    a.ws = (char*)ws;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdr2_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype, int save_for_bwd) {
+    if (check_shape(B, T, H, dk, dv, chunk, dtype) != GDR2_OK) return 0;
+    gdr2::Layout L = layout_for(B, T, H, dk, dv, dtype);
+    return save_for_bwd ? L.train_bytes : L.fwd_infer_bytes;
+}
+
+size_t gdr2_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
+    if (check_shape(B, T, H, dk, dv, chunk, dtype) != GDR2_OK) return 0;
+    return layout_for(B, T, H, dk, dv, dtype).train_bytes;
+}
+
+int gdr2_fwd(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+             const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+             int save_for_bwd, void* workspace, size_t workspace_bytes, void* stream,
+             void* const* stage_events) {
+    if (!q || !k || !v || !g || !b || !w || !o) return GDR2_ERR_NULL;
+    int st = check_shape(B, T, H, dk, dv, chunk, dtype);
+    if (st != GDR2_OK) return st;
+    const void* ptrs[] = {q, k, v, g, b, w, h0, o, ht, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned(p)) return GDR2_ERR_ALIGN;
+    const size_t need = gdr2_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype, save_for_bwd);
+    if (!workspace || workspace_bytes < need) return GDR2_ERR_WORKSPACE;
+
+    gdr2::Args a = {};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.b = b; a.w = w;
+    a.h0 = h0; a.o = o; a.ht = ht;
+    fill_common(a, B, T, H, dk, dv, dtype, workspace);
+    a.events = (hipEvent_t const*)stage_events;
+    hipError_t e = gdr2::launch_fwd(a, dtype == GDR2_DTYPE_BF16, save_for_bwd != 0, (hipStream_t)stream);
+    return e == hipSuccess ? GDR2_OK : GDR2_ERR_HIP;
+}
+
+int gdr2_bwd(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+             const float* h0, const void* dout, const float* dht, void* dq, void* dk_, void* dv_, void* dg,
+             void* db, void* dw, float* dh0, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+             int fwd_saved, void* workspace, size_t workspace_bytes, void* stream,
+             void* const* stage_events) {
+    if (!q || !k || !v || !g || !b || !w || !dout || !dq || !dk_ || !dv_ || !dg || !db || !dw)
+        return GDR2_ERR_NULL;
+    int st = check_shape(B, T, H, dk, dv, chunk, dtype);
+    if (st != GDR2_OK) return st;
+    const void* ptrs[] = {q, k, v, g, b, w, h0, dout, dht, dq, dk_, dv_, dg, db, dw, dh0, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned(p)) return GDR2_ERR_ALIGN;
+    const size_t need = gdr2_bwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype);
+    if (!workspace || workspace_bytes < need) return GDR2_ERR_WORKSPACE;
+
+    gdr2::Args a = {};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.b = b; a.w = w;
+    a.h0 = h0; a.dout = dout; a.dht = dht;
+    a.dq = dq; a.dk = dk_; a.dv = dv_; a.dg = dg; a.db = db; a.dw = dw; a.dh0 = dh0;
+    a.o = nullptr; a.ht = nullptr;
+    fill_common(a, B, T, H, dk, dv, dtype, workspace);
+    const bool bf = dtype == GDR2_DTYPE_BF16;
+    hipError_t e = hipSuccess;
+    a.events = (hipEvent_t const*)stage_events;
+    if (!fwd_saved) {
+        e = gdr2::launch_fwd(a, bf, true, (hipStream_t)stream);
+        if (a.events) a.events += 2;  // the backward kernels record after the two forward ones
+    }
+    if (e == hipSuccess) e = gdr2::launch_bwd(a, bf, (hipStream_t)stream);
+    return e == hipSuccess ? GDR2_OK : GDR2_ERR_HIP;
+}
+
+const char* gdr2_strerror(int status) {
+    switch (status) {
+        case GDR2_OK: return "ok";
+        case GDR2_ERR_NULL: return "a required pointer is NULL";
+        case GDR2_ERR_SHAPE: return "invalid shape (B, T and H must be >= 1; sizes must fit)";
+        case GDR2_ERR_UNSUPPORTED: return "unsupported dk/dv/chunk/dtype combination";
+        case GDR2_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case GDR2_ERR_WORKSPACE: return "workspace is NULL or too small";
+        case GDR2_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int gdr2_version(void) { return 100; }
+
+}  // extern "C"

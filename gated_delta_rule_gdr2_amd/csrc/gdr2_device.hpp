@@ -1,0 +1,228 @@
+// Device-side building blocks for the Gated Delta Rule-2 kernels (gfx950 / CDNA4).
+//
+// MFMA conventions used by every kernel in this library
+// -----------------------------------------------------
+// All products are built from 16x16 output tiles with 32-deep K blocks:
+//   bf16 operands : one v_mfma_f32_16x16x32_bf16 per K block,
+//   fp32 operands : eight v_mfma_f32_16x16x4_f32 per K block.
+// A wave holds an operand "fragment" of 8 elements per lane. Lane l = li + 16*lq
+// (li = l % 16, lq = l / 16) holds, for an A operand, row li and the 8 K indices
+//     kmap(lq, e) = 16*(e/4) + 4*lq + (e%4),   e = 0..7,
+// and for a B operand column li with the same 8 K indices. The hardware sums
+// over (lane group, element) pairs, so any K numbering is exact as long as A and
+// B agree; this one is chosen because it matches the accumulator layout:
+// an accumulator tile D (16x16, 4 fp32 per lane) holds D[4*lq + i][li], i = 0..3.
+// Hence two vertically stacked accumulator tiles (rows 0..15 and 16..31 of a
+// 32-row block) ARE, element for element, the B fragment of that 32-row block,
+// and also the A fragment of its transpose. Sequential chains therefore keep
+// their state in accumulator registers and feed it straight back into the next
+// MFMA without any LDS round trip.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr2 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int CH = 64;    // chunk length (tokens)
+constexpr int BLK = 16;   // sub-block for the exponent split and the blocked inverse
+constexpr int NBLK = CH / BLK;
+constexpr int NPAIR = NBLK * (NBLK + 1) / 2;  // lower-triangular 16x16 block pairs
+
+template <class OT> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 type; };
+template <> struct Frag<float> { typedef f32x8 type; };
+
+__device__ __forceinline__ int kmap(int lq, int e) { return 16 * (e >> 2) + 4 * lq + (e & 3); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// pair index -> (R, I), I <= R, in the order (0,0),(1,0),(1,1),(2,0),...
+__device__ __forceinline__ void pair_ri(int p, int& R, int& I) {
+    R = (p >= 6) ? 3 : (p >= 3) ? 2 : (p >= 1) ? 1 : 0;
+    I = p - R * (R + 1) / 2;
+}
+__device__ __host__ __forceinline__ int pair_id(int R, int I) { return R * (R + 1) / 2 + I; }
+
+// ----------------------------------------------------------------------------- MMA
+__device__ __forceinline__ void mma(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+}
+// fp32 product with a 16-deep K (the first half of the K-slot map: k = 4*lq + e)
+__device__ __forceinline__ void mma_k16_f32(f32x4& acc, const float a[4], const float b[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+}
+
+// ----------------------------------------------------------------------------- conversions
+template <class OT> __device__ __forceinline__ OT to_ot(float x);
+template <> __device__ __forceinline__ bf16 to_ot<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float to_ot<float>(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+
+// fragment from two accumulator tiles (rows 0..15 -> e 0..3, rows 16..31 -> e 4..7)
+template <class OT>
+__device__ __forceinline__ typename Frag<OT>::type frag_of(const f32x4& d0, const f32x4& d1) {
+    typename Frag<OT>::type f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i] = to_ot<OT>(d0[i]);
+        f[4 + i] = to_ot<OT>(d1[i]);
+    }
+    return f;
+}
+
+// ----------------------------------------------------------------------------- 4-element vectors
+// load / store 4 consecutive elements (8 B for bf16, 16 B for fp32); p must be aligned
+__device__ __forceinline__ void ld4(const bf16* p, float out[4]) {
+    bf16x4 v = *(const bf16x4*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = (float)v[i];
+}
+__device__ __forceinline__ void ld4(const float* p, float out[4]) {
+    f32x4 v = *(const f32x4*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = v[i];
+}
+__device__ __forceinline__ void st4(bf16* p, const float in[4]) {
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (bf16)in[i];
+    *(bf16x4*)p = v;
+}
+__device__ __forceinline__ void st4(float* p, const float in[4]) {
+    f32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = in[i];
+    *(f32x4*)p = v;
+}
+
+// ----------------------------------------------------------------------------- fragment loads
+// "rowk": lane (li, lq) reads X[row0 + li][k0 + kmap(lq, e)] -- contiguous along K
+// (two runs of four). X is row-major with leading dimension ld (elements).
+template <class OT>
+__device__ __forceinline__ typename Frag<OT>::type frag_rowk(const OT* X, int ld, int row0, int k0) {
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    const OT* p = X + (size_t)(row0 + li) * ld + k0 + 4 * lq;
+    typename Frag<OT>::type f;
+    float a[4], b[4];
+    ld4(p, a);
+    ld4(p + 16, b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i] = to_ot<OT>(a[i]);
+        f[4 + i] = to_ot<OT>(b[i]);
+    }
+    return f;
+}
+// rowk from an fp32 matrix, converted to the operand type
+template <class OT>
+__device__ __forceinline__ typename Frag<OT>::type frag_rowk_f32(const float* X, int ld, int row0, int k0) {
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    const float* p = X + (size_t)(row0 + li) * ld + k0 + 4 * lq;
+    typename Frag<OT>::type f;
+    float a[4], b[4];
+    ld4(p, a);
+    ld4(p + 16, b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i] = to_ot<OT>(a[i]);
+        f[4 + i] = to_ot<OT>(b[i]);
+    }
+    return f;
+}
+// rowk with a per-K-index scale (scale[k0 + kmap] multiplies element e)
+template <class OT, class XT>
+__device__ __forceinline__ typename Frag<OT>::type frag_rowk_scaled(const XT* X, int ld, int row0, int k0,
+                                                                    const float* scale) {
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    const XT* p = X + (size_t)(row0 + li) * ld + k0 + 4 * lq;
+    const float* s = scale + k0 + 4 * lq;
+    typename Frag<OT>::type f;
+    float a[4], b[4], sa[4], sb[4];
+    ld4(p, a);
+    ld4(p + 16, b);
+    ld4(s, sa);
+    ld4(s + 16, sb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i] = to_ot<OT>(a[i] * sa[i]);
+        f[4 + i] = to_ot<OT>(b[i] * sb[i]);
+    }
+    return f;
+}
+// "colk": lane (li, lq) reads X[k0 + kmap(lq, e)][col0 + li] -- strided along K.
+// rs0 / rs1 scale the elements of the first / second 16-row half of the K block.
+template <class OT, class XT>
+__device__ __forceinline__ typename Frag<OT>::type frag_colk(const XT* X, int ld, int col0, int k0,
+                                                             float rs0 = 1.f, float rs1 = 1.f) {
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    const XT* p = X + (size_t)(k0 + 4 * lq) * ld + col0 + li;
+    typename Frag<OT>::type f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i] = to_ot<OT>(to_f(p[(size_t)i * ld]) * rs0);
+        f[4 + i] = to_ot<OT>(to_f(p[(size_t)(16 + i) * ld]) * rs1);
+    }
+    return f;
+}
+
+// ----------------------------------------------------------------------------- global fragments
+// A fragment block (one 16x32 operand) is stored lane-major: 64 lanes x 8 elements.
+template <class OT>
+__device__ __forceinline__ void store_frag(OT* base, const typename Frag<OT>::type& f) {
+    *(typename Frag<OT>::type*)(base + lane_id() * 8) = f;
+}
+template <class OT>
+__device__ __forceinline__ typename Frag<OT>::type load_frag(const OT* base) {
+    return *(const typename Frag<OT>::type*)(base + lane_id() * 8);
+}
+// accumulator tile dump: 64 lanes x 4 elements
+template <class OT>
+__device__ __forceinline__ void store_tile(OT* base, const f32x4& d) {
+    float t[4] = {d[0], d[1], d[2], d[3]};
+    st4(base + lane_id() * 4, t);
+}
+template <class OT>
+__device__ __forceinline__ f32x4 load_tile(const OT* base) {
+    float t[4];
+    ld4(base + lane_id() * 4, t);
+    f32x4 d = {t[0], t[1], t[2], t[3]};
+    return d;
+}
+
+// ----------------------------------------------------------------------------- wave scans
+// inclusive prefix sum across the 16 lanes of each DPP row (lanes li = 0..15)
+__device__ __forceinline__ float row_scan16(float x) {
+    int v;
+    v = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __int_as_float(v);
+    v = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __int_as_float(v);
+    v = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __int_as_float(v);
+    v = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __int_as_float(v);
+    return x;
+}
+// value held by lane (src_li, same lq) of the caller's 16-lane row
+__device__ __forceinline__ float row_bcast(float x, int src_li) {
+    const int l = lane_id();
+    return __shfl(x, (l & ~15) | src_li, 64);
+}
+// sum over the 16 lanes of a row (result in every lane of the row)
+__device__ __forceinline__ float row_sum16(float x) {
+    float s = row_scan16(x);
+    return row_bcast(s, 15);
+}
+
+}  // namespace gdr2

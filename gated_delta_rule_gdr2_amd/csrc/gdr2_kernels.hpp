@@ -1,0 +1,38 @@
+// Kernel arguments and launcher declarations (internal to libgdr2).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "gdr2_layout.hpp"
+
+namespace gdr2 {
+
+struct Args {
+    // inputs, [B, T, H, D] row-major in the operand type
+    const void *q, *k, *v, *g, *b, *w;
+    const float* h0;    // [B, H, DK, DV] or null
+    const void* dout;   // [B, T, H, DV]
+    const float* dht;   // [B, H, DK, DV] or null
+    // outputs
+    void* o;            // [B, T, H, DV] or null (forward recompute inside the backward)
+    float* ht;          // [B, H, DK, DV] or null
+    void *dq, *dk, *dv, *dg, *db, *dw;
+    float* dh0;         // [B, H, DK, DV] or null
+    char* ws;           // workspace base
+    Layout L;
+    int B, T, H, NT;
+    long long NC;       // B * H * NT chunks
+    hipEvent_t const* events;  // optional: recorded before the first and after each kernel
+};
+
+// record events[i] on the stream when per-kernel timing was requested
+inline hipError_t mark(const Args& a, int i, hipStream_t stream) {
+    return a.events ? hipEventRecord(a.events[i], stream) : hipSuccess;
+}
+
+// Launchers: enqueue on `stream`, return hipSuccess or the launch error.
+hipError_t launch_fwd(const Args& a, bool bf16, bool train, hipStream_t stream);
+hipError_t launch_bwd(const Args& a, bool bf16, hipStream_t stream);
+size_t fwd_intra_lds_bytes(int DK, int DV, int esz);
+size_t bwd_intra_lds_bytes(int DK, int DV, int esz);
+
+}  // namespace gdr2

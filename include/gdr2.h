@@ -1,0 +1,107 @@
+/*
+ * gdr2.h -- C ABI of libgdr2, the MI355X (gfx950) implementation of the
+ * Gated Delta Rule-2 sequence-mixing operator.
+ *
+ * Operator ("Gated DeltaNet-2: Decoupling Erase and Write in Linear
+ * Attention", anthology record LIT-802, "Key takeaways", first bullet; paper
+ * Sec. 3.1, Eqs. 8-10), for every batch row b and head h independently:
+ *
+ *     S_t = (I - k_t (b_t * k_t)^T) diag(exp g_t) S_{t-1} + k_t (w_t * v_t)^T
+ *     o_t = S_t^T q_t                        (readout after the update)
+ *
+ * b_t is the channel-wise erase gate on the key axis, w_t the channel-wise
+ * write gate on the value axis, g_t the channel-wise log-decay on the key axis
+ * (alpha_t = exp g_t). The gates arrive already activated and nothing is
+ * normalised or scaled inside the operator. The forward pass runs the
+ * chunkwise algorithm with the cumulative decay folded into asymmetric erase
+ * factors and one shared WY/UT inverse (LIT-802 takeaway 2, App. A); the
+ * backward pass is the gate-aware one (App. B).
+ *
+ * Layouts (all contiguous, row-major, in the element type `dtype`):
+ *   q, k, g, b and dq, dk, dg, db : [B][T][H][dk]
+ *   v, w, o, dout and dv, dw      : [B][T][H][dv]
+ *   h0, ht, dht, dh0              : [B][H][dk][dv], always fp32
+ * Supported: dtype BF16 with dk, dv in {64, 128}; dtype F32 with dk = dv = 64;
+ * chunk = 64; any T >= 1 (a partial last chunk is padded with zero tokens,
+ * which leave the recurrence unchanged).
+ *
+ * Ownership: the caller owns every buffer, including the workspace. All device
+ * pointers must stay valid until the stream has passed the enqueued work. The
+ * library allocates nothing, keeps no state between calls, never synchronises
+ * and enqueues everything on `stream` (a hipStream_t, 0 = null stream). Calls on
+ * different streams with different workspaces may run concurrently.
+ *
+ * Errors: every argument is checked on the host before any HIP call; a failed
+ * check returns a negative status and enqueues nothing. A failed launch
+ * returns GDR2_ERR_HIP. Non-finite inputs are not checked; they propagate.
+ */
+#ifndef GDR2_H
+#define GDR2_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gdr2_dtype { GDR2_DTYPE_F32 = 0, GDR2_DTYPE_BF16 = 1 };
+
+enum gdr2_status {
+    GDR2_OK = 0,
+    GDR2_ERR_NULL = -1,        /* a required pointer is NULL */
+    GDR2_ERR_SHAPE = -2,       /* B, T or H < 1, or sizes overflow */
+    GDR2_ERR_UNSUPPORTED = -3, /* dk/dv/chunk/dtype combination not built */
+    GDR2_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+    GDR2_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
+    GDR2_ERR_HIP = -6          /* a HIP launch failed */
+};
+
+/* Bytes of workspace gdr2_fwd needs. save_for_bwd = 1 sizes it for a later
+ * gdr2_bwd(..., fwd_saved = 1) on the same buffer. Returns 0 for unsupported
+ * or invalid arguments. */
+size_t gdr2_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype,
+                                int save_for_bwd);
+
+/* Bytes of workspace gdr2_bwd needs (either value of fwd_saved). */
+size_t gdr2_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);
+
+/* Forward pass: writes o and, if ht != NULL, the final state.
+ * h0: initial state or NULL (= 0). save_for_bwd = 1 also keeps in the
+ * workspace what gdr2_bwd needs (per-chunk states and operands), so the
+ * backward does not recompute the forward. */
+int gdr2_fwd(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+             const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk,
+             int dtype, int save_for_bwd, void* workspace, size_t workspace_bytes, void* stream,
+             void* const* stage_events);
+
+/* Backward pass: given dout (= dL/do) and dht (= dL/dS_T, NULL = 0), writes
+ * dq, dk_, dv_, dg, db, dw (same layouts and dtype as the inputs) and, if
+ * dh0 != NULL, dL/dh0. fwd_saved = 1: the workspace holds what
+ * gdr2_fwd(..., save_for_bwd = 1) left there for the same inputs and has not
+ * been touched since; fwd_saved = 0: the forward quantities are recomputed
+ * inside this call (o is not written). */
+int gdr2_bwd(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+             const float* h0, const void* dout, const float* dht, void* dq, void* dk_, void* dv_,
+             void* dg, void* db, void* dw, float* dh0, int B, int T, int H, int dk, int dv, int chunk,
+             int dtype, int fwd_saved, void* workspace, size_t workspace_bytes, void* stream,
+             void* const* stage_events);
+
+/* stage_events (both calls): NULL, or an array of hipEvent_t that the call
+ * records on `stream` around its kernels, for per-kernel timing: element 0
+ * before the first kernel and element i after the i-th kernel. gdr2_fwd runs
+ * 2 kernels (intra-chunk, state chain), so it needs 3 events; gdr2_bwd runs
+ * 2 kernels (reverse state chain, intra-chunk gradients) when fwd_saved = 1,
+ * and 4 (the two forward kernels first) when fwd_saved = 0, so it needs 3 or 5.
+ * The events belong to the caller. */
+
+/* Static description of a status code. */
+const char* gdr2_strerror(int status);
+
+/* Library version as an integer (major * 10000 + minor * 100 + patch). */
+int gdr2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR2_H */

@@ -1,0 +1,140 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/gdr2.h declares, sizes workspaces, and rejects bad
+arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_gdr2_amd as g2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr2.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(g2.library_path()):
+        from gated_delta_rule_gdr2_amd import build
+        build.build()
+    return g2.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr2_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_exported_api():
+    assert declared_functions() == sorted(g2.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # the dynamic symbol table holds them as plain C names
+    out = os.popen("nm -D --defined-only %s" % g2.library_path()).read()
+    for name in declared_functions():
+        assert re.search(r"\bT %s$" % name, out, flags=re.M), name
+
+
+def test_version_and_strerror(lib):
+    assert g2.gdr2_version() >= 100
+    for st in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_HIP):
+        assert g2.gdr2_strerror(st) and g2.gdr2_strerror(st) != "unknown status"
+    assert g2.gdr2_strerror(-99) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    BF = g2.DTYPE_BF16
+    a = g2.gdr2_fwd_workspace_bytes(2, 4096, 16, 128, 128, 64, BF, False)
+    b = g2.gdr2_fwd_workspace_bytes(2, 4096, 16, 128, 128, 64, BF, True)
+    c = g2.gdr2_bwd_workspace_bytes(2, 4096, 16, 128, 128, 64, BF)
+    assert 0 < a < b == c
+    # tail chunk rounds up
+    assert g2.gdr2_fwd_workspace_bytes(1, 65, 1, 64, 64, 64, BF, False) == \
+        g2.gdr2_fwd_workspace_bytes(1, 128, 1, 64, 64, 64, BF, False)
+    # unsupported -> 0
+    assert g2.gdr2_fwd_workspace_bytes(1, 64, 1, 96, 64, 64, BF, False) == 0
+    assert g2.gdr2_fwd_workspace_bytes(1, 64, 1, 64, 64, 32, BF, False) == 0
+    assert g2.gdr2_fwd_workspace_bytes(1, 64, 1, 128, 128, 64, g2.DTYPE_F32, False) == 0
+    assert g2.gdr2_fwd_workspace_bytes(0, 64, 1, 64, 64, 64, BF, False) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def fwd(lib, ptrs=None, B=1, T=64, H=1, dk=64, dv=64, chunk=64, dtype=g2.DTYPE_BF16, save=0,
+        ws=FAKE, ws_bytes=1 << 40):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    return lib.gdr2_fwd(*[ctypes.c_void_p(x) for x in p], B, T, H, dk, dv, chunk, dtype, save,
+                        ctypes.c_void_p(ws), ws_bytes, None, None)
+
+
+def bwd(lib, ptrs=None, B=1, T=64, H=1, dk=64, dv=64, chunk=64, dtype=g2.DTYPE_BF16, saved=1,
+        ws=FAKE, ws_bytes=1 << 40):
+    p = [FAKE] * 16 if ptrs is None else ptrs
+    return lib.gdr2_bwd(*[ctypes.c_void_p(x) for x in p], B, T, H, dk, dv, chunk, dtype, saved,
+                        ctypes.c_void_p(ws), ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("idx", range(8))
+def test_fwd_rejects_null_required_pointers(lib, idx):
+    # q k v g b w h0 o ht: h0 (6) and ht (8) are optional
+    required = [0, 1, 2, 3, 4, 5, 7]
+    if idx >= len(required):
+        return
+    p = [FAKE] * 9
+    p[required[idx]] = 0
+    assert fwd(lib, p) == ERR_NULL
+
+
+def test_bwd_rejects_null_required_pointers(lib):
+    # q k v g b w h0 dout dht dq dk dv dg db dw dh0: h0 (6), dht (8), dh0 (15) optional
+    for i in [0, 1, 2, 3, 4, 5, 7, 9, 10, 11, 12, 13, 14]:
+        p = [FAKE] * 16
+        p[i] = 0
+        assert bwd(lib, p) == ERR_NULL, i
+
+
+def test_shape_and_support_errors(lib):
+    assert fwd(lib, B=0) == ERR_SHAPE
+    assert fwd(lib, T=0) == ERR_SHAPE
+    assert fwd(lib, H=-1) == ERR_SHAPE
+    assert fwd(lib, dk=96) == ERR_UNSUP
+    assert fwd(lib, dv=32) == ERR_UNSUP
+    assert fwd(lib, chunk=32) == ERR_UNSUP
+    assert fwd(lib, dtype=7) == ERR_UNSUP
+    assert fwd(lib, dk=128, dv=128, dtype=g2.DTYPE_F32) == ERR_UNSUP
+    assert bwd(lib, dk=48) == ERR_UNSUP
+
+
+def test_alignment_errors(lib):
+    for i in range(9):
+        p = [FAKE] * 9
+        p[i] = FAKE + 2
+        assert fwd(lib, p) == ERR_ALIGN, i
+    assert fwd(lib, ws=FAKE + 8) == ERR_ALIGN
+    p = [FAKE] * 16
+    p[15] = FAKE + 4
+    assert bwd(lib, p) == ERR_ALIGN
+
+
+def test_workspace_errors(lib):
+    need = g2.gdr2_fwd_workspace_bytes(1, 64, 1, 64, 64, 64, g2.DTYPE_BF16, False)
+    assert fwd(lib, ws_bytes=need - 1) == ERR_WS
+    assert fwd(lib, ws=0) == ERR_WS
+    need_t = g2.gdr2_fwd_workspace_bytes(1, 64, 1, 64, 64, 64, g2.DTYPE_BF16, True)
+    assert fwd(lib, save=1, ws_bytes=need_t - 1) == ERR_WS
+    assert bwd(lib, ws_bytes=g2.gdr2_bwd_workspace_bytes(1, 64, 1, 64, 64, 64, g2.DTYPE_BF16) - 1) == ERR_WS
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(g2, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(g2, "_lib", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        g2.load_library()
