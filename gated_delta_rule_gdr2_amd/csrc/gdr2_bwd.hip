@@ -17,123 +17,16 @@
 // at the chunk's last row the scaling of the carried state,
 // sum_r dKd*Kd + exp(gam_C) * rowsum(dS' * S); dg is its reverse running sum.
 //
-// Two kernels:
-//   k_bwd_chain : one wave per (sequence, 16-column value slice), chunks in
-//                 reverse; state gradient in accumulator registers; writes dS'
-//                 (row-major) and dY (tiles) per chunk.
+// Kernels:
+//   k_bwd_chain : (gdr2_chain.hip) one wave per (sequence, 16-column value
+//                 slice), chunks in reverse; state gradient in accumulator
+//                 registers; writes dS' (row-major) and dY (tiles) per chunk.
 //   k_bwd_intra : one workgroup per chunk, fully parallel; reads the saved S,
 //                 Delta, dS', dY and the inputs, writes dq, dk, dv, dg, db, dw.
 #include "gdr2_intra_common.hpp"
 #include "gdr2_kernels.hpp"
 
 namespace gdr2 {
-
-__device__ __forceinline__ void chain_map_b(int gid, int NS, int NJ, int& s, int& j) {
-    if (NS % 8 == 0) {
-        const int x = gid % 8, rest = gid / 8;
-        j = rest % NJ;
-        s = (rest / NJ) * 8 + x;
-    } else {
-        s = gid / NJ;
-        j = gid % NJ;
-    }
-}
-
-template <class OT, int DK, int DV>
-__global__ __launch_bounds__(64) void k_bwd_chain(Args a) {
-    using FT = typename Frag<OT>::type;
-    constexpr int KB = DK / 32, AT = DK / 16, NJ = DV / 16;
-    const int l = threadIdx.x, li = l & 15, lq = l >> 4;
-    int s, j;
-    chain_map_b(blockIdx.x, a.B * a.H, NJ, s, j);
-    const int bidx = s / a.H, h = s % a.H;
-    const Layout& L = a.L;
-    char* ws = a.ws;
-    const OT* dout = (const OT*)a.dout;
-
-    f32x4 dS[AT];
-#pragma unroll
-    for (int at = 0; at < AT; ++at)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            dS[at][i] = a.dht ? a.dht[((size_t)s * DK + 16 * at + 4 * lq + i) * DV + 16 * j + li] : 0.f;
-
-    for (int c = a.NT - 1; c >= 0; --c) {
-        const long long cid = (long long)s * a.NT + c;
-        {  // gradient w.r.t. this chunk's end state, row-major [DK][DV]
-            OT* dsv = (OT*)(ws + L.o_ds) + cid * L.ds;
-#pragma unroll
-            for (int at = 0; at < AT; ++at)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dsv[(16 * at + 4 * lq + i) * DV + 16 * j + li] = to_ot<OT>(dS[at][i]);
-        }
-        const OT* mt = (const OT*)(ws + L.o_mtA) + cid * L.mtA;
-        const OT* kdr = (const OT*)(ws + L.o_kdRA) + cid * L.kdRA;
-        const OT* qgt = (const OT*)(ws + L.o_qgtA) + cid * L.qgtA;
-        const OT* wmt = (const OT*)(ws + L.o_wmtA) + cid * L.wmtA;
-        const OT* tt = (const OT*)(ws + L.o_ttA) + cid * L.ttA;
-        const float* gc = (const float*)(ws + L.o_gc) + cid * L.gc;
-
-        // B fragments of dO (K = token, N = this wave's 16 value channels)
-        FT dOB[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int row = c * CH + 32 * kb + kmap(lq, e);
-                dOB[kb][e] = row < a.T ? dout[(((size_t)bidx * a.T + row) * a.H + h) * DV + 16 * j + li] : to_ot<OT>(0.f);
-            }
-        FT dSB[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) dSB[kb] = frag_of<OT>(dS[2 * kb], dS[2 * kb + 1]);
-
-        // dDelta = M^T dO + Kd dS'
-        f32x4 dD[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) mma(acc, load_frag<OT>(mt + (t * 2 + kb) * 512), dOB[kb]);
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) mma(acc, load_frag<OT>(kdr + (t * KB + kb) * 512), dSB[kb]);
-            dD[t] = acc;
-        }
-        FT dDB[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) dDB[kb] = frag_of<OT>(dD[2 * kb], dD[2 * kb + 1]);
-
-        // dY = T^T dDelta  (tiles for the intra-chunk kernel)
-        OT* dy = (OT*)(ws + L.o_dy) + cid * L.dy + j * 4 * 256;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) mma(acc, load_frag<OT>(tt + (t * 2 + kb) * 512), dDB[kb]);
-            store_tile<OT>(dy + t * 256, acc);
-        }
-
-        // dS = diag(exp gam_C) dS' + Qg^T dO - Wm^T dDelta
-#pragma unroll
-        for (int at = 0; at < AT; ++at) {
-            float g4[4];
-            ld4(gc + 16 * at + 4 * lq, g4);
-            f32x4 pos = {g4[0] * dS[at][0], g4[1] * dS[at][1], g4[2] * dS[at][2], g4[3] * dS[at][3]};
-            f32x4 neg = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                mma(pos, load_frag<OT>(qgt + (at * 2 + kb) * 512), dOB[kb]);
-                mma(neg, load_frag<OT>(wmt + (at * 2 + kb) * 512), dDB[kb]);
-            }
-            dS[at] = pos - neg;
-        }
-    }
-    if (a.dh0) {
-#pragma unroll
-        for (int at = 0; at < AT; ++at)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a.dh0[((size_t)s * DK + 16 * at + 4 * lq + i) * DV + 16 * j + li] = dS[at][i];
-    }
-}
 
 template <class OT, int DK, int DV>
 struct BwdLds {
@@ -210,7 +103,7 @@ __global__ __launch_bounds__(256) void k_bwd_intra(Args a) {
             for (int t = 0; t < 4; ++t) {
                 const int r = 16 * t + li;
                 float x[4];
-                ld4_masked(dob + (size_t)r * rsv + ch0, r < nvalid, x);
+                ld4_row(dob, rsv, r, ch0, nvalid, x);
                 st4(sDO + r * LDV + ch0, x);
             }
         }
@@ -322,9 +215,9 @@ __global__ __launch_bounds__(256) void k_bwd_intra(Args a) {
             const int r = 16 * t + li;
             const bool ok = r < nvalid;
             float qv[4], kv[4], bv[4], dq[4], dk[4], db[4];
-            ld4_masked(qb + (size_t)r * rsk + ch0, ok, qv);
-            ld4_masked(kb_ + (size_t)r * rsk + ch0, ok, kv);
-            ld4_masked(bb + (size_t)r * rsk + ch0, ok, bv);
+            ld4_row(qb, rsk, r, ch0, nvalid, qv);
+            ld4_row(kb_, rsk, r, ch0, nvalid, kv);
+            ld4_row(bb, rsk, r, ch0, nvalid, bv);
             const float dmd = sDMd[r];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -387,16 +280,16 @@ __global__ __launch_bounds__(256) void k_bwd_intra(Args a) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int r = 16 * t + li;
-                if (r < nvalid) {
-                    float dy[4], vv[4], ww[4], dvv[4], dww[4];
-                    ld4(sDY + r * LDV + ch0, dy);
-                    ld4(vb + (size_t)r * rsv + ch0, vv);
-                    ld4(wb + (size_t)r * rsv + ch0, ww);
+                float dy[4], vv[4], ww[4], dvv[4], dww[4];
+                ld4(sDY + r * LDV + ch0, dy);
+                ld4_row(vb, rsv, r, ch0, nvalid, vv);
+                ld4_row(wb, rsv, r, ch0, nvalid, ww);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        dvv[i] = dy[i] * ww[i];
-                        dww[i] = dy[i] * vv[i];
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    dvv[i] = dy[i] * ww[i];
+                    dww[i] = dy[i] * vv[i];
+                }
+                if (r < nvalid) {
                     st4((OT*)a.dv + rowk0 * DV + (size_t)r * rsv + ch0, dvv);
                     st4((OT*)a.dw + rowk0 * DV + (size_t)r * rsv + ch0, dww);
                 }
@@ -421,8 +314,7 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t stream) {
     hipError_t e = hipFuncSetAttribute((const void*)intra, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     if ((e = mark(a, 0, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_chain<OT, DK, DV>), dim3((unsigned)(a.B * a.H * (DV / 16))), dim3(64), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_bwd_chain_t<OT, DK, DV>(a, stream)) != hipSuccess) return e;
     if ((e = mark(a, 1, stream)) != hipSuccess) return e;
     hipLaunchKernelGGL(intra, dim3((unsigned)a.NC), dim3(256), lds, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

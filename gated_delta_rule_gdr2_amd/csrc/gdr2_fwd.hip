@@ -13,16 +13,15 @@
 //   O = Qg S + M Delta,  S' = diag(exp gam_C) S + Kd^T Delta
 // with Kb = b*k*exp(gam), Qg = q*exp(gam), Kd = k*exp(gam_C - gam).
 //
-// Two kernels:
+// Kernels:
 //   k_fwd_intra : one workgroup per chunk, fully parallel. Builds A and M on
 //                 MFMA, inverts (I + A) in fp32 (16x16 diagonal blocks by
 //                 substitution, off-diagonal blocks on fp32 MFMA), forms U and
 //                 Wm on MFMA, and writes every per-chunk operand the two state
 //                 chains need, already in MFMA fragment order.
-//   k_fwd_chain : one wave per (sequence, 16-column slice of the value axis),
-//                 walks the chunks in order. The state slice lives in
-//                 accumulator registers; each step loads its operands with
-//                 coalesced 16-byte-per-lane loads and never touches LDS.
+//   k_fwd_chain : (gdr2_chain.hip) one wave per (sequence, 16-column slice of
+//                 the value axis), walks the chunks in order with the state in
+//                 accumulator registers.
 #include "gdr2_intra_common.hpp"
 #include "gdr2_kernels.hpp"
 
@@ -264,113 +263,6 @@ __global__ __launch_bounds__(256) void k_fwd_intra(Args a) {
     }
 }
 
-// Sequence/slice mapping for the chain kernels. Workgroups are dispatched to the
-// 8 XCDs round-robin (XCD = id % 8); when the sequence count allows, all slices
-// of one sequence land on the same XCD so they share its L2 for the per-chunk
-// operands they all read.
-__device__ __forceinline__ void chain_map(int gid, int NS, int NJ, int& s, int& j) {
-    if (NS % 8 == 0) {
-        const int x = gid % 8, rest = gid / 8;
-        j = rest % NJ;
-        s = (rest / NJ) * 8 + x;
-    } else {
-        s = gid / NJ;
-        j = gid % NJ;
-    }
-}
-
-template <class OT, int DK, int DV, bool TRAIN>
-__global__ __launch_bounds__(64) void k_fwd_chain(Args a) {
-    using FT = typename Frag<OT>::type;
-    constexpr int KB = DK / 32, AT = DK / 16, NJ = DV / 16;
-    const int l = threadIdx.x, li = l & 15, lq = l >> 4;
-    int s, j;
-    chain_map(blockIdx.x, a.B * a.H, NJ, s, j);
-    const int bidx = s / a.H, h = s % a.H;
-    const Layout& L = a.L;
-    char* ws = a.ws;
-
-    f32x4 S[AT];
-#pragma unroll
-    for (int at = 0; at < AT; ++at)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[at][i] = a.h0 ? a.h0[((size_t)s * DK + 16 * at + 4 * lq + i) * DV + 16 * j + li] : 0.f;
-
-    for (int c = 0; c < a.NT; ++c) {
-        const long long cid = (long long)s * a.NT + c;
-        const OT* wm = (const OT*)(ws + L.o_wmA) + cid * L.wmA;
-        const OT* kd = (const OT*)(ws + L.o_kdA) + cid * L.kdA;
-        const OT* qg = (const OT*)(ws + L.o_qgB) + cid * L.qgB;
-        const OT* mb = (const OT*)(ws + L.o_mB) + cid * L.mB;
-        const OT* u = (const OT*)(ws + L.o_u) + cid * L.u + j * 4 * 256;
-        const float* gc = (const float*)(ws + L.o_gc) + cid * L.gc;
-
-        if (TRAIN) {  // chunk start state, row-major [DK][DV]
-            OT* sv = (OT*)(ws + L.o_s) + cid * L.s;
-#pragma unroll
-            for (int at = 0; at < AT; ++at)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sv[(16 * at + 4 * lq + i) * DV + 16 * j + li] = to_ot<OT>(S[at][i]);
-        }
-        FT SB[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) SB[kb] = frag_of<OT>(S[2 * kb], S[2 * kb + 1]);
-
-        // Delta = U - Wm S
-        f32x4 D[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) mma(acc, load_frag<OT>(wm + (t * KB + kb) * 512), SB[kb]);
-            D[t] = load_tile<OT>(u + t * 256) - acc;
-        }
-        FT DB[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) DB[kb] = frag_of<OT>(D[2 * kb], D[2 * kb + 1]);
-        if (TRAIN) {
-            OT* dl = (OT*)(ws + L.o_delta) + cid * L.delta + j * 4 * 256;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) store_tile<OT>(dl + t * 256, D[t]);
-        }
-
-        // O^T = S^T Qg^T + Delta^T M^T  (rows: 16 value channels, columns: tokens)
-        if (a.o) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) mma(acc, SB[kb], load_frag<OT>(qg + (t * KB + kb) * 512));
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) mma(acc, DB[kb], load_frag<OT>(mb + (t * 2 + kb) * 512));
-                const int row = c * CH + 16 * t + li;
-                if (row < a.T) {
-                    float ov[4] = {acc[0], acc[1], acc[2], acc[3]};
-                    st4((OT*)a.o + (((size_t)bidx * a.T + row) * a.H + h) * DV + 16 * j + 4 * lq, ov);
-                }
-            }
-        }
-
-        // S' = diag(exp gam_C) S + Kd^T Delta
-#pragma unroll
-        for (int at = 0; at < AT; ++at) {
-            float g4[4];
-            ld4(gc + 16 * at + 4 * lq, g4);
-            f32x4 acc = {g4[0] * S[at][0], g4[1] * S[at][1], g4[2] * S[at][2], g4[3] * S[at][3]};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) mma(acc, load_frag<OT>(kd + (at * 2 + kb) * 512), DB[kb]);
-            S[at] = acc;
-        }
-    }
-    if (a.ht) {
-#pragma unroll
-        for (int at = 0; at < AT; ++at)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a.ht[((size_t)s * DK + 16 * at + 4 * lq + i) * DV + 16 * j + li] = S[at][i];
-    }
-}
-
 size_t fwd_intra_lds_bytes(int DK, int DV, int esz) {
 #define GDR2_LDS(OT_, DK_, DV_) \
     if (DK == DK_ && DV == DV_ && esz == (int)sizeof(OT_)) return FwdLds<OT_, DK_, DV_>::BYTES;
@@ -384,15 +276,13 @@ template <class OT, int DK, int DV>
 static hipError_t launch_fwd_t(const Args& a, bool train, hipStream_t stream) {
     const size_t lds = FwdLds<OT, DK, DV>::BYTES;
     auto intra = train ? k_fwd_intra<OT, DK, DV, true> : k_fwd_intra<OT, DK, DV, false>;
-    auto chain = train ? k_fwd_chain<OT, DK, DV, true> : k_fwd_chain<OT, DK, DV, false>;
     hipError_t e = hipFuncSetAttribute((const void*)intra, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     if ((e = mark(a, 0, stream)) != hipSuccess) return e;
     hipLaunchKernelGGL(intra, dim3((unsigned)a.NC), dim3(256), lds, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(a, 1, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(chain, dim3((unsigned)(a.B * a.H * (DV / 16))), dim3(64), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_fwd_chain_t<OT, DK, DV>(a, train, stream)) != hipSuccess) return e;
     return mark(a, 2, stream);
 }
 

@@ -31,14 +31,16 @@ constexpr int F_ROWS = 2 * NBLK + NPAIR;
 template <class OT>
 constexpr int pad_ot() { return sizeof(OT) == 2 ? 8 : 4; }
 
-// Load 4 consecutive elements of a [.., D] row, zero when the row is past T.
+// Load 4 consecutive elements of token row r (row stride rs) at column ch; rows at or
+// past nvalid (>= 1) read as zero. Branch-free: the address is clamped to a valid row
+// and the value selected afterwards, so independent loads can all be in flight at once.
 template <class IT>
-__device__ __forceinline__ void ld4_masked(const IT* p, bool valid, float out[4]) {
-    if (valid) {
-        ld4(p, out);
-    } else {
-        out[0] = out[1] = out[2] = out[3] = 0.f;
-    }
+__device__ __forceinline__ void ld4_row(const IT* base, size_t rs, int r, int ch, int nvalid, float out[4]) {
+    const int rr = r < nvalid ? r : nvalid - 1;
+    ld4(base + (size_t)rr * rs + ch, out);
+    const bool ok = r < nvalid;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = ok ? out[i] : 0.f;
 }
 
 // Computes gam (registers), the factor arrays (LDS), exp(gam_C) (global) and
@@ -59,7 +61,7 @@ __device__ __forceinline__ void chunk_factors(const OT* gb, const OT* qb, const 
         for (int t = 0; t < 4; ++t) {
             const int r = 16 * t + li;
             float gv[4];
-            ld4_masked(gb + (size_t)r * rs + ch0, r < nvalid, gv);
+            ld4_row(gb, rs, r, ch0, nvalid, gv);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float x = row_scan16(gv[i]) + run[i];
@@ -92,11 +94,10 @@ __device__ __forceinline__ void chunk_factors(const OT* gb, const OT* qb, const 
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int r = 16 * t + li;
-            const bool ok = r < nvalid;
             float qv[4], kv[4], bv[4], xa[4], xm[4], y[4];
-            ld4_masked(qb + (size_t)r * rs + ch0, ok, qv);
-            ld4_masked(kb + (size_t)r * rs + ch0, ok, kv);
-            ld4_masked(bb + (size_t)r * rs + ch0, ok, bv);
+            ld4_row(qb, rs, r, ch0, nvalid, qv);
+            ld4_row(kb, rs, r, ch0, nvalid, kv);
+            ld4_row(bb, rs, r, ch0, nvalid, bv);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float e1 = __expf(gam[ac][t][i] - g0[t][i]);
@@ -124,8 +125,8 @@ __device__ __forceinline__ void chunk_x(const OT* vb, const OT* wb, size_t rs, i
         for (int t = 0; t < 4; ++t) {
             const int r = 16 * t + li;
             float vv[4], ww[4], x[4];
-            ld4_masked(vb + (size_t)r * rs + ch0, r < nvalid, vv);
-            ld4_masked(wb + (size_t)r * rs + ch0, r < nvalid, ww);
+            ld4_row(vb, rs, r, ch0, nvalid, vv);
+            ld4_row(wb, rs, r, ch0, nvalid, ww);
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[i] = vv[i] * ww[i];
             st4(sX + r * LDV + ch0, x);

@@ -30,6 +30,10 @@ inline hipError_t mark(const Args& a, int i, hipStream_t stream) {
 }
 
 // Launchers: enqueue on `stream`, return hipSuccess or the launch error.
+template <class OT, int DK, int DV>
+hipError_t launch_fwd_chain_t(const Args& a, bool train, hipStream_t stream);
+template <class OT, int DK, int DV>
+hipError_t launch_bwd_chain_t(const Args& a, hipStream_t stream);
 hipError_t launch_fwd(const Args& a, bool bf16, bool train, hipStream_t stream);
 hipError_t launch_bwd(const Args& a, bool bf16, hipStream_t stream);
 size_t fwd_intra_lds_bytes(int DK, int DV, int esz);
