@@ -30,52 +30,58 @@ namespace gdr2 {
 
 template <class OT, int DK, int DV>
 struct BwdLds {
+    static constexpr int ES = sizeof(OT);
     static constexpr int LDK = DK + pad_ot<OT>();
     static constexpr int LDV = DV + pad_ot<OT>();
     static constexpr int LDCO = CH + pad_ot<OT>();
-    static constexpr size_t XA = 0;
-    static constexpr size_t XM = XA + sizeof(OT) * CH * LDK;
-    static constexpr size_t Y = XM + sizeof(OT) * CH * LDK;
-    static constexpr size_t DO = Y + sizeof(OT) * CH * LDK;
-    static constexpr size_t DL = DO + sizeof(OT) * CH * LDV;
-    static constexpr size_t DY = DL + sizeof(OT) * CH * LDV;
-    static constexpr size_t DA = DY + sizeof(OT) * CH * LDV;
-    static constexpr size_t DM = DA + sizeof(OT) * CH * LDCO;
-    static constexpr size_t F = DM + sizeof(OT) * CH * LDCO;
-    static constexpr size_t DMD = F + sizeof(float) * F_ROWS * DK;  // diagonal of dM, fp32
-    static constexpr size_t BYTES = DMD + sizeof(float) * CH;
+    static constexpr int KMAT = CH * LDK * ES;
+    static constexpr int VMAT = CH * LDV * ES;
+    static constexpr int SLOT = KMAT > VMAT ? KMAT : VMAT;
+    static constexpr int S0 = 0;             // dO, later XA
+    static constexpr int S1 = S0 + SLOT;     // Delta, later XM
+    static constexpr int S2 = S1 + SLOT;     // dY, later Y
+    static constexpr int DA = S2 + SLOT;     // dA [CH][LDCO]
+    static constexpr int DM = DA + CH * LDCO * ES;
+    static constexpr int F = DM + CH * LDCO * ES;
+    static constexpr int DMD = F + F_ROWS * DK * 4;  // diagonal of dM, fp32
+    static constexpr int BYTES = DMD + CH * 4;
 };
 
-// tile dump [DV/16][4][64 lanes][4] -> row-major LDS [CH][ld]
-template <class OT, int DV>
-__device__ __forceinline__ void undump_tiles(const OT* src, OT* dst, int ld) {
-    for (int e = threadIdx.x; e < (DV / 16) * 4 * 64; e += 256) {
+// tile dump [DV/16][4][64 lanes][4] -> padded row-major LDS [CH][ld]
+template <class OT, int DV, int NTHR>
+__device__ __forceinline__ void undump_tiles(const OT* src, lds_char* dst, int ld) {
+    for (int e = threadIdx.x; e < (DV / 16) * 4 * 64; e += NTHR) {
         const int lane = e & 63, t = (e >> 6) & 3, jj = e >> 8;
         float v[4];
         ld4(src + (size_t)e * 4, v);
         const int row = 16 * t + 4 * (lane >> 4), col = 16 * jj + (lane & 15);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(row + i) * ld + col] = to_ot<OT>(v[i]);
+        for (int i = 0; i < 4; ++i) lds_store<OT>(dst + ((row + i) * ld + col) * (int)sizeof(OT), to_ot<OT>(v[i]));
     }
 }
 
+constexpr int BWD_NW = 8;  // waves per workgroup of the backward intra-chunk kernel
+
 template <class OT, int DK, int DV>
-__global__ __launch_bounds__(256) void k_bwd_intra(Args a) {
+__global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     using LS = BwdLds<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
     constexpr int LDK = LS::LDK, LDV = LS::LDV, LDCO = LS::LDCO;
-    constexpr int KV = DV / 32, CPW = DK / 64, VPW = DV / 64;
-    extern __shared__ __align__(16) char smem[];
-    OT* sXA = (OT*)(smem + LS::XA);
-    OT* sXM = (OT*)(smem + LS::XM);
-    OT* sY = (OT*)(smem + LS::Y);
-    OT* sDO = (OT*)(smem + LS::DO);
-    OT* sDL = (OT*)(smem + LS::DL);
-    OT* sDY = (OT*)(smem + LS::DY);
-    OT* sDA = (OT*)(smem + LS::DA);
-    OT* sDM = (OT*)(smem + LS::DM);
-    float* sF = (float*)(smem + LS::F);
-    float* sDMd = (float*)(smem + LS::DMD);
+    constexpr int NW = BWD_NW, NTHR = 64 * NW;
+    constexpr int KV = DV / 32;
+    constexpr int CPW = (DK / 16 + NW - 1) / NW;  // key-channel tiles per wave
+    extern __shared__ __align__(16) char smem_[];
+    lds_char* smem = (lds_char*)smem_;
+    lds_char* sDO = smem + LS::S0;
+    lds_char* sDL = smem + LS::S1;
+    lds_char* sDY = smem + LS::S2;
+    lds_char* sXA = smem + LS::S0;
+    lds_char* sXM = smem + LS::S1;
+    lds_char* sY = smem + LS::S2;
+    lds_char* sDA = smem + LS::DA;
+    lds_char* sDM = smem + LS::DM;
+    lds_char* sF = smem + LS::F;
+    lds_char* sDMd = smem + LS::DMD;
 
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, li = l & 15, lq = l >> 4;
     const long long cid = blockIdx.x;
@@ -86,35 +92,38 @@ __global__ __launch_bounds__(256) void k_bwd_intra(Args a) {
     const size_t rowk0 = ((size_t)bidx * a.T + t0) * a.H + h;
     const size_t rsk = (size_t)a.H * DK, rsv = (size_t)a.H * DV;
     const Layout& L = a.L;
-    char* ws = a.ws;
     const OT* qb = (const OT*)a.q + rowk0 * DK;
     const OT* kb_ = (const OT*)a.k + rowk0 * DK;
     const OT* bb = (const OT*)a.b + rowk0 * DK;
 
-    // ---- phase 1: factors, dO, Delta, dY into LDS
+    // ---- phase 1: cumulative decay and factors; dO, Delta, dY into LDS
     float gam[CPW][4][4];
-    chunk_factors<OT, DK>((const OT*)a.g + rowk0 * DK, qb, kb_, bb, rsk, nvalid, gam, sXA, sXM, sY, LDK, sF, nullptr);
+#pragma unroll
+    for (int ac = 0; ac < CPW; ++ac) {
+        if (wv + NW * ac >= DK / 16) break;
+        const int ch0 = 16 * (wv + NW * ac) + 4 * lq;
+        float g0[4][4], ge[4][4];
+        chunk_gamma((const OT*)a.g + rowk0 * DK, rsk, ch0, nvalid, gam[ac], g0, ge);
+        write_factors<DK>(sF, ch0, g0, ge);
+    }
     {
         const OT* dob = (const OT*)a.dout + rowk0 * DV;
+        for (int jt = wv; jt < DV / 16; jt += NW) {
+            const int ch0 = 16 * jt + 4 * lq;
+            float x[4][4];
 #pragma unroll
-        for (int jc = 0; jc < VPW; ++jc) {
-            const int ch0 = 16 * (wv * VPW + jc) + 4 * lq;
+            for (int t = 0; t < 4; ++t) ld4_row(dob, rsv, 16 * t + li, ch0, nvalid, x[t]);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int r = 16 * t + li;
-                float x[4];
-                ld4_row(dob, rsv, r, ch0, nvalid, x);
-                st4(sDO + r * LDV + ch0, x);
-            }
+            for (int t = 0; t < 4; ++t) lds_put4<OT>(sDO + ((16 * t + li) * LDV + ch0) * (int)sizeof(OT), x[t]);
         }
     }
-    undump_tiles<OT, DV>((const OT*)(ws + L.o_delta) + cid * L.delta, sDL, LDV);
-    undump_tiles<OT, DV>((const OT*)(ws + L.o_dy) + cid * L.dy, sDY, LDV);
-    for (int idx = tid; idx < CH * CH; idx += 256) {  // zero the upper blocks of dA, dM
+    undump_tiles<OT, DV, NTHR>((const OT*)(a.ws + L.o_delta) + cid * L.delta, sDL, LDV);
+    undump_tiles<OT, DV, NTHR>((const OT*)(a.ws + L.o_dy) + cid * L.dy, sDY, LDV);
+    for (int idx = tid; idx < CH * CH; idx += NTHR) {  // zero the upper blocks of dA, dM
         const int r = idx / CH, cc = idx % CH;
         if ((cc >> 4) > (r >> 4)) {
-            sDA[r * LDCO + cc] = to_ot<OT>(0.f);
-            sDM[r * LDCO + cc] = to_ot<OT>(0.f);
+            lds_store<OT>(sDA + (r * LDCO + cc) * (int)sizeof(OT), to_ot<OT>(0.f));
+            lds_store<OT>(sDM + (r * LDCO + cc) * (int)sizeof(OT), to_ot<OT>(0.f));
         }
     }
     __syncthreads();
@@ -123,82 +132,170 @@ __global__ __launch_bounds__(256) void k_bwd_intra(Args a) {
     // The diagonal of M, q_r . k_r, does not depend on the decay; its gradient is
     // kept apart in fp32 (sDMd) so that its query-side and key-side terms cancel
     // exactly in the log-decay gradient instead of up to bf16 rounding.
-    for (int p = wv; p < 2 * NPAIR; p += 4) {
+    const LPad<OT> vDO{sDO, LDV}, vDL{sDL, LDV}, vDY{sDY, LDV};
+    for (int p = wv; p < 2 * NPAIR; p += NW) {
         const bool isM = p >= NPAIR;
         int R, I;
         pair_ri(isM ? p - NPAIR : p, R, I);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KV; ++kb)
-            mma(acc, frag_rowk<OT>(isM ? sDO : sDY, LDV, 16 * R, 32 * kb), frag_rowk<OT>(sDL, LDV, 16 * I, 32 * kb));
+            mma(acc, lfrag_rowk<OT, OT>(isM ? vDO : vDY, 16 * R, 32 * kb), lfrag_rowk<OT, OT>(vDL, 16 * I, 32 * kb));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * R + 4 * lq + i, col = 16 * I + li;
             float v = isM ? acc[i] : -acc[i];
-            if (isM && col == row) sDMd[row] = v;
+            if (isM && col == row) lds_store<float>(sDMd + row * 4, v);
             if (R == I && col >= row) v = 0.f;  // dA strictly lower; dM diagonal kept in sDMd
-            (isM ? sDM : sDA)[row * LDCO + col] = to_ot<OT>(v);
+            lds_store<OT>((isM ? sDM : sDA) + (row * LDCO + col) * (int)sizeof(OT), to_ot<OT>(v));
         }
     }
     __syncthreads();
 
-    // ---- phases 3+4, one key-channel tile at a time: products, then elementwise finals
-    const OT* Sg = (const OT*)(ws + L.o_s) + cid * L.s;
-    const OT* dSg = (const OT*)(ws + L.o_ds) + cid * L.ds;
-#pragma unroll 1
+    // ---- phase 3a: products with the saved states, dv and dw
+    // Per key-channel tile, transposed tiles (rows = key channel, columns = token):
+    //   Pq = exp(gam_R0) * (dO S^T)^T, Pb = -exp(gam_R0) * (dY S^T)^T,
+    //   Pk = exp(gam_C - gam_Rend) * (Delta dS'^T)^T
+    // The bilinear terms are accumulated into the same registers in phase 3c.
+    const OT* Sg = (const OT*)(a.ws + L.o_s) + cid * L.s;
+    const OT* dSg = (const OT*)(a.ws + L.o_ds) + cid * L.ds;
+    f32x4 Pq[CPW][4], Pb[CPW][4], Pk[CPW][4];
+    float rsum[CPW], kdx[CPW][4];
+#pragma unroll
     for (int ac = 0; ac < CPW; ++ac) {
-        const int at = wv * CPW + ac;
-        const int mcol = 16 * at + li;  // key channel held as operand row by this lane
+        const int at = wv + NW * ac;
+        if (at >= DK / 16) break;
         FT Sf[KV], dSf[KV];
         float pr = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KV; ++kb) {
             Sf[kb] = frag_rowk<OT>(Sg, DV, 16 * at, 32 * kb);
             dSf[kb] = frag_rowk<OT>(dSg, DV, 16 * at, 32 * kb);
+        }
+#pragma unroll
+        for (int kb = 0; kb < KV; ++kb)
 #pragma unroll
             for (int e = 0; e < 8; ++e) pr += to_f(Sf[kb][e]) * to_f(dSf[kb][e]);
-        }
         pr += __shfl_xor(pr, 16, 64);
-        pr += __shfl_xor(pr, 32, 64);  // rowsum(dS' * S) for key channel mcol, in every lane li
-
-        f32x4 dQg[4], dKb[4], dKd[4], xA[4], xM[4], yA[4], yM[4];
+        pr += __shfl_xor(pr, 32, 64);  // rowsum(dS' * S) of key channel 16at + li
+        rsum[ac] = pr;
+        float g0[4][4], ge[4][4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                g0[R][i] = row_bcast(gam[ac][R][i], 0);
+                ge[R][i] = row_bcast(gam[ac][R][i], 15);
+            }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            dQg[t] = z; dKb[t] = z; dKd[t] = z; xA[t] = z; xM[t] = z; yA[t] = z; yM[t] = z;
+            f32x4 q4 = {0.f, 0.f, 0.f, 0.f}, b4 = q4, k4 = q4;
 #pragma unroll
             for (int kb = 0; kb < KV; ++kb) {
-                mma(dQg[t], Sf[kb], frag_rowk<OT>(sDO, LDV, 16 * t, 32 * kb));
-                mma(dKb[t], Sf[kb], frag_rowk<OT>(sDY, LDV, 16 * t, 32 * kb));  // (dY S^T)^T
-                mma(dKd[t], dSf[kb], frag_rowk<OT>(sDL, LDV, 16 * t, 32 * kb));
+                mma(q4, Sf[kb], lfrag_rowk<OT, OT>(vDO, 16 * t, 32 * kb));
+                mma(b4, Sf[kb], lfrag_rowk<OT, OT>(vDY, 16 * t, 32 * kb));
+                mma(k4, dSf[kb], lfrag_rowk<OT, OT>(vDL, 16 * t, 32 * kb));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e0 = __expf(g0[t][i]), ec = __expf(ge[3][i] - ge[t][i]);
+                Pq[ac][t][i] = e0 * q4[i];
+                Pb[ac][t][i] = -e0 * b4[i];
+                Pk[ac][t][i] = ec * k4[i];
             }
         }
-        // bilinear back-propagation, transposed: rows = key channel, columns = token
+        // sum over the chunk's tokens of dKd * Kd (Kd = k * exp(gam_C - gam)), per channel
+        const int ch0 = 16 * at + 4 * lq;
+        float kx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int R = 0; R < 4; ++R) {  // Xbar (erase/query side) for target block R
+        for (int t = 0; t < 4; ++t) {
+            float kv[4];
+            ld4_row(kb_, rsk, 16 * t + li, ch0, nvalid, kv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kx[i] += Pk[ac][t][i] * kv[i] * __expf(ge[t][i] - gam[ac][t][i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kdx[ac][i] = row_sum16(kx[i]);
+    }
+    {  // dv = dY * w, dw = dY * v
+        const OT* vb = (const OT*)a.v + rowk0 * DV;
+        const OT* wb = (const OT*)a.w + rowk0 * DV;
+        for (int jt = wv; jt < DV / 16; jt += NW) {
+            const int ch0 = 16 * jt + 4 * lq;
+            float vv[4][4], ww[4][4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                ld4_row(vb, rsv, 16 * t + li, ch0, nvalid, vv[t]);
+                ld4_row(wb, rsv, 16 * t + li, ch0, nvalid, ww[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = 16 * t + li;
+                float dy[4], dvv[4], dww[4];
+                lds_get4<OT>(sDY + (r * LDV + ch0) * (int)sizeof(OT), dy);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dvv[i] = dy[i] * ww[t][i];
+                    dww[i] = dy[i] * vv[t][i];
+                }
+                if (r < nvalid) {
+                    st4((OT*)a.dv + rowk0 * DV + (size_t)r * rsv + ch0, dvv);
+                    st4((OT*)a.dw + rowk0 * DV + (size_t)r * rsv + ch0, dww);
+                }
+            }
+        }
+    }
+    __syncthreads();  // dO, Delta, dY are dead; their slots take the key/query factors
+
+    // ---- phase 3b: XA = b*k*E1, XM = q*E1, Y = k*E2 into LDS
+#pragma unroll
+    for (int ac = 0; ac < CPW; ++ac) {
+        if (wv + NW * ac >= DK / 16) break;
+        const int ch0 = 16 * (wv + NW * ac) + 4 * lq;
+        float g0[4][4], ge[4][4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                g0[R][i] = row_bcast(gam[ac][R][i], 0);
+                ge[R][i] = row_bcast(gam[ac][R][i], 15);
+            }
+        scaled_factors<OT, DK>(qb, kb_, bb, rsk, ch0, nvalid, gam[ac], g0, ge, sXA, sXM, sY, LDK, nullptr,
+                               nullptr);
+    }
+    __syncthreads();
+
+    // ---- phase 3c: bilinear back-propagation, then the elementwise finals
+    const LPad<OT> vXA{sXA, LDK}, vXM{sXM, LDK}, vY{sY, LDK}, vDA{sDA, LDCO}, vDM{sDM, LDCO};
+#pragma unroll
+    for (int ac = 0; ac < CPW; ++ac) {
+        const int at = wv + NW * ac;
+        if (at >= DK / 16) break;
+        const int mcol = 16 * at + li;  // key channel held as operand row by this lane
+        auto sfac = [&](int R, int I) { return lds_load<float>(sF + ((F_S + pair_id(R, I)) * DK + mcol) * 4); };
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {  // Xbar (erase / query side) for target block R
             for (int kb = 0; kb <= R / 2; ++kb) {
                 const int I0 = 2 * kb, I1 = 2 * kb + 1;
-                const float r0 = sF[(F_S + pair_id(R, I0)) * DK + mcol];
-                const float r1 = I1 <= R ? sF[(F_S + pair_id(R, I1)) * DK + mcol] : 0.f;
-                FT ay = frag_colk<OT, OT>(sY, LDK, 16 * at, 32 * kb, r0, r1);
-                mma(xA[R], ay, frag_rowk<OT>(sDA, LDCO, 16 * R, 32 * kb));
-                mma(xM[R], ay, frag_rowk<OT>(sDM, LDCO, 16 * R, 32 * kb));
+                FT ay = lfrag_colk<OT, OT>(vY, 16 * at, 32 * kb, sfac(R, I0), I1 <= R ? sfac(R, I1) : 0.f);
+                mma(Pb[ac][R], ay, lfrag_rowk<OT, OT>(vDA, 16 * R, 32 * kb));
+                mma(Pq[ac][R], ay, lfrag_rowk<OT, OT>(vDM, 16 * R, 32 * kb));
             }
         }
 #pragma unroll
         for (int I = 0; I < 4; ++I) {  // Ybar (key side) for source block I
             for (int kb = I / 2; kb < 2; ++kb) {
                 const int R0 = 2 * kb, R1 = 2 * kb + 1;
-                const float r0 = R0 >= I ? sF[(F_S + pair_id(R0, I)) * DK + mcol] : 0.f;
-                const float r1 = R1 >= I ? sF[(F_S + pair_id(R1, I)) * DK + mcol] : 0.f;
-                FT bA = frag_colk<OT, OT>(sDA, LDCO, 16 * I, 32 * kb);
-                FT bM = frag_colk<OT, OT>(sDM, LDCO, 16 * I, 32 * kb);
-                mma(yA[I], frag_colk<OT, OT>(sXA, LDK, 16 * at, 32 * kb, r0, r1), bA);
-                mma(yM[I], frag_colk<OT, OT>(sXM, LDK, 16 * at, 32 * kb, r0, r1), bM);
+                const float r0 = R0 >= I ? sfac(R0, I) : 0.f;
+                const float r1 = R1 >= I ? sfac(R1, I) : 0.f;
+                mma(Pk[ac][I], lfrag_colk<OT, OT>(vXA, 16 * at, 32 * kb, r0, r1),
+                    lfrag_colk<OT, OT>(vDA, 16 * I, 32 * kb));
+                mma(Pk[ac][I], lfrag_colk<OT, OT>(vXM, 16 * at, 32 * kb, r0, r1),
+                    lfrag_colk<OT, OT>(vDM, 16 * I, 32 * kb));
             }
         }
 
-        // ---- finals at (key channel 16at + 4lq + i, token 16t + li)
+        // finals at (key channel 16at + 4lq + i, token 16t + li)
         const int ch0 = 16 * at + 4 * lq;
         float g0[4][4], ge[4][4];
 #pragma unroll
@@ -208,47 +305,44 @@ __global__ __launch_bounds__(256) void k_bwd_intra(Args a) {
                 g0[R][i] = row_bcast(gam[ac][R][i], 0);
                 ge[R][i] = row_bcast(gam[ac][R][i], 15);
             }
-        float kdsum[4] = {0.f, 0.f, 0.f, 0.f};
+        float qv[4][4], kv[4][4], bv[4][4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            ld4_row(qb, rsk, 16 * t + li, ch0, nvalid, qv[t]);
+            ld4_row(kb_, rsk, 16 * t + li, ch0, nvalid, kv[t]);
+            ld4_row(bb, rsk, 16 * t + li, ch0, nvalid, bv[t]);
+        }
         float dgam[4][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int r = 16 * t + li;
-            const bool ok = r < nvalid;
-            float qv[4], kv[4], bv[4], dq[4], dk[4], db[4];
-            ld4_row(qb, rsk, r, ch0, nvalid, qv);
-            ld4_row(kb_, rsk, r, ch0, nvalid, kv);
-            ld4_row(bb, rsk, r, ch0, nvalid, bv);
-            const float dmd = sDMd[r];
+            const float dmd = lds_load<float>(sDMd + r * 4);
+            float dq[4], dk[4], db[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float gm = gam[ac][t][i];
-                const float e1 = __expf(gm - g0[t][i]);
-                const float e2 = __expf(ge[t][i] - gm);
-                const float G = __expf(gm);             // exp(gam_r)
-                const float Gd = __expf(ge[3][i] - gm);  // exp(gam_C - gam_r)
-                const float gq = dQg[t][i] * G + e1 * xM[t][i] + dmd * kv[i];
-                const float gbk = e1 * xA[t][i] - dKb[t][i] * G;  // dKb holds +dY S^T
-                const float gk = dKd[t][i] * Gd + e2 * (yA[t][i] + yM[t][i]) + dmd * qv[i];
-                dq[i] = gq;
-                db[i] = gbk * kv[i];
-                dk[i] = gbk * bv[i] + gk;
-                dgam[t][i] = qv[i] * dq[i] + 2.f * bv[i] * db[i] - kv[i] * dk[i];
-                kdsum[i] += dKd[t][i] * kv[i] * Gd;
+                const float e1 = __expf(gam[ac][t][i] - g0[t][i]);
+                const float e2 = __expf(ge[t][i] - gam[ac][t][i]);
+                const float gbk = e1 * Pb[ac][t][i];
+                dq[i] = e1 * Pq[ac][t][i] + dmd * kv[t][i];
+                db[i] = gbk * kv[t][i];
+                dk[i] = gbk * bv[t][i] + e2 * Pk[ac][t][i] + dmd * qv[t][i];
+                dgam[t][i] = qv[t][i] * dq[i] + 2.f * bv[t][i] * db[i] - kv[t][i] * dk[i];
             }
-            if (ok) {
+            if (r < nvalid) {
                 const size_t off = (size_t)r * rsk + ch0;
                 st4((OT*)a.dq + rowk0 * DK + off, dq);
                 st4((OT*)a.dk + rowk0 * DK + off, dk);
                 st4((OT*)a.db + rowk0 * DK + off, db);
             }
         }
-        // carried-state scaling at the chunk's last row, then the reverse running sum
+        // scaling of the carried state at the chunk's last row: sum_r dKd*Kd + exp(gam_C) rowsum(dS'*S)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float rsumS = __shfl(pr, (l & 48) | (4 * lq + i), 64);  // rowsum for channel ch0 + i
-            const float extra = row_sum16(kdsum[i]) + __expf(ge[3][i]) * rsumS;
+            const float rs_i = __shfl(rsum[ac], (l & 48) | (4 * lq + i), 64);  // row sum of channel ch0 + i
+            const float extra = kdx[ac][i] + __expf(ge[3][i]) * rs_i;
             if (li == 15) dgam[3][i] += extra;
         }
+        // dg = reverse running sum of dgam over the chunk's tokens
         float tot[4] = {0.f, 0.f, 0.f, 0.f}, pre[4][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -266,33 +360,6 @@ __global__ __launch_bounds__(256) void k_bwd_intra(Args a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dg[i] = tot[i] - pre[t][i] + dgam[t][i];
                 st4((OT*)a.dg + rowk0 * DK + (size_t)r * rsk + ch0, dg);
-            }
-        }
-    }
-
-    // ---- dv = dY * w, dw = dY * v
-    {
-        const OT* vb = (const OT*)a.v + rowk0 * DV;
-        const OT* wb = (const OT*)a.w + rowk0 * DV;
-#pragma unroll
-        for (int jc = 0; jc < VPW; ++jc) {
-            const int ch0 = 16 * (wv * VPW + jc) + 4 * lq;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int r = 16 * t + li;
-                float dy[4], vv[4], ww[4], dvv[4], dww[4];
-                ld4(sDY + r * LDV + ch0, dy);
-                ld4_row(vb, rsv, r, ch0, nvalid, vv);
-                ld4_row(wb, rsv, r, ch0, nvalid, ww);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    dvv[i] = dy[i] * ww[i];
-                    dww[i] = dy[i] * vv[i];
-                }
-                if (r < nvalid) {
-                    st4((OT*)a.dv + rowk0 * DV + (size_t)r * rsv + ch0, dvv);
-                    st4((OT*)a.dw + rowk0 * DV + (size_t)r * rsv + ch0, dww);
-                }
             }
         }
     }
@@ -316,7 +383,7 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t stream) {
     if ((e = mark(a, 0, stream)) != hipSuccess) return e;
     if ((e = launch_bwd_chain_t<OT, DK, DV>(a, stream)) != hipSuccess) return e;
     if ((e = mark(a, 1, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(intra, dim3((unsigned)a.NC), dim3(256), lds, stream, a);
+    hipLaunchKernelGGL(intra, dim3((unsigned)a.NC), dim3(64 * BWD_NW), lds, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return mark(a, 2, stream);
 }

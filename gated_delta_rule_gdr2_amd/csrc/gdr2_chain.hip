@@ -24,10 +24,6 @@
 
 namespace gdr2 {
 
-// LDS pointers are kept in the LDS address space end to end.
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) void lds_void;
-
 // Copy `bytes` (a multiple of 1024) from global memory into LDS, 16 bytes per lane.
 __device__ __forceinline__ void dma16(const void* src, lds_char* dst, int bytes) {
     const int l = lane_id();
@@ -41,29 +37,6 @@ __device__ __forceinline__ void dma4(const void* src, lds_char* dst, int bytes) 
         __builtin_amdgcn_global_load_lds((const char*)src + k + l * 4, (lds_void*)(dst + k), 4, 0, 0);
 }
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-
-template <class OT>
-__device__ __forceinline__ typename Frag<OT>::type lds_frag(const lds_char* base) {
-    typedef __attribute__((address_space(3))) const typename Frag<OT>::type lfrag;
-    return *(lfrag*)(base + lane_id() * 8 * sizeof(OT));
-}
-__device__ __forceinline__ void lds_ld4(const lds_char* p, float out[4], bf16) {
-    typedef __attribute__((address_space(3))) const bf16x4 T4;
-    bf16x4 v = *(T4*)p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = (float)v[i];
-}
-__device__ __forceinline__ void lds_ld4(const lds_char* p, float out[4], float) {
-    typedef __attribute__((address_space(3))) const f32x4 T4;
-    f32x4 v = *(T4*)p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = v[i];
-}
-template <class OT>
-__device__ __forceinline__ OT lds_elem(const lds_char* base, int idx) {
-    typedef __attribute__((address_space(3))) const OT TE;
-    return ((TE*)base)[idx];
-}
 
 // Sequence/slice mapping. Workgroups go to the 8 XCDs round-robin (XCD = id % 8);
 // when the sequence count allows, all slices of one sequence share an XCD and
@@ -127,14 +100,13 @@ __device__ __forceinline__ void store_state(OT* dst, int j, const f32x4 (&pend)[
 // ============================================================================ forward chain
 template <class OT, int DK, int DV>
 struct FwdChainBuf {
-    static constexpr int FB = 512 * sizeof(OT);  // bytes per fragment block
-    static constexpr int KB = DK / 32;
-    static constexpr int WM = 0;                          // 4*KB blocks
-    static constexpr int KD = WM + 4 * KB * FB;           // (DK/16)*2 blocks
-    static constexpr int QG = KD + (DK / 16) * 2 * FB;    // 4*KB blocks
-    static constexpr int MB = QG + 4 * KB * FB;           // 8 blocks
-    static constexpr int U = MB + 8 * FB;                 // 4 tiles of this slice
-    static constexpr int GC = U + 4 * 256 * sizeof(OT);   // DK floats
+    static constexpr int ES = sizeof(OT);
+    static constexpr int WM = 0;                  // Wm [64][DK] swizzled
+    static constexpr int KD = WM + CH * DK * ES;  // Kd [64][DK]
+    static constexpr int QG = KD + CH * DK * ES;  // Qg [64][DK]
+    static constexpr int M = QG + CH * DK * ES;   // M [64][64]
+    static constexpr int U = M + CH * CH * ES;    // 4 U tiles of this slice
+    static constexpr int GC = U + 4 * 256 * ES;   // DK floats
     static constexpr int BYTES = GC + DK * 4;
 };
 
@@ -142,11 +114,11 @@ template <class OT, int DK, int DV>
 __device__ __forceinline__ void fwd_prefetch(const Args& a, long long cid, int j, lds_char* buf) {
     using B = FwdChainBuf<OT, DK, DV>;
     const Layout& L = a.L;
-    dma16(a.ws + L.o_wmA + cid * L.wmA * sizeof(OT), buf + B::WM, 4 * B::KB * B::FB);
-    dma16(a.ws + L.o_kdA + cid * L.kdA * sizeof(OT), buf + B::KD, (DK / 16) * 2 * B::FB);
+    dma16(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM, CH * DK * sizeof(OT));
+    dma16(a.ws + L.o_kd + cid * L.kd * sizeof(OT), buf + B::KD, CH * DK * sizeof(OT));
     if (a.o) {
-        dma16(a.ws + L.o_qgB + cid * L.qgB * sizeof(OT), buf + B::QG, 4 * B::KB * B::FB);
-        dma16(a.ws + L.o_mB + cid * L.mB * sizeof(OT), buf + B::MB, 8 * B::FB);
+        dma16(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG, CH * DK * sizeof(OT));
+        dma16(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M, CH * CH * sizeof(OT));
     }
     dma16(a.ws + L.o_u + (cid * L.u + (size_t)j * 4 * 256) * sizeof(OT), buf + B::U, 4 * 256 * sizeof(OT));
     dma4(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC, DK * 4);
@@ -192,6 +164,8 @@ __device__ __forceinline__ void fwd_step(const Args& a, int c, const lds_char* b
     using FT = typename Frag<OT>::type;
     constexpr int KB = DK / 32, AT = DK / 16;
     const int l = lane_id(), lq = l >> 4;
+    const LSwz<OT, DK> vWM{buf + B::WM}, vKD{buf + B::KD}, vQG{buf + B::QG};
+    const LSwz<OT, CH> vM{buf + B::M};
     if (TRAIN) {  // chunk start state -> pending row-major store
         stage_state<OT, DK>(stage, S);
         unstage_state<OT, DK>(stage, pd.st);
@@ -205,9 +179,9 @@ __device__ __forceinline__ void fwd_step(const Args& a, int c, const lds_char* b
     for (int t = 0; t < 4; ++t) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) mma(acc, lds_frag<OT>(buf + B::WM + (t * KB + kb) * B::FB), SB[kb]);
+        for (int kb = 0; kb < KB; ++kb) mma(acc, lfrag_rowk<OT, OT>(vWM, 16 * t, 32 * kb), SB[kb]);
         float u[4];
-        lds_ld4(buf + B::U + (t * 256 + l * 4) * (int)sizeof(OT), u, OT());
+        lds_get4<OT>(buf + B::U + (t * 256 + l * 4) * (int)sizeof(OT), u);
         f32x4 uu = {u[0], u[1], u[2], u[3]};
         D[t] = uu - acc;
     }
@@ -218,10 +192,10 @@ __device__ __forceinline__ void fwd_step(const Args& a, int c, const lds_char* b
 #pragma unroll
     for (int at = 0; at < AT; ++at) {
         float g4[4];
-        lds_ld4(buf + B::GC + (16 * at + 4 * lq) * 4, g4, 0.f);
+        lds_get4<float>(buf + B::GC + (16 * at + 4 * lq) * 4, g4);
         f32x4 acc = {g4[0] * S[at][0], g4[1] * S[at][1], g4[2] * S[at][2], g4[3] * S[at][3]};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(acc, lds_frag<OT>(buf + B::KD + (at * 2 + kb) * B::FB), DB[kb]);
+        for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vKD, 16 * at, 32 * kb), DB[kb]);
         S[at] = acc;
     }
     // O^T = S^T Qg^T + Delta^T M^T (uses the chunk start state, still in SB)
@@ -230,9 +204,9 @@ __device__ __forceinline__ void fwd_step(const Args& a, int c, const lds_char* b
         for (int t = 0; t < 4; ++t) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) mma(acc, SB[kb], lds_frag<OT>(buf + B::QG + (t * KB + kb) * B::FB));
+            for (int kb = 0; kb < KB; ++kb) mma(acc, SB[kb], lfrag_rowk<OT, OT>(vQG, 16 * t, 32 * kb));
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) mma(acc, DB[kb], lds_frag<OT>(buf + B::MB + (t * 2 + kb) * B::FB));
+            for (int kb = 0; kb < 2; ++kb) mma(acc, DB[kb], lfrag_rowk<OT, OT>(vM, 16 * t, 32 * kb));
             pd.O[t] = acc;
         }
     }
@@ -300,27 +274,26 @@ __global__ __launch_bounds__(64) void k_fwd_chain(Args a) {
 // ============================================================================ backward chain
 template <class OT, int DK, int DV>
 struct BwdChainBuf {
-    static constexpr int FB = 512 * sizeof(OT);
-    static constexpr int KB = DK / 32;
-    static constexpr int MT = 0;                        // 8 blocks
-    static constexpr int KDR = MT + 8 * FB;             // 4*KB blocks
-    static constexpr int QGT = KDR + 4 * KB * FB;       // (DK/16)*2 blocks
-    static constexpr int WMT = QGT + (DK / 16) * 2 * FB;  // (DK/16)*2 blocks
-    static constexpr int TT = WMT + (DK / 16) * 2 * FB;   // 8 blocks
-    static constexpr int GC = TT + 8 * FB;              // DK floats
-    static constexpr int DO = GC + DK * 4;              // dO rows [64][16]
-    static constexpr int BYTES = DO + 64 * 16 * sizeof(OT);
+    static constexpr int ES = sizeof(OT);
+    static constexpr int M = 0;                   // M [64][64] swizzled
+    static constexpr int KD = M + CH * CH * ES;   // Kd [64][DK]
+    static constexpr int QG = KD + CH * DK * ES;  // Qg [64][DK]
+    static constexpr int WM = QG + CH * DK * ES;  // Wm [64][DK]
+    static constexpr int T = WM + CH * DK * ES;   // T [64][64]
+    static constexpr int GC = T + CH * CH * ES;   // DK floats
+    static constexpr int DO = GC + DK * 4;        // dO rows [64][16]
+    static constexpr int BYTES = DO + 64 * 16 * ES;
 };
 
 template <class OT, int DK, int DV>
 __device__ __forceinline__ void bwd_prefetch(const Args& a, long long cid, int c, int s, int j, lds_char* buf) {
     using B = BwdChainBuf<OT, DK, DV>;
     const Layout& L = a.L;
-    dma16(a.ws + L.o_mtA + cid * L.mtA * sizeof(OT), buf + B::MT, 8 * B::FB);
-    dma16(a.ws + L.o_kdRA + cid * L.kdRA * sizeof(OT), buf + B::KDR, 4 * B::KB * B::FB);
-    dma16(a.ws + L.o_qgtA + cid * L.qgtA * sizeof(OT), buf + B::QGT, (DK / 16) * 2 * B::FB);
-    dma16(a.ws + L.o_wmtA + cid * L.wmtA * sizeof(OT), buf + B::WMT, (DK / 16) * 2 * B::FB);
-    dma16(a.ws + L.o_ttA + cid * L.ttA * sizeof(OT), buf + B::TT, 8 * B::FB);
+    dma16(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M, CH * CH * sizeof(OT));
+    dma16(a.ws + L.o_kd + cid * L.kd * sizeof(OT), buf + B::KD, CH * DK * sizeof(OT));
+    dma16(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG, CH * DK * sizeof(OT));
+    dma16(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM, CH * DK * sizeof(OT));
+    dma16(a.ws + L.o_t + cid * L.t * sizeof(OT), buf + B::T, CH * CH * sizeof(OT));
     dma4(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC, DK * 4);
     // dO rows of this slice: row r, 16 columns; 4 bytes per lane, 256 bytes per instruction
     const int l = lane_id();
@@ -368,6 +341,8 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4 (&dS)
     using FT = typename Frag<OT>::type;
     constexpr int KB = DK / 32, AT = DK / 16;
     const int l = lane_id(), li = l & 15, lq = l >> 4;
+    const LSwz<OT, DK> vKD{buf + B::KD}, vQG{buf + B::QG}, vWM{buf + B::WM};
+    const LSwz<OT, CH> vM{buf + B::M}, vT{buf + B::T};
     // gradient w.r.t. this chunk's end state -> pending row-major store
     stage_state<OT, DK>(stage, dS);
     unstage_state<OT, DK>(stage, pd.st);
@@ -376,7 +351,7 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4 (&dS)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dOB[kb][e] = lds_elem<OT>(buf + B::DO, (32 * kb + kmap(lq, e)) * 16 + li);
+        for (int e = 0; e < 8; ++e) dOB[kb][e] = lds_load<OT>(buf + B::DO + ((32 * kb + kmap(lq, e)) * 16 + li) * (int)sizeof(OT));
     FT dSB[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) dSB[kb] = frag_of<OT>(dS[2 * kb], dS[2 * kb + 1]);
@@ -386,9 +361,9 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4 (&dS)
     for (int t = 0; t < 4; ++t) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) mma(acc, lds_frag<OT>(buf + B::KDR + (t * KB + kb) * B::FB), dSB[kb]);
+        for (int kb = 0; kb < KB; ++kb) mma(acc, lfrag_rowk<OT, OT>(vKD, 16 * t, 32 * kb), dSB[kb]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(acc, lds_frag<OT>(buf + B::MT + (t * 2 + kb) * B::FB), dOB[kb]);
+        for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vM, 16 * t, 32 * kb), dOB[kb]);
         dD[t] = acc;
     }
     FT dDB[2];
@@ -398,13 +373,13 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4 (&dS)
 #pragma unroll
     for (int at = 0; at < AT; ++at) {
         float g4[4];
-        lds_ld4(buf + B::GC + (16 * at + 4 * lq) * 4, g4, 0.f);
+        lds_get4<float>(buf + B::GC + (16 * at + 4 * lq) * 4, g4);
         f32x4 pos = {g4[0] * dS[at][0], g4[1] * dS[at][1], g4[2] * dS[at][2], g4[3] * dS[at][3]};
         f32x4 neg = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            mma(neg, lds_frag<OT>(buf + B::WMT + (at * 2 + kb) * B::FB), dDB[kb]);
-            mma(pos, lds_frag<OT>(buf + B::QGT + (at * 2 + kb) * B::FB), dOB[kb]);
+            mma(neg, lfrag_colk<OT, OT>(vWM, 16 * at, 32 * kb), dDB[kb]);
+            mma(pos, lfrag_colk<OT, OT>(vQG, 16 * at, 32 * kb), dOB[kb]);
         }
         dS[at] = pos - neg;
     }
@@ -413,7 +388,7 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4 (&dS)
     for (int t = 0; t < 4; ++t) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(acc, lds_frag<OT>(buf + B::TT + (t * 2 + kb) * B::FB), dDB[kb]);
+        for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vT, 16 * t, 32 * kb), dDB[kb]);
         pd.Y[t] = acc;
     }
     pd.c = c;

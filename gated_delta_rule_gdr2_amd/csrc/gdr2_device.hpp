@@ -176,6 +176,132 @@ __device__ __forceinline__ typename Frag<OT>::type frag_colk(const XT* X, int ld
     return f;
 }
 
+// ----------------------------------------------------------------------------- LDS address space
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <class T>
+__device__ __forceinline__ T lds_load(const lds_char* p) {
+    typedef __attribute__((address_space(3))) const T TA;
+    return *(const TA*)p;
+}
+template <class T>
+__device__ __forceinline__ void lds_store(lds_char* p, const T& v) {
+    typedef __attribute__((address_space(3))) T TA;
+    *(TA*)p = v;
+}
+
+// Swizzled row-major tiles. A matrix with RL elements per row is stored row by
+// row, but the 16-byte chunks of row r are permuted: chunk c sits at position
+// c ^ (r mod chunks-per-row). Row reads (16 lanes on 16 rows, same columns) and
+// the transposing reads below (4 consecutive rows per 16 lanes) then spread over
+// all LDS banks although the rows are not padded, so a tile can be copied into
+// LDS verbatim by DMA and read back conflict-free.
+template <class OT, int RL>
+__device__ __forceinline__ int swz(int r, int c) {
+    constexpr int EPC = 16 / (int)sizeof(OT);  // elements per 16-byte chunk
+    constexpr int NCH = RL / EPC;              // chunks per row
+    return r * RL + (((c / EPC) ^ (r & (NCH - 1))) * EPC) + (c % EPC);
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group the
+// hardware returns result[k][e] = src[4e + k/4][k%4], where src[s] are the four
+// 16-bit values lane s addressed. Hence, if lane (li, lq) addresses row
+// k0 + 4*lq + li/4, columns c0 + 4*(li%4) .. +3 of a row-major bf16 matrix, it
+// receives X[k0 + 4*lq + e][c0 + li], e = 0..3: one half of a fragment whose K
+// index runs down the rows.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const lds_char* p) {
+    typedef __attribute__((address_space(3))) bf16x4 T4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((T4*)p);
+}
+
+// ----------------------------------------------------------------------------- LDS fragment reads
+// Views of a matrix held in LDS: element (r, c) lives at byte offset off(r, c).
+template <class XT>
+struct LPad {  // padded row-major, leading dimension ld (elements)
+    const lds_char* p;
+    int ld;
+    __device__ __forceinline__ int off(int r, int c) const { return (r * ld + c) * (int)sizeof(XT); }
+};
+template <class XT, int RL>
+struct LSwz {  // swizzled tile with RL elements per row
+    const lds_char* p;
+    __device__ __forceinline__ int off(int r, int c) const { return swz<XT, RL>(r, c) * (int)sizeof(XT); }
+};
+
+template <class XT>
+__device__ __forceinline__ void lds_get4(const lds_char* p, float out[4]) {
+    if constexpr (sizeof(XT) == 2) {
+        bf16x4 v = lds_load<bf16x4>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = (float)v[i];
+    } else {
+        f32x4 v = lds_load<f32x4>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = v[i];
+    }
+}
+template <class XT>
+__device__ __forceinline__ float lds_get1(const lds_char* p) {
+    if constexpr (sizeof(XT) == 2)
+        return (float)lds_load<bf16>(p);
+    else
+        return lds_load<float>(p);
+}
+
+// rowk: lane (li, lq) gets X[row0 + li][k0 + kmap(lq, e)]; optional fp32 per-K scale in LDS
+template <class OT, class XT, class V>
+__device__ __forceinline__ typename Frag<OT>::type lfrag_rowk(const V& m, int row0, int k0,
+                                                              const lds_char* kscale = nullptr) {
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    const int r = row0 + li;
+    float a[4], b[4];
+    lds_get4<XT>(m.p + m.off(r, k0 + 4 * lq), a);
+    lds_get4<XT>(m.p + m.off(r, k0 + 16 + 4 * lq), b);
+    if (kscale) {
+        float sa[4], sb[4];
+        lds_get4<float>(kscale + (k0 + 4 * lq) * 4, sa);
+        lds_get4<float>(kscale + (k0 + 16 + 4 * lq) * 4, sb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[i] *= sa[i];
+            b[i] *= sb[i];
+        }
+    }
+    typename Frag<OT>::type f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i] = to_ot<OT>(a[i]);
+        f[4 + i] = to_ot<OT>(b[i]);
+    }
+    return f;
+}
+// colk: lane (li, lq) gets X[k0 + kmap(lq, e)][col0 + li], scaled by rs0 (e < 4) / rs1.
+// bf16: two transposing reads; fp32: eight scalar reads.
+template <class OT, class XT, class V>
+__device__ __forceinline__ typename Frag<OT>::type lfrag_colk(const V& m, int col0, int k0, float rs0 = 1.f,
+                                                              float rs1 = 1.f) {
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    typename Frag<OT>::type f;
+    if constexpr (sizeof(XT) == 2) {
+        const int r = k0 + 4 * lq + (li >> 2), c = col0 + 4 * (li & 3);
+        bf16x4 v0 = lds_read_tr16(m.p + m.off(r, c));
+        bf16x4 v1 = lds_read_tr16(m.p + m.off(r + 16, c));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = to_ot<OT>((float)v0[e] * rs0);
+            f[4 + e] = to_ot<OT>((float)v1[e] * rs1);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = to_ot<OT>(lds_get1<XT>(m.p + m.off(k0 + 4 * lq + e, col0 + li)) * rs0);
+            f[4 + e] = to_ot<OT>(lds_get1<XT>(m.p + m.off(k0 + 16 + 4 * lq + e, col0 + li)) * rs1);
+        }
+    }
+    return f;
+}
+
 // ----------------------------------------------------------------------------- global fragments
 // A fragment block (one 16x32 operand) is stored lane-major: 64 lanes x 8 elements.
 template <class OT>

@@ -1,4 +1,4 @@
-// Forward pass of the Gated Delta Rule-2 operator on gfx950.
+// Forward pass of the Gated Delta Rule-2 operator on gfx950: the intra-chunk kernel.
 //
 // Operator ("Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention",
 // anthology record LIT-802, takeaway 1; paper Sec. 3.1 Eqs. 8-10):
@@ -13,15 +13,14 @@
 //   O = Qg S + M Delta,  S' = diag(exp gam_C) S + Kd^T Delta
 // with Kb = b*k*exp(gam), Qg = q*exp(gam), Kd = k*exp(gam_C - gam).
 //
-// Kernels:
-//   k_fwd_intra : one workgroup per chunk, fully parallel. Builds A and M on
-//                 MFMA, inverts (I + A) in fp32 (16x16 diagonal blocks by
-//                 substitution, off-diagonal blocks on fp32 MFMA), forms U and
-//                 Wm on MFMA, and writes every per-chunk operand the two state
-//                 chains need, already in MFMA fragment order.
-//   k_fwd_chain : (gdr2_chain.hip) one wave per (sequence, 16-column slice of
-//                 the value axis), walks the chunks in order with the state in
-//                 accumulator registers.
+// k_fwd_intra: one workgroup (4 waves) per chunk, fully parallel. It builds A
+// and M on MFMA from the block-split factors, inverts (I + A) in fp32 (16x16
+// diagonal blocks by substitution from registers, off-diagonal blocks on fp32
+// MFMA), forms U and Wm on MFMA, and writes the per-chunk operands of the two
+// state chains (gdr2_chain.hip): Wm, Kd, Qg, M and (training) T as swizzled
+// tiles, U as accumulator tiles, exp(gam_C). Phases reuse LDS (A over the
+// query factors, T over the key factors once each is dead) so that two
+// workgroups fit on one compute unit.
 #include "gdr2_intra_common.hpp"
 #include "gdr2_kernels.hpp"
 
@@ -29,40 +28,46 @@ namespace gdr2 {
 
 template <class OT, int DK, int DV>
 struct FwdLds {
+    static constexpr int ES = sizeof(OT);
     static constexpr int LDK = DK + pad_ot<OT>();
     static constexpr int LDV = DV + pad_ot<OT>();
-    static constexpr int LDC = CH + 4;             // fp32 [CH][CH]
-    static constexpr int LDCO = CH + pad_ot<OT>();  // OT [CH][CH] and [DK][CH]
-    static constexpr size_t XA = 0;
-    static constexpr size_t XM = XA + sizeof(OT) * CH * LDK;
-    static constexpr size_t Y = XM + sizeof(OT) * CH * LDK;
-    static constexpr size_t X = Y + sizeof(OT) * CH * LDK;
-    static constexpr size_t A = X + sizeof(OT) * CH * LDV;
-    static constexpr size_t T = A + sizeof(float) * CH * LDC;
-    static constexpr size_t M = T + sizeof(float) * CH * LDC;
-    static constexpr size_t WT = M + sizeof(OT) * CH * LDCO;
-    static constexpr size_t F = WT + sizeof(OT) * DK * LDCO;
-    static constexpr size_t BYTES = F + sizeof(float) * F_ROWS * DK;
+    static constexpr int LDC = CH + 4;  // fp32 [CH][CH]
+    static constexpr int KMAT = CH * LDK * ES;
+    static constexpr int CMAT = CH * LDC * 4;
+    static constexpr int SLOT = KMAT > CMAT ? KMAT : CMAT;
+    static constexpr int XA = 0;
+    static constexpr int SLOTM = XA + KMAT;     // XM, later A
+    static constexpr int SLOTY = SLOTM + SLOT;  // Y, later T
+    static constexpr int X = SLOTY + SLOT;
+    static constexpr int F = X + CH * LDV * ES;
+    static constexpr int BYTES = F + F_ROWS * DK * 4;
 };
 
 // Blocked inverse of the unit lower-triangular (I + A), A in sA (fp32), into sT.
-// Diagonal 16x16 blocks by forward substitution (one wave, lane = block x column);
-// then T_RI = -T_RR * sum_{K=I}^{R-1} A_RK T_KI on fp32 MFMA, one level at a time.
-__device__ __forceinline__ void blocked_inverse(const float* sA, float* sT, int LDC) {
+// Diagonal 16x16 blocks by forward substitution (one wave, lane = block x column,
+// the block's rows read into registers first); then
+// T_RI = -T_RR * sum_{K=I}^{R-1} A_RK T_KI on fp32 MFMA, one level at a time.
+__device__ __forceinline__ void blocked_inverse(const lds_char* sA, lds_char* sT, int LDC) {
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, li = l & 15, lq = l >> 4;
+    auto A = [&](int r, int c) { return sA + (r * LDC + c) * 4; };
+    auto Tp = [&](int r, int c) { return sT + (r * LDC + c) * 4; };
     if (wv == 0) {
         const int D = lq, j = li;
+        float arow[16][16];
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+#pragma unroll
+            for (int c4 = 0; c4 < r; c4 += 4) lds_get4<float>(A(16 * D + r, 16 * D + c4), &arow[r][c4]);
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float acc = (r == j) ? 1.f : 0.f;
-            const float* arow = sA + (16 * D + r) * LDC + 16 * D;
 #pragma unroll
-            for (int i = 0; i < r; ++i) acc -= arow[i] * x[i];
+            for (int i = 0; i < r; ++i) acc -= arow[r][i] * x[i];
             x[r] = acc;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sT[(16 * D + r) * LDC + 16 * D + j] = x[r];
+        for (int r = 0; r < 16; ++r) lds_store<float>(Tp(16 * D + r, 16 * D + j), x[r]);
     }
     __syncthreads();
 #pragma unroll
@@ -71,39 +76,44 @@ __device__ __forceinline__ void blocked_inverse(const float* sA, float* sT, int 
             const int I = wv, R = wv + lev;
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
             for (int K = I; K < R; ++K) {
-                float a[4], b[4];
-                ld4(sA + (16 * R + li) * LDC + 16 * K + 4 * lq, a);
+                float a4[4], b4[4];
+                lds_get4<float>(A(16 * R + li, 16 * K + 4 * lq), a4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) b[e] = sT[(16 * K + 4 * lq + e) * LDC + 16 * I + li];
-                mma_k16_f32(z, a, b);
+                for (int e = 0; e < 4; ++e) b4[e] = lds_load<float>(Tp(16 * K + 4 * lq + e, 16 * I + li));
+                mma_k16_f32(z, a4, b4);
             }
-            float a[4], b[4] = {z[0], z[1], z[2], z[3]};
-            ld4(sT + (16 * R + li) * LDC + 16 * R + 4 * lq, a);
+            float a4[4], b4[4] = {z[0], z[1], z[2], z[3]};
+            lds_get4<float>(Tp(16 * R + li, 16 * R + 4 * lq), a4);
             f32x4 t = {0.f, 0.f, 0.f, 0.f};
-            mma_k16_f32(t, a, b);
+            mma_k16_f32(t, a4, b4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sT[(16 * R + 4 * lq + i) * LDC + 16 * I + li] = -t[i];
+            for (int i = 0; i < 4; ++i) lds_store<float>(Tp(16 * R + 4 * lq + i, 16 * I + li), -t[i]);
         }
         __syncthreads();
     }
 }
 
+// upper 16x16 block (R, I), I > R, number u = 0..5
+__device__ __forceinline__ void upper_ri(int u, int& R, int& I) {
+    R = u < 3 ? 0 : (u < 5 ? 1 : 2);
+    I = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
+}
+
 template <class OT, int DK, int DV, bool TRAIN>
-__global__ __launch_bounds__(256) void k_fwd_intra(Args a) {
+__global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
     using LS = FwdLds<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
-    constexpr int LDK = LS::LDK, LDV = LS::LDV, LDC = LS::LDC, LDCO = LS::LDCO;
+    constexpr int LDK = LS::LDK, LDV = LS::LDV, LDC = LS::LDC;
     constexpr int KB = DK / 32;
-    extern __shared__ __align__(16) char smem[];
-    OT* sXA = (OT*)(smem + LS::XA);
-    OT* sXM = (OT*)(smem + LS::XM);
-    OT* sY = (OT*)(smem + LS::Y);
-    OT* sX = (OT*)(smem + LS::X);
-    float* sA = (float*)(smem + LS::A);
-    float* sT = (float*)(smem + LS::T);
-    OT* sM = (OT*)(smem + LS::M);
-    OT* sWt = (OT*)(smem + LS::WT);
-    float* sF = (float*)(smem + LS::F);
+    extern __shared__ __align__(16) char smem_[];
+    lds_char* smem = (lds_char*)smem_;
+    lds_char* sXA = smem + LS::XA;
+    lds_char* sXM = smem + LS::SLOTM;
+    lds_char* sA = smem + LS::SLOTM;
+    lds_char* sY = smem + LS::SLOTY;
+    lds_char* sT = smem + LS::SLOTY;
+    lds_char* sX = smem + LS::X;
+    lds_char* sF = smem + LS::F;
 
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, li = l & 15, lq = l >> 4;
     const long long cid = blockIdx.x;
@@ -112,153 +122,116 @@ __global__ __launch_bounds__(256) void k_fwd_intra(Args a) {
     const int t0 = c * CH;
     const int nvalid = min(CH, a.T - t0);
     const size_t rowk0 = ((size_t)bidx * a.T + t0) * a.H + h;  // token-row index of row 0
+    const size_t rsk = (size_t)a.H * DK, rsv = (size_t)a.H * DV;
     const Layout& L = a.L;
-    char* ws = a.ws;
+    OT* qg_out = (OT*)(a.ws + L.o_qg) + cid * L.qg;
+    OT* kd_out = (OT*)(a.ws + L.o_kd) + cid * L.kd;
+    OT* m_out = (OT*)(a.ws + L.o_m) + cid * L.m;
+    OT* wm_out = (OT*)(a.ws + L.o_wm) + cid * L.wm;
+    OT* u_out = (OT*)(a.ws + L.o_u) + cid * L.u;
+    float* gc_out = (float*)(a.ws + L.o_gc) + cid * L.gc;
 
-    // ---- phase 1: cumulative decay, factors, X = w*v
-    float gam[DK / 64][4][4];
-    chunk_factors<OT, DK>((const OT*)a.g + rowk0 * DK, (const OT*)a.q + rowk0 * DK, (const OT*)a.k + rowk0 * DK,
-                          (const OT*)a.b + rowk0 * DK, (size_t)a.H * DK, nvalid, gam, sXA, sXM, sY, LDK, sF,
-                          (float*)(ws + L.o_gc) + cid * L.gc);
-    chunk_x<OT, DV>((const OT*)a.v + rowk0 * DV, (const OT*)a.w + rowk0 * DV, (size_t)a.H * DV, nvalid, sX, LDV);
-    // zero the upper blocks of M and T
-    for (int idx = tid; idx < CH * CH; idx += 256) {
-        const int r = idx / CH, cc = idx % CH;
-        if ((cc >> 4) > (r >> 4)) {
-            sM[r * LDCO + cc] = to_ot<OT>(0.f);
-            sT[r * LDC + cc] = 0.f;
+    // ---- phase 1: cumulative decay, factors, Qg / Kd / exp(gam_C) out, X = w*v
+    for (int at = wv; at < DK / 16; at += 4) {
+        const int ch0 = 16 * at + 4 * lq;
+        float gam[4][4], g0[4][4], ge[4][4];
+        chunk_gamma((const OT*)a.g + rowk0 * DK, rsk, ch0, nvalid, gam, g0, ge);
+        write_factors<DK>(sF, ch0, g0, ge);
+        if (li == 0) {
+            float gcv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gcv[i] = __expf(ge[3][i]);
+            st4(gc_out + ch0, gcv);
         }
+        scaled_factors<OT, DK>((const OT*)a.q + rowk0 * DK, (const OT*)a.k + rowk0 * DK,
+                               (const OT*)a.b + rowk0 * DK, rsk, ch0, nvalid, gam, g0, ge, sXA, sXM, sY, LDK,
+                               qg_out, kd_out);
     }
+    for (int jt = wv; jt < DV / 16; jt += 4)
+        chunk_x_tile((const OT*)a.v + rowk0 * DV, (const OT*)a.w + rowk0 * DV, rsv, jt, nvalid, sX, LDV);
     __syncthreads();
 
-    // ---- phase 2: A (strictly lower) and M (lower) per 16x16 block pair
-    for (int p = wv; p < 2 * NPAIR; p += 4) {
-        const bool isM = p >= NPAIR;
-        const int pp = isM ? p - NPAIR : p;
+    // ---- phase 2a: M = lower(Qg Khat^T), computed as M^T tiles, out to global
+    const LPad<OT> vXA{sXA, LDK}, vXM{sXM, LDK}, vY{sY, LDK}, vX{sX, LDV};
+    for (int p = wv; p < NPAIR; p += 4) {
         int R, I;
-        pair_ri(pp, R, I);
+        pair_ri(p, R, I);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            FT af = frag_rowk_scaled<OT, OT>(isM ? sXM : sXA, LDK, 16 * R, 32 * kb, sF + (F_S + pp) * DK);
-            FT bf = frag_rowk<OT>(sY, LDK, 16 * I, 32 * kb);
-            mma(acc, af, bf);
-        }
+        for (int kb = 0; kb < KB; ++kb)
+            mma(acc, lfrag_rowk<OT, OT>(vY, 16 * I, 32 * kb),
+                lfrag_rowk<OT, OT>(vXM, 16 * R, 32 * kb, sF + (F_S + p) * DK * 4));
+        float v[4];  // lane holds M[16R + li][16I + 4lq + i]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * R + 4 * lq + i, col = 16 * I + li;
-            float v = acc[i];
-            if (R == I && (isM ? (col > row) : (col >= row))) v = 0.f;
-            if (isM)
-                sM[row * LDCO + col] = to_ot<OT>(v);
-            else
-                sA[row * LDC + col] = v;
-        }
+        for (int i = 0; i < 4; ++i) v[i] = (R == I && 4 * lq + i > li) ? 0.f : acc[i];
+        st4(m_out + swz<OT, CH>(16 * R + li, 16 * I + 4 * lq), v);
     }
-    __syncthreads();
+    for (int u = wv; u < 6; u += 4) {
+        int R, I;
+        upper_ri(u, R, I);
+        const float z[4] = {0.f, 0.f, 0.f, 0.f};
+        st4(m_out + swz<OT, CH>(16 * R + li, 16 * I + 4 * lq), z);
+    }
+    __syncthreads();  // XM is dead from here on; its slot becomes A
+
+    // ---- phase 2b: A = strict_lower(Kb Khat^T), fp32 into LDS
+    for (int p = wv; p < NPAIR; p += 4) {
+        int R, I;
+        pair_ri(p, R, I);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            mma(acc, lfrag_rowk<OT, OT>(vY, 16 * I, 32 * kb),
+                lfrag_rowk<OT, OT>(vXA, 16 * R, 32 * kb, sF + (F_S + p) * DK * 4));
+        float v[4];  // lane holds A[16R + li][16I + 4lq + i]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (R == I && 4 * lq + i >= li) ? 0.f : acc[i];
+        lds_put4<float>(sA + ((16 * R + li) * LDC + 16 * I + 4 * lq) * 4, v);
+    }
+    __syncthreads();  // Y is dead from here on; its slot becomes T
 
     // ---- phase 3: T = (I + A)^-1
+    for (int idx = tid; idx < 6 * 64; idx += 256) {  // zero the upper blocks of T
+        int R, I;
+        upper_ri(idx / 64, R, I);
+        const int e = idx % 64;
+        const float z[4] = {0.f, 0.f, 0.f, 0.f};
+        lds_put4<float>(sT + ((16 * R + e / 4) * LDC + 16 * I + 4 * (e % 4)) * 4, z);
+    }
     blocked_inverse(sA, sT, LDC);
 
-    // ---- phase 4: U = T X (tiles) and Wm^T = Kb^T T^T (-> A fragments of Wm)
+    // ---- phase 4: U = T X (tiles) and Wm = T Kb (computed as Wm^T tiles -> row pieces)
     {
-        const int tt = wv;  // time tile of U rows / Wm rows
+        const int tt = wv;           // token tile of the U / Wm rows
+        const int nkb = tt / 2 + 1;  // T is lower triangular
+        const LPad<float> vT{sT, LDC};
         FT aT[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) aT[kb] = frag_rowk_f32<OT>(sT, LDC, 16 * tt, 32 * kb);
-        const int nkb = tt / 2 + 1;  // T is lower triangular
-        OT* u = (OT*)(ws + L.o_u) + cid * L.u;
+        for (int kb = 0; kb < 2; ++kb) aT[kb] = lfrag_rowk<OT, float>(vT, 16 * tt, 32 * kb);
         for (int j = 0; j < DV / 16; ++j) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int kb = 0; kb < nkb; ++kb) mma(acc, aT[kb], frag_colk<OT, OT>(sX, LDV, 16 * j, 32 * kb));
-            store_tile<OT>(u + (j * 4 + tt) * 256, acc);
+            for (int kb = 0; kb < nkb; ++kb) mma(acc, aT[kb], lfrag_colk<OT, OT>(vX, 16 * j, 32 * kb));
+            store_tile<OT>(u_out + (j * 4 + tt) * 256, acc);
         }
-        OT* wm = (OT*)(ws + L.o_wmA) + cid * L.wmA;
-        for (int kb2 = 0; kb2 < KB; ++kb2) {
-            f32x4 wt[2];
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int at = 2 * kb2 + h2;  // key-channel tile
-                const int col = 16 * at + li;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                for (int kb = 0; kb < nkb; ++kb) {
-                    FT ak = frag_colk<OT, OT>(sXA, LDK, 16 * at, 32 * kb, sF[(F_ER0 + 2 * kb) * DK + col],
-                                              sF[(F_ER0 + 2 * kb + 1) * DK + col]);
-                    mma(acc, ak, aT[kb]);
-                }
-                wt[h2] = acc;
-                if (TRAIN) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sWt[(16 * at + 4 * lq + i) * LDCO + 16 * tt + li] = to_ot<OT>(acc[i]);
-                }
+        for (int at = 0; at < DK / 16; ++at) {
+            const int col = 16 * at + li;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < nkb; ++kb) {
+                const float f0 = lds_load<float>(sF + ((F_ER0 + 2 * kb) * DK + col) * 4);
+                const float f1 = lds_load<float>(sF + ((F_ER0 + 2 * kb + 1) * DK + col) * 4);
+                mma(acc, lfrag_colk<OT, OT>(vXA, 16 * at, 32 * kb, f0, f1), aT[kb]);
             }
-            store_frag<OT>(wm + (tt * KB + kb2) * 512, frag_of<OT>(wt[0], wt[1]));
+            float v[4] = {acc[0], acc[1], acc[2], acc[3]};  // Wm[16tt + li][16at + 4lq + i]
+            st4(wm_out + swz<OT, DK>(16 * tt + li, 16 * at + 4 * lq), v);
         }
     }
-    __syncthreads();
-
-    // ---- phase 5: operand fragments for the state chains
-    {
-        OT* kdA = (OT*)(ws + L.o_kdA) + cid * L.kdA;
-        OT* qgB = (OT*)(ws + L.o_qgB) + cid * L.qgB;
-        OT* mB = (OT*)(ws + L.o_mB) + cid * L.mB;
-        constexpr int N_KDA = (DK / 16) * 2, N_QGB = 4 * KB, N_MB = 8;
-        constexpr int N_FWD = N_KDA + N_QGB + N_MB;
-        constexpr int N_MTA = 8, N_KDRA = 4 * KB, N_QGTA = (DK / 16) * 2, N_WMTA = (DK / 16) * 2, N_TTA = 8;
-        constexpr int N_ALL = N_FWD + (TRAIN ? N_MTA + N_KDRA + N_QGTA + N_WMTA + N_TTA : 0);
-        for (int f = wv; f < N_ALL; f += 4) {
-            int x = f;
-            if (x < N_KDA) {  // A fragments of Kd^T: rows = key channel, K = time
-                const int mt = x / 2, kb = x % 2, col = 16 * mt + li;
-                store_frag<OT>(kdA + x * 512, frag_colk<OT, OT>(sY, LDK, 16 * mt, 32 * kb, sF[(F_ECE + 2 * kb) * DK + col],
-                                                                sF[(F_ECE + 2 * kb + 1) * DK + col]));
-                continue;
-            }
-            x -= N_KDA;
-            if (x < N_QGB) {  // B fragments of Qg^T: K = key channel, N = time
-                const int nt = x / KB, kb = x % KB;
-                store_frag<OT>(qgB + x * 512, frag_rowk_scaled<OT, OT>(sXM, LDK, 16 * nt, 32 * kb, sF + (F_ER0 + nt) * DK));
-                continue;
-            }
-            x -= N_QGB;
-            if (x < N_MB) {  // B fragments of M^T: K = source token i, N = target token r
-                const int nt = x / 2, kb = x % 2;
-                store_frag<OT>(mB + x * 512, frag_rowk<OT>(sM, LDCO, 16 * nt, 32 * kb));
-                continue;
-            }
-            x -= N_MB;
-            if (!TRAIN) continue;
-            if (x < N_MTA) {  // A fragments of M^T
-                const int mt = x / 2, kb = x % 2;
-                store_frag<OT>((OT*)(ws + L.o_mtA) + cid * L.mtA + x * 512, frag_colk<OT, OT>(sM, LDCO, 16 * mt, 32 * kb));
-                continue;
-            }
-            x -= N_MTA;
-            if (x < N_KDRA) {  // A fragments of Kd: rows = time, K = key channel
-                const int mt = x / KB, kb = x % KB;
-                store_frag<OT>((OT*)(ws + L.o_kdRA) + cid * L.kdRA + x * 512,
-                               frag_rowk_scaled<OT, OT>(sY, LDK, 16 * mt, 32 * kb, sF + (F_ECE + mt) * DK));
-                continue;
-            }
-            x -= N_KDRA;
-            if (x < N_QGTA) {  // A fragments of Qg^T: rows = key channel, K = time
-                const int mt = x / 2, kb = x % 2, col = 16 * mt + li;
-                store_frag<OT>((OT*)(ws + L.o_qgtA) + cid * L.qgtA + x * 512,
-                               frag_colk<OT, OT>(sXM, LDK, 16 * mt, 32 * kb, sF[(F_ER0 + 2 * kb) * DK + col],
-                                                 sF[(F_ER0 + 2 * kb + 1) * DK + col]));
-                continue;
-            }
-            x -= N_QGTA;
-            if (x < N_WMTA) {  // A fragments of Wm^T: rows = key channel, K = time
-                const int mt = x / 2, kb = x % 2;
-                store_frag<OT>((OT*)(ws + L.o_wmtA) + cid * L.wmtA + x * 512, frag_rowk<OT>(sWt, LDCO, 16 * mt, 32 * kb));
-                continue;
-            }
-            x -= N_WMTA;
-            {  // A fragments of T^T: rows = source token i, K = target token r
-                const int mt = x / 2, kb = x % 2;
-                store_frag<OT>((OT*)(ws + L.o_ttA) + cid * L.ttA + x * 512, frag_colk<OT, float>(sT, LDC, 16 * mt, 32 * kb));
-            }
+    if (TRAIN) {  // T for the backward chain
+        OT* t_out = (OT*)(a.ws + L.o_t) + cid * L.t;
+        for (int idx = tid; idx < CH * CH / 4; idx += 256) {
+            const int r = idx / 16, c4 = 4 * (idx % 16);
+            float v[4];
+            lds_get4<float>(sT + (r * LDC + c4) * 4, v);
+            st4(t_out + swz<OT, CH>(r, c4), v);
         }
     }
 }

@@ -1,4 +1,4 @@
-// Shared first phase of the two intra-chunk kernels: chunk-local cumulative
+// Shared pieces of the two intra-chunk kernels: chunk-local cumulative
 // log-decay and the decay-scaled key/query factors.
 //
 // Normalising the state by the cumulative decay inside a chunk folds the
@@ -12,10 +12,10 @@
 //   E1_r = exp(gam_r - gam_R0)   (<= 1; R0 = first row of r's block R)
 //   E2_i = exp(gam_Iend - gam_i) (<= 1; Iend = last row of i's block I)
 //   s(R, I) = exp(gam_R0 - gam_Iend) (<= 1 for I < R; covers < 16 tokens for I = R)
-// Layout of this phase: wave w owns key-channel tiles [w*CPW, (w+1)*CPW) and
-// lane (li, lq) holds channels 16a + 4lq + (0..3) of token rows 16t + li,
-// t = 0..3 -- the accumulator-tile layout of a (channel x time) product, so
-// the backward kernel can reuse the same registers in its final phase.
+// Lane layout of these phases: wave w owns key-channel tiles w, w + NW, ...
+// and lane (li, lq) holds channels 16a + 4lq + (0..3) of token rows 16t + li,
+// t = 0..3 -- the accumulator-tile layout of a (channel x time) product, so the
+// backward kernel meets the same positions again in its final phase.
 #pragma once
 #include "gdr2_device.hpp"
 
@@ -43,94 +43,129 @@ __device__ __forceinline__ void ld4_row(const IT* base, size_t rs, int r, int ch
     for (int i = 0; i < 4; ++i) out[i] = ok ? out[i] : 0.f;
 }
 
-// Computes gam (registers), the factor arrays (LDS), exp(gam_C) (global) and
-// the scaled matrices XA = b*k*E1, XM = q*E1, Y = k*E2 (LDS, [CH][LDK]).
-// base_* point at token row 0 of this chunk; rs = H * DK is the token stride.
-template <class OT, int DK>
-__device__ __forceinline__ void chunk_factors(const OT* gb, const OT* qb, const OT* kb, const OT* bb,
-                                              size_t rs, int nvalid, float (&gam)[DK / 64][4][4],
-                                              OT* sXA, OT* sXM, OT* sY, int LDK, float* sF,
-                                              float* gc_out) {
-    constexpr int CPW = DK / 64;
-    const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, li = l & 15, lq = l >> 4;
+template <class OT>
+__device__ __forceinline__ void lds_put4(lds_char* p, const float v[4]) {
+    if constexpr (sizeof(OT) == 2) {
+        bf16x4 x;
 #pragma unroll
-    for (int ac = 0; ac < CPW; ++ac) {
-        const int ch0 = 16 * (wv * CPW + ac) + 4 * lq;
-        float run[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) x[i] = (bf16)v[i];
+        lds_store<bf16x4>(p, x);
+    } else {
+        f32x4 x = {v[0], v[1], v[2], v[3]};
+        lds_store<f32x4>(p, x);
+    }
+}
+
+// Per-lane cumulative log-decay for channel tile `at` (4 channels ch0..ch0+3, rows 16t+li):
+// gam[t][i] (inclusive running sum over the chunk), g0[R][i] = gam at row 16R, ge[R][i] =
+// gam at row 16R+15.
+template <class OT>
+__device__ __forceinline__ void chunk_gamma(const OT* gb, size_t rs, int ch0, int nvalid, float (&gam)[4][4],
+                                            float (&g0)[4][4], float (&ge)[4][4]) {
+    const int li = lane_id() & 15;
+    float gv[4][4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int r = 16 * t + li;
-            float gv[4];
-            ld4_row(gb, rs, r, ch0, nvalid, gv);
+    for (int t = 0; t < 4; ++t) ld4_row(gb, rs, 16 * t + li, ch0, nvalid, gv[t]);
+    float run[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float x = row_scan16(gv[i]) + run[i];
-                gam[ac][t][i] = x;
-                run[i] = row_bcast(x, 15);
-            }
-        }
-        float g0[4][4], ge[4][4];  // gam at block start / end rows, per block R
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int R = 0; R < 4; ++R)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                g0[R][i] = row_bcast(gam[ac][R][i], 0);
-                ge[R][i] = row_bcast(gam[ac][R][i], 15);
-            }
-        if (li == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = ch0 + i;
-#pragma unroll
-                for (int R = 0; R < 4; ++R) {
-                    sF[(F_ER0 + R) * DK + c] = __expf(g0[R][i]);
-                    sF[(F_ECE + R) * DK + c] = __expf(ge[3][i] - ge[R][i]);
-#pragma unroll
-                    for (int I = 0; I <= R; ++I) sF[(F_S + pair_id(R, I)) * DK + c] = __expf(g0[R][i] - ge[I][i]);
-                }
-                if (gc_out) gc_out[c] = __expf(ge[3][i]);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const float x = row_scan16(gv[t][i]) + run[i];
+            gam[t][i] = x;
+            run[i] = row_bcast(x, 15);
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int r = 16 * t + li;
-            float qv[4], kv[4], bv[4], xa[4], xm[4], y[4];
-            ld4_row(qb, rs, r, ch0, nvalid, qv);
-            ld4_row(kb, rs, r, ch0, nvalid, kv);
-            ld4_row(bb, rs, r, ch0, nvalid, bv);
+    for (int R = 0; R < 4; ++R)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float e1 = __expf(gam[ac][t][i] - g0[t][i]);
-                const float e2 = __expf(ge[t][i] - gam[ac][t][i]);
-                xa[i] = bv[i] * kv[i] * e1;
-                xm[i] = qv[i] * e1;
-                y[i] = kv[i] * e2;
-            }
-            st4(sXA + r * LDK + ch0, xa);
-            st4(sXM + r * LDK + ch0, xm);
-            st4(sY + r * LDK + ch0, y);
+        for (int i = 0; i < 4; ++i) {
+            g0[R][i] = row_bcast(gam[R][i], 0);
+            ge[R][i] = row_bcast(gam[R][i], 15);
+        }
+}
+
+// Factor arrays for the four channels ch0..ch0+3 (written by the li == 0 lanes).
+template <int DK>
+__device__ __forceinline__ void write_factors(lds_char* sF, int ch0, const float (&g0)[4][4],
+                                              const float (&ge)[4][4]) {
+    if ((lane_id() & 15) != 0) return;
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+        float e0[4], ec[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            e0[i] = __expf(g0[R][i]);
+            ec[i] = __expf(ge[3][i] - ge[R][i]);
+        }
+        lds_put4<float>(sF + ((F_ER0 + R) * DK + ch0) * 4, e0);
+        lds_put4<float>(sF + ((F_ECE + R) * DK + ch0) * 4, ec);
+#pragma unroll
+        for (int I = 0; I <= R; ++I) {
+            float sv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[i] = __expf(g0[R][i] - ge[I][i]);
+            lds_put4<float>(sF + ((F_S + pair_id(R, I)) * DK + ch0) * 4, sv);
         }
     }
 }
 
-// X = w * v into LDS [CH][LDV] (value channels, same lane layout)
-template <class OT, int DV>
-__device__ __forceinline__ void chunk_x(const OT* vb, const OT* wb, size_t rs, int nvalid, OT* sX, int LDV) {
-    constexpr int VPW = DV / 64;
-    const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, li = l & 15, lq = l >> 4;
+// XA = b*k*E1, XM = q*E1, Y = k*E2 for channel tile rows of this lane, into padded LDS
+// [CH][LDK]; optionally also Qg = q*exp(gam) and Kd = k*exp(gam_C - gam) as swizzled
+// tiles in global memory.
+template <class OT, int DK>
+__device__ __forceinline__ void scaled_factors(const OT* qb, const OT* kb, const OT* bb, size_t rs, int ch0,
+                                               int nvalid, const float (&gam)[4][4], const float (&g0)[4][4],
+                                               const float (&ge)[4][4], lds_char* sXA, lds_char* sXM,
+                                               lds_char* sY, int LDK, OT* qg_out, OT* kd_out) {
+    const int li = lane_id() & 15;
+    float qv[4][4], kv[4][4], bv[4][4];
 #pragma unroll
-    for (int jc = 0; jc < VPW; ++jc) {
-        const int ch0 = 16 * (wv * VPW + jc) + 4 * lq;
+    for (int t = 0; t < 4; ++t) {
+        ld4_row(qb, rs, 16 * t + li, ch0, nvalid, qv[t]);
+        ld4_row(kb, rs, 16 * t + li, ch0, nvalid, kv[t]);
+        ld4_row(bb, rs, 16 * t + li, ch0, nvalid, bv[t]);
+    }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int r = 16 * t + li;
-            float vv[4], ww[4], x[4];
-            ld4_row(vb, rs, r, ch0, nvalid, vv);
-            ld4_row(wb, rs, r, ch0, nvalid, ww);
+    for (int t = 0; t < 4; ++t) {
+        const int r = 16 * t + li;
+        float xa[4], xm[4], y[4], qg[4], kd[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = vv[i] * ww[i];
-            st4(sX + r * LDV + ch0, x);
+        for (int i = 0; i < 4; ++i) {
+            const float e1 = __expf(gam[t][i] - g0[t][i]);
+            const float e2 = __expf(ge[t][i] - gam[t][i]);
+            xa[i] = bv[t][i] * kv[t][i] * e1;
+            xm[i] = qv[t][i] * e1;
+            y[i] = kv[t][i] * e2;
+            qg[i] = xm[i] * __expf(g0[t][i]);
+            kd[i] = y[i] * __expf(ge[3][i] - ge[t][i]);
         }
+        const int o = (r * LDK + ch0) * (int)sizeof(OT);
+        lds_put4<OT>(sXA + o, xa);
+        lds_put4<OT>(sXM + o, xm);
+        lds_put4<OT>(sY + o, y);
+        if (qg_out) st4(qg_out + swz<OT, DK>(r, ch0), qg);
+        if (kd_out) st4(kd_out + swz<OT, DK>(r, ch0), kd);
+    }
+}
+
+// X = w * v into padded LDS [CH][LDV] for value-channel tile jt
+template <class OT>
+__device__ __forceinline__ void chunk_x_tile(const OT* vb, const OT* wb, size_t rs, int jt, int nvalid,
+                                             lds_char* sX, int LDV) {
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    const int ch0 = 16 * jt + 4 * lq;
+    float vv[4][4], ww[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        ld4_row(vb, rs, 16 * t + li, ch0, nvalid, vv[t]);
+        ld4_row(wb, rs, 16 * t + li, ch0, nvalid, ww[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = vv[t][i] * ww[t][i];
+        lds_put4<OT>(sX + ((16 * t + li) * LDV + ch0) * (int)sizeof(OT), x);
     }
 }
 
