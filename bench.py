@@ -120,6 +120,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="also run one plain device-to-device copy of MB MiB (outside the timed region), "
+                         "the reference that HBM byte counters are scaled by")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -159,6 +162,14 @@ def main():
         g2.gdr2_bwd(*(x[n] for n in names), x["h0"], x["do"], ws=ws, fwd_saved=True, grads=grads,
                     need_dh0=x["h0"] is not None, stream=stream, stage_events=be)
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(W):
         step(None)
     torch.cuda.synchronize()

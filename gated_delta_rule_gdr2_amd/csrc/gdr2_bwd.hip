@@ -29,34 +29,31 @@
 namespace gdr2 {
 
 template <class OT, int DK, int DV>
-struct BwdLds {
+struct BwdLds {  // all matrices are swizzled tiles (see swz())
     static constexpr int ES = sizeof(OT);
-    static constexpr int LDK = DK + pad_ot<OT>();
-    static constexpr int LDV = DV + pad_ot<OT>();
-    static constexpr int LDCO = CH + pad_ot<OT>();
-    static constexpr int KMAT = CH * LDK * ES;
-    static constexpr int VMAT = CH * LDV * ES;
+    static constexpr int KMAT = CH * DK * ES;
+    static constexpr int VMAT = CH * DV * ES;
     static constexpr int SLOT = KMAT > VMAT ? KMAT : VMAT;
     static constexpr int S0 = 0;             // dO, later XA
     static constexpr int S1 = S0 + SLOT;     // Delta, later XM
     static constexpr int S2 = S1 + SLOT;     // dY, later Y
-    static constexpr int DA = S2 + SLOT;     // dA [CH][LDCO]
-    static constexpr int DM = DA + CH * LDCO * ES;
-    static constexpr int F = DM + CH * LDCO * ES;
+    static constexpr int DA = S2 + SLOT;     // dA [CH][CH]
+    static constexpr int DM = DA + CH * CH * ES;
+    static constexpr int F = DM + CH * CH * ES;
     static constexpr int DMD = F + F_ROWS * DK * 4;  // diagonal of dM, fp32
     static constexpr int BYTES = DMD + CH * 4;
 };
 
-// tile dump [DV/16][4][64 lanes][4] -> padded row-major LDS [CH][ld]
+// tile dump [DV/16][4][64 lanes][4] -> swizzled LDS tile [CH][DV]
 template <class OT, int DV, int NTHR>
-__device__ __forceinline__ void undump_tiles(const OT* src, lds_char* dst, int ld) {
+__device__ __forceinline__ void undump_tiles(const OT* src, lds_char* dst) {
     for (int e = threadIdx.x; e < (DV / 16) * 4 * 64; e += NTHR) {
         const int lane = e & 63, t = (e >> 6) & 3, jj = e >> 8;
         float v[4];
         ld4(src + (size_t)e * 4, v);
         const int row = 16 * t + 4 * (lane >> 4), col = 16 * jj + (lane & 15);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_store<OT>(dst + ((row + i) * ld + col) * (int)sizeof(OT), to_ot<OT>(v[i]));
+        for (int i = 0; i < 4; ++i) lds_store<OT>(dst + swz<OT, DV>(row + i, col) * (int)sizeof(OT), to_ot<OT>(v[i]));
     }
 }
 
@@ -66,7 +63,6 @@ template <class OT, int DK, int DV>
 __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     using LS = BwdLds<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
-    constexpr int LDK = LS::LDK, LDV = LS::LDV, LDCO = LS::LDCO;
     constexpr int NW = BWD_NW, NTHR = 64 * NW;
     constexpr int KV = DV / 32;
     constexpr int CPW = (DK / 16 + NW - 1) / NW;  // key-channel tiles per wave
@@ -114,16 +110,16 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) ld4_row(dob, rsv, 16 * t + li, ch0, nvalid, x[t]);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) lds_put4<OT>(sDO + ((16 * t + li) * LDV + ch0) * (int)sizeof(OT), x[t]);
+            for (int t = 0; t < 4; ++t) lds_put4<OT>(sDO + swz<OT, DV>(16 * t + li, ch0) * (int)sizeof(OT), x[t]);
         }
     }
-    undump_tiles<OT, DV, NTHR>((const OT*)(a.ws + L.o_delta) + cid * L.delta, sDL, LDV);
-    undump_tiles<OT, DV, NTHR>((const OT*)(a.ws + L.o_dy) + cid * L.dy, sDY, LDV);
+    undump_tiles<OT, DV, NTHR>((const OT*)(a.ws + L.o_delta) + cid * L.delta, sDL);
+    undump_tiles<OT, DV, NTHR>((const OT*)(a.ws + L.o_dy) + cid * L.dy, sDY);
     for (int idx = tid; idx < CH * CH; idx += NTHR) {  // zero the upper blocks of dA, dM
         const int r = idx / CH, cc = idx % CH;
         if ((cc >> 4) > (r >> 4)) {
-            lds_store<OT>(sDA + (r * LDCO + cc) * (int)sizeof(OT), to_ot<OT>(0.f));
-            lds_store<OT>(sDM + (r * LDCO + cc) * (int)sizeof(OT), to_ot<OT>(0.f));
+            lds_store<OT>(sDA + swz<OT, CH>(r, cc) * (int)sizeof(OT), to_ot<OT>(0.f));
+            lds_store<OT>(sDM + swz<OT, CH>(r, cc) * (int)sizeof(OT), to_ot<OT>(0.f));
         }
     }
     __syncthreads();
@@ -132,7 +128,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     // The diagonal of M, q_r . k_r, does not depend on the decay; its gradient is
     // kept apart in fp32 (sDMd) so that its query-side and key-side terms cancel
     // exactly in the log-decay gradient instead of up to bf16 rounding.
-    const LPad<OT> vDO{sDO, LDV}, vDL{sDL, LDV}, vDY{sDY, LDV};
+    const LSwz<OT, DV> vDO{sDO}, vDL{sDL}, vDY{sDY};
     for (int p = wv; p < 2 * NPAIR; p += NW) {
         const bool isM = p >= NPAIR;
         int R, I;
@@ -147,7 +143,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             float v = isM ? acc[i] : -acc[i];
             if (isM && col == row) lds_store<float>(sDMd + row * 4, v);
             if (R == I && col >= row) v = 0.f;  // dA strictly lower; dM diagonal kept in sDMd
-            lds_store<OT>((isM ? sDM : sDA) + (row * LDCO + col) * (int)sizeof(OT), to_ot<OT>(v));
+            lds_store<OT>((isM ? sDM : sDA) + swz<OT, CH>(row, col) * (int)sizeof(OT), to_ot<OT>(v));
         }
     }
     __syncthreads();
@@ -232,7 +228,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             for (int t = 0; t < 4; ++t) {
                 const int r = 16 * t + li;
                 float dy[4], dvv[4], dww[4];
-                lds_get4<OT>(sDY + (r * LDV + ch0) * (int)sizeof(OT), dy);
+                lds_get4<OT>(sDY + swz<OT, DV>(r, ch0) * (int)sizeof(OT), dy);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     dvv[i] = dy[i] * ww[t][i];
@@ -260,13 +256,13 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
                 g0[R][i] = row_bcast(gam[ac][R][i], 0);
                 ge[R][i] = row_bcast(gam[ac][R][i], 15);
             }
-        scaled_factors<OT, DK>(qb, kb_, bb, rsk, ch0, nvalid, gam[ac], g0, ge, sXA, sXM, sY, LDK, nullptr,
-                               nullptr);
+        scaled_factors<OT, DK>(qb, kb_, bb, rsk, ch0, nvalid, gam[ac], g0, ge, sXA, sXM, sY, nullptr, nullptr);
     }
     __syncthreads();
 
     // ---- phase 3c: bilinear back-propagation, then the elementwise finals
-    const LPad<OT> vXA{sXA, LDK}, vXM{sXM, LDK}, vY{sY, LDK}, vDA{sDA, LDCO}, vDM{sDM, LDCO};
+    const LSwz<OT, DK> vXA{sXA}, vXM{sXM}, vY{sY};
+    const LSwz<OT, CH> vDA{sDA}, vDM{sDM};
 #pragma unroll
     for (int ac = 0; ac < CPW; ++ac) {
         const int at = wv + NW * ac;

@@ -113,16 +113,13 @@ template <class OT>
 __device__ __forceinline__ typename Frag<OT>::type frag_rowk(const OT* X, int ld, int row0, int k0) {
     const int l = lane_id(), li = l & 15, lq = l >> 4;
     const OT* p = X + (size_t)(row0 + li) * ld + k0 + 4 * lq;
-    typename Frag<OT>::type f;
-    float a[4], b[4];
-    ld4(p, a);
-    ld4(p + 16, b);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[i] = to_ot<OT>(a[i]);
-        f[4 + i] = to_ot<OT>(b[i]);
+    if constexpr (sizeof(OT) == 2) {
+        bf16x4 x0 = *(const bf16x4*)p, x1 = *(const bf16x4*)(p + 16);
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        f32x4 x0 = *(const f32x4*)p, x1 = *(const f32x4*)(p + 16);
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    return f;
 }
 // rowk from an fp32 matrix, converted to the operand type
 template <class OT>
@@ -193,15 +190,23 @@ __device__ __forceinline__ void lds_store(lds_char* p, const T& v) {
 
 // Swizzled row-major tiles. A matrix with RL elements per row is stored row by
 // row, but the 16-byte chunks of row r are permuted: chunk c sits at position
-// c ^ (r mod chunks-per-row). Row reads (16 lanes on 16 rows, same columns) and
-// the transposing reads below (4 consecutive rows per 16 lanes) then spread over
-// all LDS banks although the rows are not padded, so a tile can be copied into
-// LDS verbatim by DMA and read back conflict-free.
+// c ^ f(r). The two LDS access patterns of the MFMA fragment loads are then free
+// of bank conflicts although rows are not padded (64 banks of 4 bytes):
+//   row reads        : 16 lanes on 16 consecutive rows, same chunk;
+//   transposing reads: 16 lanes on 4 consecutive rows x 2 adjacent chunks.
+// 16 chunks per row (256-byte rows, one full bank period):
+//   f(r) = 2*(r mod 8) + (r/8 mod 2) -- a bijection on 16 rows, and 4 consecutive
+//   rows differ in bits 1-3 while the adjacent-chunk pair differs in bit 0.
+// 8 chunks per row (128-byte rows; odd rows already sit in the other half of the
+// banks): f(r) = 2*(r/2 mod 4) + (r/8 mod 2).
+// A tile is therefore copied into LDS verbatim by DMA and read back conflict-free.
 template <class OT, int RL>
 __device__ __forceinline__ int swz(int r, int c) {
     constexpr int EPC = 16 / (int)sizeof(OT);  // elements per 16-byte chunk
     constexpr int NCH = RL / EPC;              // chunks per row
-    return r * RL + (((c / EPC) ^ (r & (NCH - 1))) * EPC) + (c % EPC);
+    static_assert(NCH == 8 || NCH == 16, "swizzled tiles have 8 or 16 chunks per row");
+    const int f = NCH == 16 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+    return r * RL + (((c / EPC) ^ f) * EPC) + (c % EPC);
 }
 
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group the
@@ -249,15 +254,30 @@ __device__ __forceinline__ float lds_get1(const lds_char* p) {
         return lds_load<float>(p);
 }
 
-// rowk: lane (li, lq) gets X[row0 + li][k0 + kmap(lq, e)]; optional fp32 per-K scale in LDS
+// rowk: lane (li, lq) gets X[row0 + li][k0 + kmap(lq, e)]. When the stored type is the
+// operand type and no scale is applied the fragment is assembled from the two raw
+// loads without any conversion.
 template <class OT, class XT, class V>
 __device__ __forceinline__ typename Frag<OT>::type lfrag_rowk(const V& m, int row0, int k0,
                                                               const lds_char* kscale = nullptr) {
     const int l = lane_id(), li = l & 15, lq = l >> 4;
     const int r = row0 + li;
+    const lds_char* p0 = m.p + m.off(r, k0 + 4 * lq);
+    const lds_char* p1 = m.p + m.off(r, k0 + 16 + 4 * lq);
+    if constexpr (sizeof(XT) == sizeof(OT)) {
+        if (!kscale) {
+            if constexpr (sizeof(OT) == 2) {
+                bf16x4 x0 = lds_load<bf16x4>(p0), x1 = lds_load<bf16x4>(p1);
+                return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+                f32x4 x0 = lds_load<f32x4>(p0), x1 = lds_load<f32x4>(p1);
+                return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+    }
     float a[4], b[4];
-    lds_get4<XT>(m.p + m.off(r, k0 + 4 * lq), a);
-    lds_get4<XT>(m.p + m.off(r, k0 + 16 + 4 * lq), b);
+    lds_get4<XT>(p0, a);
+    lds_get4<XT>(p1, b);
     if (kscale) {
         float sa[4], sb[4];
         lds_get4<float>(kscale + (k0 + 4 * lq) * 4, sa);
@@ -276,11 +296,28 @@ __device__ __forceinline__ typename Frag<OT>::type lfrag_rowk(const V& m, int ro
     }
     return f;
 }
-// colk: lane (li, lq) gets X[k0 + kmap(lq, e)][col0 + li], scaled by rs0 (e < 4) / rs1.
-// bf16: two transposing reads; fp32: eight scalar reads.
+// colk: lane (li, lq) gets X[k0 + kmap(lq, e)][col0 + li], optionally scaled by rs0 (e < 4)
+// and rs1 (e >= 4). bf16: two transposing reads; fp32: eight scalar reads.
 template <class OT, class XT, class V>
-__device__ __forceinline__ typename Frag<OT>::type lfrag_colk(const V& m, int col0, int k0, float rs0 = 1.f,
-                                                              float rs1 = 1.f) {
+__device__ __forceinline__ typename Frag<OT>::type lfrag_colk(const V& m, int col0, int k0) {
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    if constexpr (sizeof(XT) == 2 && sizeof(OT) == 2) {
+        const int r = k0 + 4 * lq + (li >> 2), c = col0 + 4 * (li & 3);
+        bf16x4 v0 = lds_read_tr16(m.p + m.off(r, c));
+        bf16x4 v1 = lds_read_tr16(m.p + m.off(r + 16, c));
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        typename Frag<OT>::type f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = to_ot<OT>(lds_get1<XT>(m.p + m.off(k0 + 4 * lq + e, col0 + li)));
+            f[4 + e] = to_ot<OT>(lds_get1<XT>(m.p + m.off(k0 + 16 + 4 * lq + e, col0 + li)));
+        }
+        return f;
+    }
+}
+template <class OT, class XT, class V>
+__device__ __forceinline__ typename Frag<OT>::type lfrag_colk(const V& m, int col0, int k0, float rs0, float rs1) {
     const int l = lane_id(), li = l & 15, lq = l >> 4;
     typename Frag<OT>::type f;
     if constexpr (sizeof(XT) == 2) {

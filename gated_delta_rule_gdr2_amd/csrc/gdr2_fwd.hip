@@ -27,19 +27,16 @@
 namespace gdr2 {
 
 template <class OT, int DK, int DV>
-struct FwdLds {
+struct FwdLds {  // all matrices are swizzled tiles (see swz())
     static constexpr int ES = sizeof(OT);
-    static constexpr int LDK = DK + pad_ot<OT>();
-    static constexpr int LDV = DV + pad_ot<OT>();
-    static constexpr int LDC = CH + 4;  // fp32 [CH][CH]
-    static constexpr int KMAT = CH * LDK * ES;
-    static constexpr int CMAT = CH * LDC * 4;
+    static constexpr int KMAT = CH * DK * ES;
+    static constexpr int CMAT = CH * CH * 4;  // fp32 [CH][CH]
     static constexpr int SLOT = KMAT > CMAT ? KMAT : CMAT;
     static constexpr int XA = 0;
     static constexpr int SLOTM = XA + KMAT;     // XM, later A
     static constexpr int SLOTY = SLOTM + SLOT;  // Y, later T
     static constexpr int X = SLOTY + SLOT;
-    static constexpr int F = X + CH * LDV * ES;
+    static constexpr int F = X + CH * DV * ES;
     static constexpr int BYTES = F + F_ROWS * DK * 4;
 };
 
@@ -47,10 +44,10 @@ struct FwdLds {
 // Diagonal 16x16 blocks by forward substitution (one wave, lane = block x column,
 // the block's rows read into registers first); then
 // T_RI = -T_RR * sum_{K=I}^{R-1} A_RK T_KI on fp32 MFMA, one level at a time.
-__device__ __forceinline__ void blocked_inverse(const lds_char* sA, lds_char* sT, int LDC) {
+__device__ __forceinline__ void blocked_inverse(const lds_char* sA, lds_char* sT) {
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, li = l & 15, lq = l >> 4;
-    auto A = [&](int r, int c) { return sA + (r * LDC + c) * 4; };
-    auto Tp = [&](int r, int c) { return sT + (r * LDC + c) * 4; };
+    auto A = [&](int r, int c) { return sA + swz<float, CH>(r, c) * 4; };
+    auto Tp = [&](int r, int c) { return sT + swz<float, CH>(r, c) * 4; };
     if (wv == 0) {
         const int D = lq, j = li;
         float arow[16][16];
@@ -103,7 +100,6 @@ template <class OT, int DK, int DV, bool TRAIN>
 __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
     using LS = FwdLds<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
-    constexpr int LDK = LS::LDK, LDV = LS::LDV, LDC = LS::LDC;
     constexpr int KB = DK / 32;
     extern __shared__ __align__(16) char smem_[];
     lds_char* smem = (lds_char*)smem_;
@@ -144,15 +140,16 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
             st4(gc_out + ch0, gcv);
         }
         scaled_factors<OT, DK>((const OT*)a.q + rowk0 * DK, (const OT*)a.k + rowk0 * DK,
-                               (const OT*)a.b + rowk0 * DK, rsk, ch0, nvalid, gam, g0, ge, sXA, sXM, sY, LDK,
+                               (const OT*)a.b + rowk0 * DK, rsk, ch0, nvalid, gam, g0, ge, sXA, sXM, sY,
                                qg_out, kd_out);
     }
     for (int jt = wv; jt < DV / 16; jt += 4)
-        chunk_x_tile((const OT*)a.v + rowk0 * DV, (const OT*)a.w + rowk0 * DV, rsv, jt, nvalid, sX, LDV);
+        chunk_x_tile<OT, DV>((const OT*)a.v + rowk0 * DV, (const OT*)a.w + rowk0 * DV, rsv, jt, nvalid, sX);
     __syncthreads();
 
     // ---- phase 2a: M = lower(Qg Khat^T), computed as M^T tiles, out to global
-    const LPad<OT> vXA{sXA, LDK}, vXM{sXM, LDK}, vY{sY, LDK}, vX{sX, LDV};
+    const LSwz<OT, DK> vXA{sXA}, vXM{sXM}, vY{sY};
+    const LSwz<OT, DV> vX{sX};
     for (int p = wv; p < NPAIR; p += 4) {
         int R, I;
         pair_ri(p, R, I);
@@ -186,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
         float v[4];  // lane holds A[16R + li][16I + 4lq + i]
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = (R == I && 4 * lq + i >= li) ? 0.f : acc[i];
-        lds_put4<float>(sA + ((16 * R + li) * LDC + 16 * I + 4 * lq) * 4, v);
+        lds_put4<float>(sA + swz<float, CH>(16 * R + li, 16 * I + 4 * lq) * 4, v);
     }
     __syncthreads();  // Y is dead from here on; its slot becomes T
 
@@ -196,15 +193,15 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
         upper_ri(idx / 64, R, I);
         const int e = idx % 64;
         const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        lds_put4<float>(sT + ((16 * R + e / 4) * LDC + 16 * I + 4 * (e % 4)) * 4, z);
+        lds_put4<float>(sT + swz<float, CH>(16 * R + e / 4, 16 * I + 4 * (e % 4)) * 4, z);
     }
-    blocked_inverse(sA, sT, LDC);
+    blocked_inverse(sA, sT);
 
     // ---- phase 4: U = T X (tiles) and Wm = T Kb (computed as Wm^T tiles -> row pieces)
     {
         const int tt = wv;           // token tile of the U / Wm rows
         const int nkb = tt / 2 + 1;  // T is lower triangular
-        const LPad<float> vT{sT, LDC};
+        const LSwz<float, CH> vT{sT};
         FT aT[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) aT[kb] = lfrag_rowk<OT, float>(vT, 16 * tt, 32 * kb);
@@ -230,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
         for (int idx = tid; idx < CH * CH / 4; idx += 256) {
             const int r = idx / 16, c4 = 4 * (idx % 16);
             float v[4];
-            lds_get4<float>(sT + (r * LDC + c4) * 4, v);
+            lds_get4<float>(sT + swz<float, CH>(r, c4) * 4, v);
             st4(t_out + swz<OT, CH>(r, c4), v);
         }
     }

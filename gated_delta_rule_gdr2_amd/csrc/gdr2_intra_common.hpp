@@ -109,14 +109,14 @@ __device__ __forceinline__ void write_factors(lds_char* sF, int ch0, const float
     }
 }
 
-// XA = b*k*E1, XM = q*E1, Y = k*E2 for channel tile rows of this lane, into padded LDS
-// [CH][LDK]; optionally also Qg = q*exp(gam) and Kd = k*exp(gam_C - gam) as swizzled
+// XA = b*k*E1, XM = q*E1, Y = k*E2 for channel tile rows of this lane, into swizzled LDS
+// tiles [CH][DK]; optionally also Qg = q*exp(gam) and Kd = k*exp(gam_C - gam) as swizzled
 // tiles in global memory.
 template <class OT, int DK>
 __device__ __forceinline__ void scaled_factors(const OT* qb, const OT* kb, const OT* bb, size_t rs, int ch0,
                                                int nvalid, const float (&gam)[4][4], const float (&g0)[4][4],
                                                const float (&ge)[4][4], lds_char* sXA, lds_char* sXM,
-                                               lds_char* sY, int LDK, OT* qg_out, OT* kd_out) {
+                                               lds_char* sY, OT* qg_out, OT* kd_out) {
     const int li = lane_id() & 15;
     float qv[4][4], kv[4][4], bv[4][4];
 #pragma unroll
@@ -139,7 +139,7 @@ __device__ __forceinline__ void scaled_factors(const OT* qb, const OT* kb, const
             qg[i] = xm[i] * __expf(g0[t][i]);
             kd[i] = y[i] * __expf(ge[3][i] - ge[t][i]);
         }
-        const int o = (r * LDK + ch0) * (int)sizeof(OT);
+        const int o = swz<OT, DK>(r, ch0) * (int)sizeof(OT);
         lds_put4<OT>(sXA + o, xa);
         lds_put4<OT>(sXM + o, xm);
         lds_put4<OT>(sY + o, y);
@@ -148,10 +148,10 @@ __device__ __forceinline__ void scaled_factors(const OT* qb, const OT* kb, const
     }
 }
 
-// X = w * v into padded LDS [CH][LDV] for value-channel tile jt
-template <class OT>
+// X = w * v into a swizzled LDS tile [CH][DV] for value-channel tile jt
+template <class OT, int DV>
 __device__ __forceinline__ void chunk_x_tile(const OT* vb, const OT* wb, size_t rs, int jt, int nvalid,
-                                             lds_char* sX, int LDV) {
+                                             lds_char* sX) {
     const int l = lane_id(), li = l & 15, lq = l >> 4;
     const int ch0 = 16 * jt + 4 * lq;
     float vv[4][4], ww[4][4];
@@ -165,7 +165,7 @@ __device__ __forceinline__ void chunk_x_tile(const OT* vb, const OT* wb, size_t 
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = vv[t][i] * ww[t][i];
-        lds_put4<OT>(sX + ((16 * t + li) * LDV + ch0) * (int)sizeof(OT), x);
+        lds_put4<OT>(sX + swz<OT, DV>(16 * t + li, ch0) * (int)sizeof(OT), x);
     }
 }
 
