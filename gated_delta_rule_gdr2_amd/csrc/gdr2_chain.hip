@@ -2,41 +2,71 @@
 //
 // Only the state is carried between chunks (digg thread post 9/; anthology
 // record LIT-802, takeaway 2), so each (sequence, 16-column slice of the value
-// axis) is an independent chain over the chunks: one wave per workgroup.
+// axis) is an independent chain over the chunks:
 //
 //   forward  : Delta = U - Wm S ;  O^T = S^T Qg^T + Delta^T M^T ;
 //              S' = diag(exp gam_C) S + Kd^T Delta
 //   backward : dDelta = M^T dO + Kd dS' ; dY = T^T dDelta ;
 //              dS = diag(exp gam_C) dS' + Qg^T dO - Wm^T dDelta
 //
-// The state slice lives in MFMA accumulator registers for the whole walk and
-// feeds the next MFMA directly (see the K-slot convention in gdr2_device.hpp).
-// Per-chunk operands were written by the intra-chunk kernel as lane-major MFMA
-// fragment blocks; the chain streams them into LDS with asynchronous
-// global->LDS DMA (16 bytes per lane), double-buffered one chunk ahead, so the
-// next chunk's ~60 KB arrive while the current chunk computes. The two buffers
-// are distinct LDS objects and the loop is unrolled by two, which lets the
-// compiler see that reads of one buffer never alias the DMA into the other.
-// Global stores of a step are issued at the start of the following step, so
-// the per-step wait for the DMA never waits on them.
+// One workgroup per chain: NW = d_k / 32 compute waves and one producer wave.
+//
+// Compute waves split the key axis of the state. Wave w keeps rows 32w .. 32w + 31
+// of the state slice in MFMA accumulator registers for the whole walk and feeds
+// them straight back into the next MFMA (see the K-slot convention in
+// gdr2_device.hpp). Products that contract over the key axis (Wm S, Kd dS',
+// S^T Qg^T) are split over K: each wave forms the partial product of its own rows,
+// the partials meet in LDS behind a barrier, and each wave then updates its own
+// rows and 4 / NW token tiles of the outputs.
+//
+// The producer wave streams the per-chunk operands (swizzled tiles written by the
+// intra-chunk kernels) into LDS with asynchronous global->LDS DMA, 16 bytes per
+// lane, into two buffers. A chunk step has two phases separated by the exchange
+// barrier, and each phase reads only some of the operands (group 1 before the
+// barrier, group 2 after it), so the producer refills each group as soon as the
+// phase that reads it is over everywhere: group 2 of chunk n + 1 after barrier A of
+// step n, group 1 of chunk n + 2 after barrier B of step n. Before each barrier A it
+// waits for everything but the newest group. The compute waves issue no DMA, so
+// their LDS reads never wait for the transfers in flight, and the transfer time
+// overlaps the whole step.
 #include "gdr2_device.hpp"
 #include "gdr2_kernels.hpp"
 
 namespace gdr2 {
 
-// Copy `bytes` (a multiple of 1024) from global memory into LDS, 16 bytes per lane.
-__device__ __forceinline__ void dma16(const void* src, lds_char* dst, int bytes) {
-    const int l = lane_id();
-    for (int k = 0; k < bytes; k += 1024)
-        __builtin_amdgcn_global_load_lds((const char*)src + k + l * 16, (lds_void*)(dst + k), 16, 0, 0);
+// Workgroup barrier after this wave's LDS stores have completed (the compiler's own
+// barrier would also wait for every DMA in flight).
+__device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-// Copy `bytes` (a multiple of 256) 4 bytes per lane.
-__device__ __forceinline__ void dma4(const void* src, lds_char* dst, int bytes) {
+
+// this wave's index in the workgroup, as a wave-uniform (scalar) value
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Copy BYTES (a multiple of 1024) from global memory into LDS, 16 bytes per lane:
+// BYTES / 1024 DMA instructions.
+template <int BYTES>
+__device__ __forceinline__ void dma16(const void* src, lds_char* dst) {
+    static_assert(BYTES % 1024 == 0, "16-byte DMA copies whole 1 KB pieces");
     const int l = lane_id();
-    for (int k = 0; k < bytes; k += 256)
-        __builtin_amdgcn_global_load_lds((const char*)src + k + l * 4, (lds_void*)(dst + k), 4, 0, 0);
+#pragma unroll
+    for (int k = 0; k < BYTES / 1024; ++k)
+        __builtin_amdgcn_global_load_lds((const char*)src + k * 1024 + l * 16, (lds_void*)(dst + k * 1024), 16, 0, 0);
 }
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// Copy BYTES (a multiple of 256), 4 bytes per lane: BYTES / 256 DMA instructions.
+template <int BYTES>
+__device__ __forceinline__ void dma4(const void* src, lds_char* dst) {
+    static_assert(BYTES % 256 == 0, "4-byte DMA copies whole 256-byte pieces");
+    const int l = lane_id();
+#pragma unroll
+    for (int k = 0; k < BYTES / 256; ++k)
+        __builtin_amdgcn_global_load_lds((const char*)src + k * 256 + l * 4, (lds_void*)(dst + k * 256), 4, 0, 0);
+}
 
 // Sequence/slice mapping. Workgroups go to the 8 XCDs round-robin (XCD = id % 8);
 // when the sequence count allows, all slices of one sequence share an XCD and
@@ -52,48 +82,106 @@ __device__ __forceinline__ void chain_map(int gid, int NS, int NJ, int& s, int& 
     }
 }
 
-// Row-major [DK][DV] store of one 16-column slice of a state held as accumulator
-// tiles: transposed through LDS so each lane stores whole 16-byte row pieces.
-template <class OT, int DK>
-struct StateStore {
-    static constexpr int LDSP = 16 + 16 / (int)sizeof(OT);              // staging pitch, rows 16-B aligned
-    static constexpr int PER_LANE = DK * 16 * (int)sizeof(OT) / 16 / 64;  // 16-byte pieces per lane
-    static constexpr int BYTES = DK * LDSP * (int)sizeof(OT);
+// Row-major [DK][DV] store of one wave's 32 state rows of a 16-column slice,
+// transposed through LDS so each lane stores whole 16-byte row pieces.
+template <class OT>
+struct RowStore {
+    static constexpr int LDSP = 16 + 16 / (int)sizeof(OT);             // staging pitch, rows 16-B aligned
+    static constexpr int PER_LANE = 32 * 16 * (int)sizeof(OT) / 16 / 64;  // 16-byte pieces per lane
+    static constexpr int BYTES = 32 * LDSP * (int)sizeof(OT);           // per wave
+    static constexpr int EPP = 16 / (int)sizeof(OT);                    // elements per piece
+    static constexpr int PPR = 16 / EPP;                                // pieces per row
 };
-
-template <class OT, int DK>
-__device__ __forceinline__ void stage_state(lds_char* stage_, const f32x4 (&S)[DK / 16]) {
+// s0 / s1: accumulator tiles of rows 0..15 / 16..31; piece p = lane + 64 k covers row
+// p / PPR, columns (p % PPR) * EPP .. + EPP - 1
+template <class OT>
+__device__ __forceinline__ void stage_rows(lds_char* stage, const f32x4& s0, const f32x4& s1,
+                                           f32x4 (&pend)[RowStore<OT>::PER_LANE]) {
     typedef __attribute__((address_space(3))) OT TE;
-    TE* stage = (TE*)stage_;
-    constexpr int P = StateStore<OT, DK>::LDSP;
+    TE* st = (TE*)stage;
+    using R = RowStore<OT>;
     const int l = lane_id(), li = l & 15, lq = l >> 4;
 #pragma unroll
-    for (int at = 0; at < DK / 16; ++at)
+    for (int i = 0; i < 4; ++i) {
+        st[(4 * lq + i) * R::LDSP + li] = to_ot<OT>(s0[i]);
+        st[(16 + 4 * lq + i) * R::LDSP + li] = to_ot<OT>(s1[i]);
+    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) stage[(16 * at + 4 * lq + i) * P + li] = to_ot<OT>(S[at][i]);
-}
-// read the staged slice back as 16-byte row pieces; piece p = lane + 64 k covers
-// row p / PPR, columns (p % PPR) * EPP .. +EPP
-template <class OT, int DK>
-__device__ __forceinline__ void unstage_state(const lds_char* stage, f32x4 (&pend)[StateStore<OT, DK>::PER_LANE]) {
-    typedef __attribute__((address_space(3))) const f32x4 T4;
-    constexpr int P = StateStore<OT, DK>::LDSP;
-    constexpr int EPP = 16 / sizeof(OT), PPR = 16 / EPP;
-    const int l = lane_id();
-#pragma unroll
-    for (int k = 0; k < StateStore<OT, DK>::PER_LANE; ++k) {
-        const int p = l + 64 * k, row = p / PPR, col = (p % PPR) * EPP;
-        pend[k] = *(T4*)(stage + (row * P + col) * (int)sizeof(OT));
+    for (int k = 0; k < R::PER_LANE; ++k) {
+        const int p = l + 64 * k, row = p / R::PPR, col = (p % R::PPR) * R::EPP;
+        pend[k] = lds_load<f32x4>(stage + (row * R::LDSP + col) * (int)sizeof(OT));
     }
 }
-template <class OT, int DK, int DV>
-__device__ __forceinline__ void store_state(OT* dst, int j, const f32x4 (&pend)[StateStore<OT, DK>::PER_LANE]) {
-    constexpr int EPP = 16 / sizeof(OT), PPR = 16 / EPP;
+template <class OT, int DV>
+__device__ __forceinline__ void store_rows(OT* dst, int row0, int j, const f32x4 (&pend)[RowStore<OT>::PER_LANE]) {
+    using R = RowStore<OT>;
     const int l = lane_id();
 #pragma unroll
-    for (int k = 0; k < StateStore<OT, DK>::PER_LANE; ++k) {
-        const int p = l + 64 * k, row = p / PPR, col = (p % PPR) * EPP;
-        *(f32x4*)(dst + (size_t)row * DV + 16 * j + col) = pend[k];
+    for (int k = 0; k < R::PER_LANE; ++k) {
+        const int p = l + 64 * k, row = p / R::PPR, col = (p % R::PPR) * R::EPP;
+        *(f32x4*)(dst + (size_t)(row0 + row) * DV + 16 * j + col) = pend[k];
+    }
+}
+
+// Exchange area for the split-K partial products: accumulator tiles, one 1 KB slot each.
+__device__ __forceinline__ void xput(lds_char* x, int slot, const f32x4& v) {
+    lds_store<f32x4>(x + (slot * 64 + lane_id()) * 16, v);
+}
+__device__ __forceinline__ f32x4 xget(const lds_char* x, int slot) {
+    return lds_load<f32x4>(x + (slot * 64 + lane_id()) * 16);
+}
+
+constexpr int LDS_LIMIT = 160 * 1024;
+
+// The producer's side of a walk over NT chunks (walk index n = 0 .. NT - 1). G1(n, buf)
+// and G2(n, buf) issue the DMA of operand groups 1 and 2 of the chunk at walk index n;
+// G1N is the number of DMA instructions G1 issues. Two buffers: barriers A_n and
+// B_n of every step, as the compute waves have them. One buffer: a third barrier C_n
+// ends every step and the transfers do not overlap compute.
+template <bool DBUF, int G1N, class F1, class F2>
+__device__ __forceinline__ void produce(int NT, lds_char* b0, lds_char* b1, F1 G1, F2 G2) {
+    if (DBUF) {
+        G1(0, b0);
+        G2(0, b0);
+        if (NT > 1) {
+            G1(1, b1);
+            wait_vm<G1N>();
+        } else {
+            wait_vm<0>();
+        }
+        for (int n = 0; n < NT; n += 2) {
+            sync_lds();  // A_n: chunk n is in b0, b1 is no longer read after phase 2
+            if (n + 1 < NT) G2(n + 1, b1);
+            sync_lds();  // B_n: group 1 of b0 is no longer read
+            if (n + 2 < NT) {
+                G1(n + 2, b0);
+                wait_vm<G1N>();
+            } else {
+                wait_vm<0>();
+            }
+            if (n + 1 >= NT) break;
+            sync_lds();  // A_{n+1}
+            if (n + 2 < NT) G2(n + 2, b0);
+            sync_lds();  // B_{n+1}
+            if (n + 3 < NT) {
+                G1(n + 3, b1);
+                wait_vm<G1N>();
+            } else {
+                wait_vm<0>();
+            }
+        }
+    } else {
+        G1(0, b0);
+        G2(0, b0);
+        wait_vm<0>();
+        for (int n = 0; n < NT; ++n) {
+            sync_lds();  // A_n
+            sync_lds();  // B_n
+            if (n + 1 < NT) G1(n + 1, b0);
+            sync_lds();  // C_n
+            if (n + 1 < NT) G2(n + 1, b0);
+            wait_vm<0>();
+        }
     }
 }
 
@@ -101,372 +189,439 @@ __device__ __forceinline__ void store_state(OT* dst, int j, const f32x4 (&pend)[
 template <class OT, int DK, int DV>
 struct FwdChainBuf {
     static constexpr int ES = sizeof(OT);
-    static constexpr int WM = 0;                  // Wm [64][DK] swizzled
-    static constexpr int KD = WM + CH * DK * ES;  // Kd [64][DK]
-    static constexpr int QG = KD + CH * DK * ES;  // Qg [64][DK]
-    static constexpr int M = QG + CH * DK * ES;   // M [64][64]
-    static constexpr int U = M + CH * CH * ES;    // 4 U tiles of this slice
-    static constexpr int GC = U + 4 * 256 * ES;   // DK floats
+    static constexpr int WM = 0;                  // group 1: Wm [64][DK] swizzled
+    static constexpr int QG = WM + CH * DK * ES;  // group 1: Qg [64][DK]
+    static constexpr int KD = QG + CH * DK * ES;  // group 2: Kd [64][DK]
+    static constexpr int M = KD + CH * DK * ES;   // group 2: M [64][64]
+    static constexpr int U = M + CH * CH * ES;    // group 2: the 4 U tiles of this slice
+    static constexpr int GC = U + 4 * 256 * ES;   // group 2: exp(gam_C), DK floats
     static constexpr int BYTES = GC + DK * 4;
 };
 
-template <class OT, int DK, int DV>
-__device__ __forceinline__ void fwd_prefetch(const Args& a, long long cid, int j, lds_char* buf) {
-    using B = FwdChainBuf<OT, DK, DV>;
-    const Layout& L = a.L;
-    dma16(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM, CH * DK * sizeof(OT));
-    dma16(a.ws + L.o_kd + cid * L.kd * sizeof(OT), buf + B::KD, CH * DK * sizeof(OT));
-    if (a.o) {
-        dma16(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG, CH * DK * sizeof(OT));
-        dma16(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M, CH * CH * sizeof(OT));
-    }
-    dma16(a.ws + L.o_u + (cid * L.u + (size_t)j * 4 * 256) * sizeof(OT), buf + B::U, 4 * 256 * sizeof(OT));
-    dma4(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC, DK * 4);
-}
-
-template <class OT, int DK, int DV, bool TRAIN>
-struct FwdPending {
-    f32x4 st[StateStore<OT, DK>::PER_LANE];
-    f32x4 D[4];
-    f32x4 O[4];
-    int c;  // chunk these belong to, -1 = nothing pending
+// outputs of one step held by one compute wave until the next step issues them
+template <class OT, int NW>
+struct FwdPend {
+    static constexpr int TPW = 4 / NW;  // token tiles per wave
+    f32x4 st[RowStore<OT>::PER_LANE];   // this wave's rows of the chunk start state
+    f32x4 D[TPW], O[TPW];               // Delta and O^T tiles wv * TPW + u
+    int c;                              // chunk, -1 = nothing pending
 };
 
-template <class OT, int DK, int DV, bool TRAIN>
-__device__ __forceinline__ void fwd_flush(const Args& a, int s, int j, FwdPending<OT, DK, DV, TRAIN>& pd) {
+template <class OT, int DK, int DV, bool TRAIN, bool OUT, int NW>
+__device__ __forceinline__ void fwd_flush(const Args& a, int s, int j, FwdPend<OT, NW>& pd) {
     if (pd.c < 0) return;
-    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    constexpr int TPW = FwdPend<OT, NW>::TPW;
+    const int l = lane_id(), li = l & 15, lq = l >> 4, wv = wave_id();
     const long long cid = (long long)s * a.NT + pd.c;
     const Layout& L = a.L;
     if (TRAIN) {
-        store_state<OT, DK, DV>((OT*)(a.ws + L.o_s) + cid * L.s, j, pd.st);
+        store_rows<OT, DV>((OT*)(a.ws + L.o_s) + cid * L.s, 32 * wv, j, pd.st);
         OT* dl = (OT*)(a.ws + L.o_delta) + cid * L.delta + j * 4 * 256;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) store_tile<OT>(dl + t * 256, pd.D[t]);
+        for (int u = 0; u < TPW; ++u) store_tile<OT>(dl + (wv * TPW + u) * 256, pd.D[u]);
     }
-    if (a.o) {
+    if (OUT) {
         const int bidx = s / a.H, h = s % a.H;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int row = pd.c * CH + 16 * t + li;
+        for (int u = 0; u < TPW; ++u) {
+            const int row = pd.c * CH + 16 * (wv * TPW + u) + li;
             if (row < a.T) {
-                float ov[4] = {pd.O[t][0], pd.O[t][1], pd.O[t][2], pd.O[t][3]};
+                float ov[4] = {pd.O[u][0], pd.O[u][1], pd.O[u][2], pd.O[u][3]};
                 st4((OT*)a.o + (((size_t)bidx * a.T + row) * a.H + h) * DV + 16 * j + 4 * lq, ov);
             }
         }
     }
 }
 
-template <class OT, int DK, int DV, bool TRAIN>
-__device__ __forceinline__ void fwd_step(const Args& a, int c, const lds_char* buf, f32x4 (&S)[DK / 16],
-                                         lds_char* stage, FwdPending<OT, DK, DV, TRAIN>& pd) {
+// One chunk step of a compute wave; contains barrier B of the step.
+template <class OT, int DK, int DV, bool TRAIN, bool OUT, int NW>
+__device__ __forceinline__ void fwd_step(int c, const lds_char* buf, f32x4& S0, f32x4& S1, lds_char* stage,
+                                         lds_char* xch, FwdPend<OT, NW>& pd) {
     using B = FwdChainBuf<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
-    constexpr int KB = DK / 32, AT = DK / 16;
-    const int l = lane_id(), lq = l >> 4;
+    constexpr int TPW = FwdPend<OT, NW>::TPW;
+    const int l = lane_id(), lq = l >> 4, wv = wave_id();
     const LSwz<OT, DK> vWM{buf + B::WM}, vKD{buf + B::KD}, vQG{buf + B::QG};
     const LSwz<OT, CH> vM{buf + B::M};
-    if (TRAIN) {  // chunk start state -> pending row-major store
-        stage_state<OT, DK>(stage, S);
-        unstage_state<OT, DK>(stage, pd.st);
-    }
-    FT SB[KB];
+    if (TRAIN) stage_rows<OT>(stage, S0, S1, pd.st);  // chunk start state -> pending row-major store
+    const FT SB = frag_of<OT>(S0, S1);                  // this wave's 32-row K block of the state
+    // phase 1 (group 1): split-K partials over this wave's key rows,
+    // Wm S into slots 8w + t, S^T Qg^T into slots 8w + 4 + t
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) SB[kb] = frag_of<OT>(S[2 * kb], S[2 * kb + 1]);
-    // Delta = U - Wm S
+    for (int t = 0; t < 4; ++t) {
+        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+        mma(p, lfrag_rowk<OT, OT>(vWM, 16 * t, 32 * wv), SB);
+        xput(xch, 8 * wv + t, p);
+        if (OUT) {
+            f32x4 po = {0.f, 0.f, 0.f, 0.f};
+            mma(po, SB, lfrag_rowk<OT, OT>(vQG, 16 * t, 32 * wv));
+            xput(xch, 8 * wv + 4 + t, po);
+        }
+    }
+    sync_lds();  // B
+    // phase 2 (group 2): Delta = U - Wm S, all four token tiles in every wave
     f32x4 D[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) mma(acc, lfrag_rowk<OT, OT>(vWM, 16 * t, 32 * kb), SB[kb]);
         float u[4];
         lds_get4<OT>(buf + B::U + (t * 256 + l * 4) * (int)sizeof(OT), u);
-        f32x4 uu = {u[0], u[1], u[2], u[3]};
-        D[t] = uu - acc;
+        f32x4 acc = {u[0], u[1], u[2], u[3]};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc -= xget(xch, 8 * w + t);
+        D[t] = acc;
     }
     FT DB[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) DB[kb] = frag_of<OT>(D[2 * kb], D[2 * kb + 1]);
-    // S' = diag(exp gam_C) S + Kd^T Delta
+    // O^T tiles of this wave: S^T Qg^T (summed partials) + Delta^T M^T
+    if (OUT) {
 #pragma unroll
-    for (int at = 0; at < AT; ++at) {
-        float g4[4];
-        lds_get4<float>(buf + B::GC + (16 * at + 4 * lq) * 4, g4);
-        f32x4 acc = {g4[0] * S[at][0], g4[1] * S[at][1], g4[2] * S[at][2], g4[3] * S[at][3]};
+        for (int u = 0; u < TPW; ++u) {
+            const int t = wv * TPW + u;
+            f32x4 acc = xget(xch, 4 + t);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vKD, 16 * at, 32 * kb), DB[kb]);
-        S[at] = acc;
-    }
-    // O^T = S^T Qg^T + Delta^T M^T (uses the chunk start state, still in SB)
-    if (a.o) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) mma(acc, SB[kb], lfrag_rowk<OT, OT>(vQG, 16 * t, 32 * kb));
+            for (int w = 1; w < NW; ++w) acc += xget(xch, 8 * w + 4 + t);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) mma(acc, DB[kb], lfrag_rowk<OT, OT>(vM, 16 * t, 32 * kb));
-            pd.O[t] = acc;
+            pd.O[u] = acc;
         }
     }
+    // S' = diag(exp gam_C) S + Kd^T Delta on this wave's rows
+    {
+        float g0[4], g1[4];
+        lds_get4<float>(buf + B::GC + (32 * wv + 4 * lq) * 4, g0);
+        lds_get4<float>(buf + B::GC + (32 * wv + 16 + 4 * lq) * 4, g1);
+        f32x4 a0 = {g0[0] * S0[0], g0[1] * S0[1], g0[2] * S0[2], g0[3] * S0[3]};
+        f32x4 a1 = {g1[0] * S1[0], g1[1] * S1[1], g1[2] * S1[2], g1[3] * S1[3]};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pd.D[t] = D[t];
+        for (int kb = 0; kb < 2; ++kb) {
+            mma(a0, lfrag_colk<OT, OT>(vKD, 32 * wv, 32 * kb), DB[kb]);
+            mma(a1, lfrag_colk<OT, OT>(vKD, 32 * wv + 16, 32 * kb), DB[kb]);
+        }
+        S0 = a0;
+        S1 = a1;
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) pd.D[u] = D[wv * TPW + u];
     pd.c = c;
 }
 
-constexpr int LDS_LIMIT = 160 * 1024;
-
-template <class OT, int DK, int DV, bool TRAIN>
-__global__ __launch_bounds__(64) void k_fwd_chain(Args a) {
+template <class OT, int DK, int DV, bool TRAIN, bool OUT, int NW, bool DBUF>
+__device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, lds_char* b0, lds_char* b1, lds_char* xch,
+                                         lds_char* stage_base) {
     using B = FwdChainBuf<OT, DK, DV>;
-    constexpr int AT = DK / 16, NJ = DV / 16;
-    constexpr bool DBUF = 2 * B::BYTES + StateStore<OT, DK>::BYTES <= LDS_LIMIT;
-    __shared__ __align__(16) char buf0[B::BYTES];
-    __shared__ __align__(16) char buf1[DBUF ? B::BYTES : 16];
-    __shared__ __align__(16) char stage_[StateStore<OT, DK>::BYTES];
-    lds_char* b0 = (lds_char*)buf0;
-    lds_char* b1 = (lds_char*)buf1;
-    lds_char* stage = (lds_char*)stage_;
-    const int l = threadIdx.x, li = l & 15, lq = l >> 4;
-    int s, j;
-    chain_map(blockIdx.x, a.B * a.H, NJ, s, j);
-
-    f32x4 S[AT];
+    const int wv = wave_id();
+    const int NT = a.NT;
+    const long long base = (long long)s * NT;
+    if (wv == NW) {  // producer
+        const Layout& L = a.L;
+        auto G1 = [&](int n, lds_char* buf) {
+            const long long cid = base + n;
+            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM);
+            if (OUT) dma16<CH * DK * sizeof(OT)>(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG);
+        };
+        auto G2 = [&](int n, lds_char* buf) {
+            const long long cid = base + n;
+            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_kd + cid * L.kd * sizeof(OT), buf + B::KD);
+            if (OUT) dma16<CH * CH * sizeof(OT)>(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M);
+            dma16<4 * 256 * sizeof(OT)>(a.ws + L.o_u + (cid * L.u + (size_t)j * 4 * 256) * sizeof(OT), buf + B::U);
+            dma4<DK * 4>(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC);
+        };
+        constexpr int G1N = (OUT ? 2 : 1) * CH * DK * (int)sizeof(OT) / 1024;
+        produce<DBUF, G1N>(NT, b0, b1, G1, G2);
+        return;
+    }
+    // compute waves: state rows 32 wv + 4 lq + i (S0) and 32 wv + 16 + 4 lq + i (S1),
+    // column 16 j + li
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    lds_char* stage = stage_base + wv * RowStore<OT>::BYTES;
+    const size_t r0 = ((size_t)s * DK + 32 * wv + 4 * lq) * DV + 16 * j + li;
+    f32x4 S0, S1;
 #pragma unroll
-    for (int at = 0; at < AT; ++at)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[at][i] = a.h0 ? a.h0[((size_t)s * DK + 16 * at + 4 * lq + i) * DV + 16 * j + li] : 0.f;
-    FwdPending<OT, DK, DV, TRAIN> pd;
+    for (int i = 0; i < 4; ++i) {
+        S0[i] = a.h0 ? a.h0[r0 + (size_t)i * DV] : 0.f;
+        S1[i] = a.h0 ? a.h0[r0 + (size_t)(16 + i) * DV] : 0.f;
+    }
+    FwdPend<OT, NW> pd;
     pd.c = -1;
-    const long long base = (long long)s * a.NT;
-    if (!DBUF) {  // one buffer: fetch, wait, compute
-        for (int c = 0; c < a.NT; ++c) {
-            fwd_flush<OT, DK, DV, TRAIN>(a, s, j, pd);
-            fwd_prefetch<OT, DK, DV>(a, base + c, j, b0);
-            wait_vm0();
-            fwd_step<OT, DK, DV, TRAIN>(a, c, b0, S, stage, pd);
+    if (DBUF) {
+        for (int n = 0; n < NT; n += 2) {
+            sync_lds();  // A_n
+            fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
+            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n, b0, S0, S1, stage, xch, pd);
+            if (n + 1 >= NT) break;
+            sync_lds();  // A_{n+1}
+            fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
+            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n + 1, b1, S0, S1, stage, xch, pd);
         }
     } else {
-    fwd_prefetch<OT, DK, DV>(a, base, j, b0);
-    for (int c = 0; c < a.NT; c += 2) {
-        wait_vm0();
-        if (c + 1 < a.NT) fwd_prefetch<OT, DK, DV>(a, base + c + 1, j, b1);
-        fwd_flush<OT, DK, DV, TRAIN>(a, s, j, pd);
-        fwd_step<OT, DK, DV, TRAIN>(a, c, b0, S, stage, pd);
-        if (c + 1 >= a.NT) break;
-        wait_vm0();
-        if (c + 2 < a.NT) fwd_prefetch<OT, DK, DV>(a, base + c + 2, j, b0);
-        fwd_flush<OT, DK, DV, TRAIN>(a, s, j, pd);
-        fwd_step<OT, DK, DV, TRAIN>(a, c + 1, b1, S, stage, pd);
+        for (int n = 0; n < NT; ++n) {
+            sync_lds();  // A_n
+            fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
+            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n, b0, S0, S1, stage, xch, pd);
+            sync_lds();  // C_n
+        }
     }
-    }
-    fwd_flush<OT, DK, DV, TRAIN>(a, s, j, pd);
+    fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
     if (a.ht) {
 #pragma unroll
-        for (int at = 0; at < AT; ++at)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a.ht[((size_t)s * DK + 16 * at + 4 * lq + i) * DV + 16 * j + li] = S[at][i];
+        for (int i = 0; i < 4; ++i) {
+            a.ht[r0 + (size_t)i * DV] = S0[i];
+            a.ht[r0 + (size_t)(16 + i) * DV] = S1[i];
+        }
     }
+}
+
+template <class OT, int DK, int DV, bool TRAIN>
+__global__ __launch_bounds__(64 * (DK / 32 + 1)) void k_fwd_chain(Args a) {
+    using B = FwdChainBuf<OT, DK, DV>;
+    constexpr int NW = DK / 32, NJ = DV / 16;
+    constexpr int XBYTES = NW * 8 * 1024;
+    constexpr int SBYTES = NW * RowStore<OT>::BYTES;
+    constexpr bool DBUF = 2 * B::BYTES + XBYTES + SBYTES <= LDS_LIMIT;
+    __shared__ __align__(16) char buf0[B::BYTES];
+    __shared__ __align__(16) char buf1[DBUF ? B::BYTES : 16];
+    __shared__ __align__(16) char xch[XBYTES];
+    __shared__ __align__(16) char stage[SBYTES];
+    int s, j;
+    chain_map(blockIdx.x, a.B * a.H, NJ, s, j);
+    if (a.o)
+        fwd_walk<OT, DK, DV, TRAIN, true, NW, DBUF>(a, s, j, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch,
+                                                    (lds_char*)stage);
+    else
+        fwd_walk<OT, DK, DV, TRAIN, false, NW, DBUF>(a, s, j, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch,
+                                                     (lds_char*)stage);
 }
 
 // ============================================================================ backward chain
 template <class OT, int DK, int DV>
 struct BwdChainBuf {
     static constexpr int ES = sizeof(OT);
-    static constexpr int M = 0;                   // M [64][64] swizzled
-    static constexpr int KD = M + CH * CH * ES;   // Kd [64][DK]
-    static constexpr int QG = KD + CH * DK * ES;  // Qg [64][DK]
-    static constexpr int WM = QG + CH * DK * ES;  // Wm [64][DK]
-    static constexpr int T = WM + CH * DK * ES;   // T [64][64]
-    static constexpr int GC = T + CH * CH * ES;   // DK floats
-    static constexpr int DO = GC + DK * 4;        // dO rows [64][16]
-    static constexpr int BYTES = DO + 64 * 16 * ES;
+    static constexpr int KD = 0;                  // group 1: Kd [64][DK] swizzled
+    static constexpr int M = KD + CH * DK * ES;   // group 1: M [64][64]
+    static constexpr int DO = M + CH * CH * ES;   // group 1: dO rows of this slice [64][16]
+    static constexpr int WM = DO + 64 * 16 * ES;  // group 2: Wm [64][DK]
+    static constexpr int QG = WM + CH * DK * ES;  // group 2: Qg [64][DK]
+    static constexpr int T = QG + CH * DK * ES;   // group 2: T [64][64]
+    static constexpr int GC = T + CH * CH * ES;   // group 2: exp(gam_C), DK floats
+    static constexpr int BYTES = GC + DK * 4;
 };
 
-template <class OT, int DK, int DV>
-__device__ __forceinline__ void bwd_prefetch(const Args& a, long long cid, int c, int s, int j, lds_char* buf) {
-    using B = BwdChainBuf<OT, DK, DV>;
-    const Layout& L = a.L;
-    dma16(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M, CH * CH * sizeof(OT));
-    dma16(a.ws + L.o_kd + cid * L.kd * sizeof(OT), buf + B::KD, CH * DK * sizeof(OT));
-    dma16(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG, CH * DK * sizeof(OT));
-    dma16(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM, CH * DK * sizeof(OT));
-    dma16(a.ws + L.o_t + cid * L.t * sizeof(OT), buf + B::T, CH * CH * sizeof(OT));
-    dma4(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC, DK * 4);
-    // dO rows of this slice: row r, 16 columns; 4 bytes per lane, 256 bytes per instruction
-    const int l = lane_id();
-    const int bidx = s / a.H, h = s % a.H;
-    constexpr int EPL = 4 / sizeof(OT);          // elements per lane-load
-    constexpr int RPI = 256 / (16 * sizeof(OT));  // rows per instruction
-#pragma unroll
-    for (int k = 0; k < 64 / RPI; ++k) {
-        const int r = k * RPI + l / (16 / EPL);
-        const int col = (l % (16 / EPL)) * EPL;
-        const int row = c * CH + r;
-        lds_char* dst = buf + B::DO + k * 256;
-        if (row < a.T) {
-            const OT* src = (const OT*)a.dout + (((size_t)bidx * a.T + row) * a.H + h) * DV + 16 * j + col;
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
-        } else {
-            typedef __attribute__((address_space(3))) uint32_t U32;
-            *(U32*)(dst + l * 4) = 0u;
-        }
-    }
-}
-
-template <class OT, int DK>
-struct BwdPending {
-    f32x4 st[StateStore<OT, DK>::PER_LANE];
-    f32x4 Y[4];
+template <class OT, int NW>
+struct BwdPend {
+    static constexpr int TPW = 4 / NW;
+    f32x4 st[RowStore<OT>::PER_LANE];  // this wave's rows of the end-state gradient
+    f32x4 Y[TPW];                      // dY tiles wv * TPW + u
     int c;
 };
 
-template <class OT, int DK, int DV>
-__device__ __forceinline__ void bwd_flush(const Args& a, int s, int j, BwdPending<OT, DK>& pd) {
+template <class OT, int DK, int DV, int NW>
+__device__ __forceinline__ void bwd_flush(const Args& a, int s, int j, BwdPend<OT, NW>& pd) {
     if (pd.c < 0) return;
+    constexpr int TPW = BwdPend<OT, NW>::TPW;
+    const int wv = wave_id();
     const long long cid = (long long)s * a.NT + pd.c;
     const Layout& L = a.L;
-    store_state<OT, DK, DV>((OT*)(a.ws + L.o_ds) + cid * L.ds, j, pd.st);
+    store_rows<OT, DV>((OT*)(a.ws + L.o_ds) + cid * L.ds, 32 * wv, j, pd.st);
     OT* dy = (OT*)(a.ws + L.o_dy) + cid * L.dy + j * 4 * 256;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) store_tile<OT>(dy + t * 256, pd.Y[t]);
+    for (int u = 0; u < TPW; ++u) store_tile<OT>(dy + (wv * TPW + u) * 256, pd.Y[u]);
 }
 
-template <class OT, int DK, int DV>
-__device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4 (&dS)[DK / 16], lds_char* stage,
-                                         BwdPending<OT, DK>& pd) {
+// One chunk step of a compute wave; contains barrier B of the step.
+template <class OT, int DK, int DV, int NW>
+__device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0, f32x4& dS1, lds_char* stage,
+                                         lds_char* xch, BwdPend<OT, NW>& pd) {
     using B = BwdChainBuf<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
-    constexpr int KB = DK / 32, AT = DK / 16;
-    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    constexpr int TPW = BwdPend<OT, NW>::TPW;
+    const int l = lane_id(), lq = l >> 4, wv = wave_id();
     const LSwz<OT, DK> vKD{buf + B::KD}, vQG{buf + B::QG}, vWM{buf + B::WM};
     const LSwz<OT, CH> vM{buf + B::M}, vT{buf + B::T};
-    // gradient w.r.t. this chunk's end state -> pending row-major store
-    stage_state<OT, DK>(stage, dS);
-    unstage_state<OT, DK>(stage, pd.st);
-    // B fragments of dO: K = token, N = this slice's 16 value channels
+    const LPad<OT> vDO{buf + B::DO, 16};
+    stage_rows<OT>(stage, dS0, dS1, pd.st);  // gradient w.r.t. this chunk's end state
+    // phase 1 (group 1). B fragments of dO: K = token, N = this slice's 16 value channels
     FT dOB[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) dOB[kb] = lfrag_colk<OT, OT>(vDO, 0, 32 * kb);
+    const FT dSB = frag_of<OT>(dS0, dS1);
+    // M^T dO on this wave's token tiles
+    f32x4 pm[TPW];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dOB[kb][e] = lds_load<OT>(buf + B::DO + ((32 * kb + kmap(lq, e)) * 16 + li) * (int)sizeof(OT));
-    FT dSB[KB];
+    for (int u = 0; u < TPW; ++u) {
+        pm[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) dSB[kb] = frag_of<OT>(dS[2 * kb], dS[2 * kb + 1]);
-    // dDelta = M^T dO + Kd dS'
+        for (int kb = 0; kb < 2; ++kb) mma(pm[u], lfrag_colk<OT, OT>(vM, 16 * (wv * TPW + u), 32 * kb), dOB[kb]);
+    }
+    // split-K partials of Kd dS' over this wave's key rows (slot 4w + t), plus M^T dO
+    // on the tiles this wave owns
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+        mma(p, lfrag_rowk<OT, OT>(vKD, 16 * t, 32 * wv), dSB);
+        const bool own = t / TPW == wv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] += own ? pm[t % TPW][i] : 0.f;
+        xput(xch, 4 * wv + t, p);
+    }
+    sync_lds();  // B
+    // phase 2 (group 2)
     f32x4 dD[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = xget(xch, t);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) mma(acc, lfrag_rowk<OT, OT>(vKD, 16 * t, 32 * kb), dSB[kb]);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vM, 16 * t, 32 * kb), dOB[kb]);
+        for (int w = 1; w < NW; ++w) acc += xget(xch, 4 * w + t);
         dD[t] = acc;
     }
     FT dDB[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) dDB[kb] = frag_of<OT>(dD[2 * kb], dD[2 * kb + 1]);
-    // dS = diag(exp gam_C) dS' + Qg^T dO - Wm^T dDelta
-#pragma unroll
-    for (int at = 0; at < AT; ++at) {
-        float g4[4];
-        lds_get4<float>(buf + B::GC + (16 * at + 4 * lq) * 4, g4);
-        f32x4 pos = {g4[0] * dS[at][0], g4[1] * dS[at][1], g4[2] * dS[at][2], g4[3] * dS[at][3]};
-        f32x4 neg = {0.f, 0.f, 0.f, 0.f};
+    // dS = diag(exp gam_C) dS' + Qg^T dO - Wm^T dDelta on this wave's rows
+    {
+        float g0[4], g1[4];
+        lds_get4<float>(buf + B::GC + (32 * wv + 4 * lq) * 4, g0);
+        lds_get4<float>(buf + B::GC + (32 * wv + 16 + 4 * lq) * 4, g1);
+        f32x4 p0 = {g0[0] * dS0[0], g0[1] * dS0[1], g0[2] * dS0[2], g0[3] * dS0[3]};
+        f32x4 p1 = {g1[0] * dS1[0], g1[1] * dS1[1], g1[2] * dS1[2], g1[3] * dS1[3]};
+        f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = n0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            mma(neg, lfrag_colk<OT, OT>(vWM, 16 * at, 32 * kb), dDB[kb]);
-            mma(pos, lfrag_colk<OT, OT>(vQG, 16 * at, 32 * kb), dOB[kb]);
+            mma(n0, lfrag_colk<OT, OT>(vWM, 32 * wv, 32 * kb), dDB[kb]);
+            mma(n1, lfrag_colk<OT, OT>(vWM, 32 * wv + 16, 32 * kb), dDB[kb]);
+            mma(p0, lfrag_colk<OT, OT>(vQG, 32 * wv, 32 * kb), dOB[kb]);
+            mma(p1, lfrag_colk<OT, OT>(vQG, 32 * wv + 16, 32 * kb), dOB[kb]);
         }
-        dS[at] = pos - neg;
+        dS0 = p0 - n0;
+        dS1 = p1 - n1;
     }
-    // dY = T^T dDelta (for the intra-chunk kernel)
+    // dY = T^T dDelta on this wave's token tiles (for the intra-chunk kernel)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int u = 0; u < TPW; ++u) {
+        const int t = wv * TPW + u;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vT, 16 * t, 32 * kb), dDB[kb]);
-        pd.Y[t] = acc;
+        pd.Y[u] = acc;
     }
     pd.c = c;
 }
 
-template <class OT, int DK, int DV>
-__global__ __launch_bounds__(64) void k_bwd_chain(Args a) {
+template <class OT, int DK, int DV, int NW, bool DBUF>
+__device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* b0, lds_char* b1, lds_char* xch,
+                                         lds_char* stage_base) {
     using B = BwdChainBuf<OT, DK, DV>;
-    constexpr int AT = DK / 16, NJ = DV / 16;
-    constexpr bool DBUF = 2 * B::BYTES + StateStore<OT, DK>::BYTES <= LDS_LIMIT;
-    __shared__ __align__(16) char buf0[B::BYTES];
-    __shared__ __align__(16) char buf1[DBUF ? B::BYTES : 16];
-    __shared__ __align__(16) char stage_[StateStore<OT, DK>::BYTES];
-    lds_char* b0 = (lds_char*)buf0;
-    lds_char* b1 = (lds_char*)buf1;
-    lds_char* stage = (lds_char*)stage_;
-    const int l = threadIdx.x, li = l & 15, lq = l >> 4;
-    int s, j;
-    chain_map(blockIdx.x, a.B * a.H, NJ, s, j);
-
-    f32x4 dS[AT];
+    const int wv = wave_id();
+    const int NT = a.NT, last = NT - 1;
+    const long long base = (long long)s * NT;
+    if (wv == NW) {  // producer; walk index n is chunk last - n
+        const Layout& L = a.L;
+        const int l = lane_id();
+        const int bidx = s / a.H, h = s % a.H;
+        constexpr int EPL = 4 / sizeof(OT);           // dO elements per lane and instruction
+        constexpr int RPI = 256 / (16 * sizeof(OT));  // dO rows per instruction
+        auto G1 = [&](int n, lds_char* buf) {
+            const int c = last - n;
+            const long long cid = base + c;
+            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_kd + cid * L.kd * sizeof(OT), buf + B::KD);
+            dma16<CH * CH * sizeof(OT)>(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M);
+            // dO rows of this slice. Rows past the end of the sequence repeat its last row:
+            // every product that reads dO (M^T dO, Qg^T dO) multiplies those rows by rows of
+            // M and Qg that the intra-chunk kernel wrote as exact zeros.
 #pragma unroll
-    for (int at = 0; at < AT; ++at)
+            for (int k = 0; k < 64 / RPI; ++k) {
+                const int r = k * RPI + l / (16 / EPL);
+                const int col = (l % (16 / EPL)) * EPL;
+                const int row = min(c * CH + r, a.T - 1);
+                const OT* src = (const OT*)a.dout + (((size_t)bidx * a.T + row) * a.H + h) * DV + 16 * j + col;
+                __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + B::DO + k * 256), 4, 0, 0);
+            }
+        };
+        auto G2 = [&](int n, lds_char* buf) {
+            const long long cid = base + (last - n);
+            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM);
+            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG);
+            dma16<CH * CH * sizeof(OT)>(a.ws + L.o_t + cid * L.t * sizeof(OT), buf + B::T);
+            dma4<DK * 4>(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC);
+        };
+        constexpr int G1N = (CH * DK + CH * CH) * (int)sizeof(OT) / 1024 + 64 / RPI;
+        produce<DBUF, G1N>(NT, b0, b1, G1, G2);
+        return;
+    }
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    lds_char* stage = stage_base + wv * RowStore<OT>::BYTES;
+    const size_t r0 = ((size_t)s * DK + 32 * wv + 4 * lq) * DV + 16 * j + li;
+    f32x4 dS0, dS1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            dS[at][i] = a.dht ? a.dht[((size_t)s * DK + 16 * at + 4 * lq + i) * DV + 16 * j + li] : 0.f;
-    BwdPending<OT, DK> pd;
+    for (int i = 0; i < 4; ++i) {
+        dS0[i] = a.dht ? a.dht[r0 + (size_t)i * DV] : 0.f;
+        dS1[i] = a.dht ? a.dht[r0 + (size_t)(16 + i) * DV] : 0.f;
+    }
+    BwdPend<OT, NW> pd;
     pd.c = -1;
-    const long long base = (long long)s * a.NT;
-    const int last = a.NT - 1;
-    if (!DBUF) {  // one buffer: fetch, wait, compute
-        for (int c = last; c >= 0; --c) {
-            bwd_flush<OT, DK, DV>(a, s, j, pd);
-            bwd_prefetch<OT, DK, DV>(a, base + c, c, s, j, b0);
-            wait_vm0();
-            bwd_step<OT, DK, DV>(c, b0, dS, stage, pd);
+    if (DBUF) {
+        for (int n = 0; n < NT; n += 2) {
+            sync_lds();  // A_n
+            bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
+            bwd_step<OT, DK, DV, NW>(last - n, b0, dS0, dS1, stage, xch, pd);
+            if (n + 1 >= NT) break;
+            sync_lds();  // A_{n+1}
+            bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
+            bwd_step<OT, DK, DV, NW>(last - n - 1, b1, dS0, dS1, stage, xch, pd);
         }
     } else {
-    bwd_prefetch<OT, DK, DV>(a, base + last, last, s, j, b0);
-    for (int c = last; c >= 0; c -= 2) {
-        wait_vm0();
-        if (c - 1 >= 0) bwd_prefetch<OT, DK, DV>(a, base + c - 1, c - 1, s, j, b1);
-        bwd_flush<OT, DK, DV>(a, s, j, pd);
-        bwd_step<OT, DK, DV>(c, b0, dS, stage, pd);
-        if (c - 1 < 0) break;
-        wait_vm0();
-        if (c - 2 >= 0) bwd_prefetch<OT, DK, DV>(a, base + c - 2, c - 2, s, j, b0);
-        bwd_flush<OT, DK, DV>(a, s, j, pd);
-        bwd_step<OT, DK, DV>(c - 1, b1, dS, stage, pd);
+        for (int n = 0; n < NT; ++n) {
+            sync_lds();  // A_n
+            bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
+            bwd_step<OT, DK, DV, NW>(last - n, b0, dS0, dS1, stage, xch, pd);
+            sync_lds();  // C_n
+        }
     }
-    }
-    bwd_flush<OT, DK, DV>(a, s, j, pd);
+    bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
     if (a.dh0) {
 #pragma unroll
-        for (int at = 0; at < AT; ++at)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a.dh0[((size_t)s * DK + 16 * at + 4 * lq + i) * DV + 16 * j + li] = dS[at][i];
+        for (int i = 0; i < 4; ++i) {
+            a.dh0[r0 + (size_t)i * DV] = dS0[i];
+            a.dh0[r0 + (size_t)(16 + i) * DV] = dS1[i];
+        }
     }
+}
+
+template <class OT, int DK, int DV>
+__global__ __launch_bounds__(64 * (DK / 32 + 1)) void k_bwd_chain(Args a) {
+    using B = BwdChainBuf<OT, DK, DV>;
+    constexpr int NW = DK / 32, NJ = DV / 16;
+    constexpr int XBYTES = NW * 4 * 1024;
+    constexpr int SBYTES = NW * RowStore<OT>::BYTES;
+    constexpr bool DBUF = 2 * B::BYTES + XBYTES + SBYTES <= LDS_LIMIT;
+    __shared__ __align__(16) char buf0[B::BYTES];
+    __shared__ __align__(16) char buf1[DBUF ? B::BYTES : 16];
+    __shared__ __align__(16) char xch[XBYTES];
+    __shared__ __align__(16) char stage[SBYTES];
+    int s, j;
+    chain_map(blockIdx.x, a.B * a.H, NJ, s, j);
+    bwd_walk<OT, DK, DV, NW, DBUF>(a, s, j, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch, (lds_char*)stage);
 }
 
 // ============================================================================ launchers
 template <class OT, int DK, int DV>
 hipError_t launch_fwd_chain_t(const Args& a, bool train, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.B * a.H * (DV / 16)));
+    const dim3 grid((unsigned)(a.B * a.H * (DV / 16))), block(64 * (DK / 32 + 1));
     if (train)
-        hipLaunchKernelGGL((k_fwd_chain<OT, DK, DV, true>), grid, dim3(64), 0, stream, a);
+        hipLaunchKernelGGL((k_fwd_chain<OT, DK, DV, true>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((k_fwd_chain<OT, DK, DV, false>), grid, dim3(64), 0, stream, a);
+        hipLaunchKernelGGL((k_fwd_chain<OT, DK, DV, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 template <class OT, int DK, int DV>
 hipError_t launch_bwd_chain_t(const Args& a, hipStream_t stream) {
-    hipLaunchKernelGGL((k_bwd_chain<OT, DK, DV>), dim3((unsigned)(a.B * a.H * (DV / 16))), dim3(64), 0, stream, a);
+    const dim3 grid((unsigned)(a.B * a.H * (DV / 16))), block(64 * (DK / 32 + 1));
+    hipLaunchKernelGGL((k_bwd_chain<OT, DK, DV>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
-#define GDR2_CHAIN_INST(OT_, DK_, DV_)                                                           \
-    template hipError_t launch_fwd_chain_t<OT_, DK_, DV_>(const Args&, bool, hipStream_t);      \
+#define GDR2_CHAIN_INST(OT_, DK_, DV_)                                                      \
+    template hipError_t launch_fwd_chain_t<OT_, DK_, DV_>(const Args&, bool, hipStream_t); \
     template hipError_t launch_bwd_chain_t<OT_, DK_, DV_>(const Args&, hipStream_t);
 GDR2_CHAIN_INST(bf16, 64, 64)
 GDR2_CHAIN_INST(bf16, 64, 128)
