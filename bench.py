@@ -12,19 +12,39 @@ roofline         : the kernel with the largest average duration, its algorithmic
                    bytes per launch (the operator inputs and outputs it must move; no
                    intermediates) over its average duration, timed with HIP events that
                    the library records on the launch stream around each kernel.
-step_roofline    : algorithmic bytes of the whole step over 8 TB/s, divided by the
-                   measured step time (the fraction of the HBM roofline for fwd+bwd).
+                   "traffic" is that kernel's measured HBM bytes per launch (rocprofv3
+                   FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), read
+                   from the summary under profiles/ when it was taken on the current
+                   kernel sources (same digest), else null.
+step_roofline    : algorithmic bytes of the whole step (each operator input and output
+                   counted once) over 8 TB/s, divided by the measured step time.
 cpu_baseline     : the fp64 oracle (test infrastructure, untuned) timed on the host
-                   cores over a bounded sample of the same workload's sequences.
+                   cores over a bounded sample of the same workload's sequences:
+                   passes over the first B*H sequences at full length until about
+                   10 s have elapsed.
+
+    python bench.py --summarize-profile DIR
+
+reads the rocprofv3 output of a profiling run (DIR/trace, DIR/pmc_FETCH_SIZE,
+DIR/pmc_WRITE_SIZE, made with --copy-calibration) and writes the per-kernel
+summary under profiles/.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
+import hashlib
 import json
 import os
 import sys
 import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(HERE, "profiles")
+CSRC = os.path.join(HERE, "gated_delta_rule_gdr2_amd", "csrc")
+KERNELS = ("fwd_intra", "fwd_chain", "bwd_chain", "bwd_intra")
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, published
@@ -40,6 +60,45 @@ def algorithmic_bytes(wl, esz):
     bwd_chain = th * wl.DV * esz + (state if wl.h0_std > 0 else 0)      # reads dout (+ writes dh0)
     bwd_intra = th * ((4 * wl.DK + 2 * wl.DV) + wl.DV + (4 * wl.DK + 2 * wl.DV)) * esz  # in + dout + grads
     return {"fwd_intra": fwd_intra, "fwd_chain": fwd_chain, "bwd_chain": bwd_chain, "bwd_intra": bwd_intra}
+
+
+def step_algorithmic_bytes(wl, esz):
+    """Operator-level bytes of one fwd+bwd step, each input and output counted once."""
+    th = wl.B * wl.T * wl.H
+    state = wl.B * wl.H * wl.DK * wl.DV * 4
+    fwd = th * (4 * wl.DK + 2 * wl.DV + wl.DV) * esz + state              # in, o, ht
+    bwd = th * (4 * wl.DK + 2 * wl.DV + wl.DV + 4 * wl.DK + 2 * wl.DV) * esz  # in, dout, grads
+    if wl.h0_std > 0:
+        fwd += state      # h0
+        bwd += state      # dh0
+    return fwd + bwd
+
+
+def source_digest():
+    """sha256 over the kernel sources; a profile summary is valid only for this digest."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_summary_path(workload):
+    return os.path.join(PROFILES, "hbm_traffic_%s.json" % workload)
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None."""
+    p = traffic_summary_path(workload)
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        d = json.load(fh)
+    if d.get("source_digest") != source_digest():
+        return None
+    k = d["kernels"].get(kernel)
+    return None if k is None else k["fetch_bytes"] + k["write_bytes"]
 
 
 def algorithmic_flops(wl, C=64):
@@ -82,13 +141,14 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def cpu_baseline(wl, inputs, budget_seqs=None):
-    """Time the fp64 oracle (fwd + bwd) on the first n (batch, head) sequences at full length."""
+def cpu_baseline(wl, inputs, min_seconds=10.0):
+    """Time the fp64 oracle (fwd + bwd) in passes over the first n (batch, head) sequences at
+    full length (n = the oracle's thread count, at most B*H) until min_seconds have elapsed."""
     import numpy as np
     import oracle
     cores = oracle.num_threads()
     NS = wl.B * wl.H
-    n = min(NS, budget_seqs or cores)
+    n = min(NS, cores)
     sel = [(s // wl.H, s % wl.H) for s in range(n)]
 
     def take(x, state=False):
@@ -102,15 +162,84 @@ def cpu_baseline(wl, inputs, budget_seqs=None):
     args = [take(inputs[k]) for k in ("q", "k", "v", "g", "b", "w")]
     h0 = take(inputs["h0"], True)
     do = take(inputs["do"])
+    passes = 0
     t0 = time.perf_counter()
-    oracle.fwd(*args, h0)
-    if wl.backward:
-        oracle.bwd(*args, h0, do)
-    dt = time.perf_counter() - t0
-    tokens = n * wl.T / wl.H
+    while True:
+        oracle.fwd(*args, h0)
+        if wl.backward:
+            oracle.bwd(*args, h0, do)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    tokens = passes * n * wl.T / wl.H
     return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "%d of %d (batch, head) sequences at full length T=%d, fwd+bwd, fp64, %.1f s"
-                      % (n, NS, wl.T, dt)}
+            "sample": "%d pass(es) over %d of %d (batch, head) sequences at full length T=%d, fwd+bwd, "
+                      "fp64, %.1f s; tokens counted as sequences*T/H" % (passes, n, NS, wl.T, dt)}
+
+
+def _short(name):
+    for k in KERNELS + ("copyBuffer",):
+        if k in name:
+            return k
+    return None
+
+
+def summarize_profile(d, workload, copy_mib, command):
+    """Write profiles/ summaries from a rocprofv3 run: kernel trace stats and HBM traffic."""
+    stats = {}
+    for r in csv.DictReader(open(os.path.join(d, "trace", "run_kernel_stats.csv"))):
+        k = _short(r["Name"])
+        if k:
+            stats[k] = {"name": r["Name"], "calls": int(r["Calls"]), "avg_ms": float(r["AverageNs"]) / 1e6,
+                        "min_ms": float(r["MinNs"]) / 1e6, "max_ms": float(r["MaxNs"]) / 1e6}
+    ctr = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        vals = {}
+        for r in csv.DictReader(open(os.path.join(d, "pmc_" + c, "run_counter_collection.csv"))):
+            k = _short(r["Kernel_Name"])
+            if k and r["Counter_Name"] == c:
+                vals.setdefault(k, []).append(float(r["Counter_Value"]))
+        ctr[c] = {k: sum(v) / len(v) for k, v in vals.items()}
+    copy_kib = copy_mib * 1024.0
+    cal_f = copy_kib / ctr["FETCH_SIZE"]["copyBuffer"]
+    cal_w = copy_kib / ctr["WRITE_SIZE"]["copyBuffer"]
+    kern = {}
+    for k in KERNELS:
+        fb = ctr["FETCH_SIZE"][k] * cal_f * 1024
+        wb = ctr["WRITE_SIZE"][k] * cal_w * 1024
+        kern[k] = {"fetch_bytes": fb, "write_bytes": wb, "avg_ms": stats[k]["avg_ms"],
+                   "gbs": (fb + wb) / (stats[k]["avg_ms"] * 1e-3) / 1e9}
+    summary = {"workload": workload, "source_digest": source_digest(), "command": command,
+               "calibration": {"copy_bytes": copy_mib << 20, "fetch_factor": cal_f, "write_factor": cal_w,
+                               "note": "FETCH_SIZE/WRITE_SIZE are KiB per dispatch; each is scaled by "
+                                       "the factor that makes a plain device copy of copy_bytes read and "
+                                       "write exactly copy_bytes"},
+               "kernels": kern}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_summary_path(workload), "w") as fh:
+        json.dump(summary, fh, indent=1)
+    tot = sum(v["avg_ms"] for k, v in stats.items() if k in KERNELS)
+    lines = ["# Kernel trace and HBM traffic: fwd+bwd step, workload %s" % workload, "",
+             "Command (repository root, one MI355X):", "", "    " + command.replace("\n", "\n    "), "",
+             "Kernel trace (rocprofv3 --kernel-trace --stats), per dispatch:", "",
+             "| kernel | calls | average (ms) | min (ms) | max (ms) | share |", "|---|---|---|---|---|---|"]
+    for k in KERNELS:
+        v = stats[k]
+        lines.append("| `%s` | %d | %.4f | %.4f | %.4f | %.1f%% |" % (v["name"], v["calls"], v["avg_ms"],
+                                                                   v["min_ms"], v["max_ms"],
+                                                                   100 * v["avg_ms"] / tot))
+    lines += ["", "Sum of the four kernel averages: %.4f ms per step." % tot, "",
+              "HBM traffic per dispatch (FETCH_SIZE x %.3f, WRITE_SIZE x %.3f; factors from a %d MiB "
+              "device copy in the same runs):" % (cal_f, cal_w, copy_mib), "",
+              "| kernel | fetched (MB) | written (MB) | GB/s at the trace average |", "|---|---|---|---|"]
+    for k in KERNELS:
+        v = kern[k]
+        lines.append("| %s | %.1f | %.1f | %.0f |" % (k, v["fetch_bytes"] / 1e6, v["write_bytes"] / 1e6, v["gbs"]))
+    lines += ["", "Kernel source digest (sha256 over gated_delta_rule_gdr2_amd/csrc): `%s`" % summary["source_digest"]]
+    with open(os.path.join(PROFILES, "kernels_%s.md" % workload), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("wrote", traffic_summary_path(workload), "and the kernel table")
 
 
 def main():
@@ -123,7 +252,15 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="also run one plain device-to-device copy of MB MiB (outside the timed region), "
                          "the reference that HBM byte counters are scaled by")
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+                    help="summarise a rocprofv3 run (no GPU needed) into profiles/")
+    ap.add_argument("--profile-command", default="", help="the command line recorded with --summarize-profile")
     args = ap.parse_args()
+    if args.summarize_profile:
+        from gated_delta_rule_gdr2_amd.inputs import HEADLINE
+        summarize_profile(args.summarize_profile, args.workload or HEADLINE, args.copy_calibration or 256,
+                          args.profile_command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this operator build has no multi-GPU path "
@@ -187,7 +324,7 @@ def main():
     dom = max(avg_ms, key=avg_ms.get)
     achieved = abytes[dom] / (avg_ms[dom] * 1e-3) / 1e9
     ms_step = elapsed / K * 1e3
-    step_bytes = sum(abytes.values())
+    step_bytes = step_algorithmic_bytes(wl, esz)
     t_roof_ms = max(step_bytes / (HBM_PEAK_GBS * 1e9), algorithmic_flops(wl) / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
 
     out = {
@@ -206,7 +343,7 @@ def main():
         "config": {"workload": wl.name, "B": B, "H": H, "T": T, "d_k": DK, "d_v": DV, "chunk": wl.chunk,
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name, dom), "kernel": dom,
                      "algorithmic_bytes_per_launch": abytes[dom], "avg_launch_ms": avg_ms[dom]},
         "step_roofline": {"bound": "hbm", "algorithmic_bytes": step_bytes, "t_roofline_ms": t_roof_ms,
                           "frac": t_roof_ms / ms_step},

@@ -18,9 +18,10 @@
 // sum_r dKd*Kd + exp(gam_C) * rowsum(dS' * S); dg is its reverse running sum.
 //
 // Kernels:
-//   k_bwd_chain : (gdr2_chain.hip) one wave per (sequence, 16-column value
-//                 slice), chunks in reverse; state gradient in accumulator
-//                 registers; writes dS' (row-major) and dY (tiles) per chunk.
+//   k_bwd_chain : (gdr2_chain.hip) one workgroup per (sequence, 16-column value
+//                 slice), chunks in reverse; the state gradient's key rows split
+//                 over the compute waves, held in accumulator registers; writes
+//                 dS' (row-major) and dY (tiles) per chunk.
 //   k_bwd_intra : one workgroup per chunk, fully parallel; reads the saved S,
 //                 Delta, dS', dY and the inputs, writes dq, dk, dv, dg, db, dw.
 #include "gdr2_intra_common.hpp"
