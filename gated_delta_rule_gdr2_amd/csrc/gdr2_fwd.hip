@@ -127,24 +127,54 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
     OT* u_out = (OT*)(a.ws + L.o_u) + cid * L.u;
     float* gc_out = (float*)(a.ws + L.o_gc) + cid * L.gc;
 
-    // ---- phase 1: cumulative decay, factors, Qg / Kd / exp(gam_C) out, X = w*v
-    for (int at = wv; at < DK / 16; at += 4) {
-        const int ch0 = 16 * at + 4 * lq;
-        float gam[4][4], g0[4][4], ge[4][4];
-        chunk_gamma((const OT*)a.g + rowk0 * DK, rsk, ch0, nvalid, gam, g0, ge);
-        write_factors<DK>(sF, ch0, g0, ge);
-        if (li == 0) {
-            float gcv[4];
+    // ---- phase 1: cumulative decay, factors, Qg / Kd / exp(gam_C) out, X = w*v.
+    // Wave wv owns key-channel tiles wv + 4 ai and value-channel tiles wv + 4 ji; all of
+    // its input loads are issued before any is used.
+    {
+        constexpr int NA = DK / 64, NJ = DV / 64;
+        using RT = typename Raw4<OT>::type;
+        RT rg[NA][4], rq[NA][4], rk[NA][4], rb[NA][4], rv[NJ][4], rw[NJ][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) gcv[i] = __expf(ge[3][i]);
-            st4(gc_out + ch0, gcv);
+        for (int ai = 0; ai < NA; ++ai) {
+            const int ch0 = 16 * (wv + 4 * ai) + 4 * lq;
+            ld_rows((const OT*)a.g + rowk0 * DK, rsk, ch0, nvalid, rg[ai]);
+            ld_rows((const OT*)a.q + rowk0 * DK, rsk, ch0, nvalid, rq[ai]);
+            ld_rows((const OT*)a.k + rowk0 * DK, rsk, ch0, nvalid, rk[ai]);
+            ld_rows((const OT*)a.b + rowk0 * DK, rsk, ch0, nvalid, rb[ai]);
         }
-        scaled_factors<OT, DK>((const OT*)a.q + rowk0 * DK, (const OT*)a.k + rowk0 * DK,
-                               (const OT*)a.b + rowk0 * DK, rsk, ch0, nvalid, gam, g0, ge, sXA, sXM, sY,
-                               qg_out, kd_out);
+#pragma unroll
+        for (int ji = 0; ji < NJ; ++ji) {
+            const int ch0 = 16 * (wv + 4 * ji) + 4 * lq;
+            ld_rows((const OT*)a.v + rowk0 * DV, rsv, ch0, nvalid, rv[ji]);
+            ld_rows((const OT*)a.w + rowk0 * DV, rsv, ch0, nvalid, rw[ji]);
+        }
+#pragma unroll
+        for (int ai = 0; ai < NA; ++ai) {
+            const int ch0 = 16 * (wv + 4 * ai) + 4 * lq;
+            float gv[4][4], gam[4][4], g0[4][4], ge[4][4];
+            cvt_rows<OT>(rg[ai], nvalid, gv);
+            gamma_scan(gv, gam, g0, ge);
+            write_factors<DK>(sF, ch0, g0, ge);
+            if (li == 0) {
+                float gcv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gcv[i] = __expf(ge[3][i]);
+                st4(gc_out + ch0, gcv);
+            }
+            float qv[4][4], kv[4][4], bv[4][4];
+            cvt_rows<OT>(rq[ai], nvalid, qv);
+            cvt_rows<OT>(rk[ai], nvalid, kv);
+            cvt_rows<OT>(rb[ai], nvalid, bv);
+            scaled_factors_from<OT, DK>(qv, kv, bv, ch0, gam, g0, ge, sXA, sXM, sY, qg_out, kd_out);
+        }
+#pragma unroll
+        for (int ji = 0; ji < NJ; ++ji) {
+            float vv[4][4], ww[4][4];
+            cvt_rows<OT>(rv[ji], nvalid, vv);
+            cvt_rows<OT>(rw[ji], nvalid, ww);
+            x_tile_from<OT, DV>(vv, ww, 16 * (wv + 4 * ji) + 4 * lq, sX);
+        }
     }
-    for (int jt = wv; jt < DV / 16; jt += 4)
-        chunk_x_tile<OT, DV>((const OT*)a.v + rowk0 * DV, (const OT*)a.w + rowk0 * DV, rsv, jt, nvalid, sX);
     __syncthreads();
 
     // ---- phase 2a: M = lower(Qg Khat^T), computed as M^T tiles, out to global
@@ -197,23 +227,28 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
     }
     blocked_inverse(sA, sT);
 
-    // ---- phase 4: U = T X (tiles) and Wm = T Kb (computed as Wm^T tiles -> row pieces)
+    // ---- phase 4: U = T X (tiles) and Wm = T Kb (computed as Wm^T tiles -> row pieces).
+    // Both K blocks are always multiplied: the upper blocks of T are stored zeros, and
+    // compile-time loops keep the fragments in registers (no dynamic indexing).
     {
-        const int tt = wv;           // token tile of the U / Wm rows
-        const int nkb = tt / 2 + 1;  // T is lower triangular
+        const int tt = wv;  // token tile of the U / Wm rows
         const LSwz<float, CH> vT{sT};
         FT aT[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) aT[kb] = lfrag_rowk<OT, float>(vT, 16 * tt, 32 * kb);
+#pragma unroll
         for (int j = 0; j < DV / 16; ++j) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int kb = 0; kb < nkb; ++kb) mma(acc, aT[kb], lfrag_colk<OT, OT>(vX, 16 * j, 32 * kb));
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) mma(acc, aT[kb], lfrag_colk<OT, OT>(vX, 16 * j, 32 * kb));
             store_tile<OT>(u_out + (j * 4 + tt) * 256, acc);
         }
+#pragma unroll
         for (int at = 0; at < DK / 16; ++at) {
             const int col = 16 * at + li;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int kb = 0; kb < nkb; ++kb) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
                 const float f0 = lds_load<float>(sF + ((F_ER0 + 2 * kb) * DK + col) * 4);
                 const float f1 = lds_load<float>(sF + ((F_ER0 + 2 * kb + 1) * DK + col) * 4);
                 mma(acc, lfrag_colk<OT, OT>(vXA, 16 * at, 32 * kb, f0, f1), aT[kb]);

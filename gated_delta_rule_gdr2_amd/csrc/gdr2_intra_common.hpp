@@ -43,6 +43,35 @@ __device__ __forceinline__ void ld4_row(const IT* base, size_t rs, int r, int ch
     for (int i = 0; i < 4; ++i) out[i] = ok ? out[i] : 0.f;
 }
 
+// Raw 4-element row pieces: loads are issued for a whole phase before any of them
+// is used, so a wave has all of its HBM requests in flight at once.
+template <class OT> struct Raw4;
+template <> struct Raw4<bf16> { typedef bf16x4 type; };
+template <> struct Raw4<float> { typedef f32x4 type; };
+
+// raw[t] = elements ch .. ch + 3 of token row 16 t + li (row clamped to nvalid - 1)
+template <class OT>
+__device__ __forceinline__ void ld_rows(const OT* base, size_t rs, int ch, int nvalid,
+                                        typename Raw4<OT>::type (&raw)[4]) {
+    const int li = lane_id() & 15;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int r = 16 * t + li, rr = r < nvalid ? r : nvalid - 1;
+        raw[t] = *(const typename Raw4<OT>::type*)(base + (size_t)rr * rs + ch);
+    }
+}
+// to fp32, rows at or past nvalid read as zero
+template <class OT>
+__device__ __forceinline__ void cvt_rows(const typename Raw4<OT>::type (&raw)[4], int nvalid, float (&out)[4][4]) {
+    const int li = lane_id() & 15;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const bool ok = 16 * t + li < nvalid;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[t][i] = ok ? (float)raw[t][i] : 0.f;
+    }
+}
+
 template <class OT>
 __device__ __forceinline__ void lds_put4(lds_char* p, const float v[4]) {
     if constexpr (sizeof(OT) == 2) {
@@ -56,16 +85,11 @@ __device__ __forceinline__ void lds_put4(lds_char* p, const float v[4]) {
     }
 }
 
-// Per-lane cumulative log-decay for channel tile `at` (4 channels ch0..ch0+3, rows 16t+li):
-// gam[t][i] (inclusive running sum over the chunk), g0[R][i] = gam at row 16R, ge[R][i] =
-// gam at row 16R+15.
-template <class OT>
-__device__ __forceinline__ void chunk_gamma(const OT* gb, size_t rs, int ch0, int nvalid, float (&gam)[4][4],
-                                            float (&g0)[4][4], float (&ge)[4][4]) {
-    const int li = lane_id() & 15;
-    float gv[4][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) ld4_row(gb, rs, 16 * t + li, ch0, nvalid, gv[t]);
+// Per-lane cumulative log-decay for channel tile `at` (4 channels ch0..ch0+3, rows 16t+li)
+// from the log-decays gv[t][i] of those rows: gam[t][i] (inclusive running sum over the
+// chunk), g0[R][i] = gam at row 16R, ge[R][i] = gam at row 16R+15.
+__device__ __forceinline__ void gamma_scan(const float (&gv)[4][4], float (&gam)[4][4], float (&g0)[4][4],
+                                           float (&ge)[4][4]) {
     float run[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -82,6 +106,15 @@ __device__ __forceinline__ void chunk_gamma(const OT* gb, size_t rs, int ch0, in
             g0[R][i] = row_bcast(gam[R][i], 0);
             ge[R][i] = row_bcast(gam[R][i], 15);
         }
+}
+template <class OT>
+__device__ __forceinline__ void chunk_gamma(const OT* gb, size_t rs, int ch0, int nvalid, float (&gam)[4][4],
+                                            float (&g0)[4][4], float (&ge)[4][4]) {
+    const int li = lane_id() & 15;
+    float gv[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ld4_row(gb, rs, 16 * t + li, ch0, nvalid, gv[t]);
+    gamma_scan(gv, gam, g0, ge);
 }
 
 // Factor arrays for the four channels ch0..ch0+3 (written by the li == 0 lanes).
@@ -113,18 +146,12 @@ __device__ __forceinline__ void write_factors(lds_char* sF, int ch0, const float
 // tiles [CH][DK]; optionally also Qg = q*exp(gam) and Kd = k*exp(gam_C - gam) as swizzled
 // tiles in global memory.
 template <class OT, int DK>
-__device__ __forceinline__ void scaled_factors(const OT* qb, const OT* kb, const OT* bb, size_t rs, int ch0,
-                                               int nvalid, const float (&gam)[4][4], const float (&g0)[4][4],
-                                               const float (&ge)[4][4], lds_char* sXA, lds_char* sXM,
-                                               lds_char* sY, OT* qg_out, OT* kd_out) {
+__device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], const float (&kv)[4][4],
+                                                    const float (&bv)[4][4], int ch0, const float (&gam)[4][4],
+                                                    const float (&g0)[4][4], const float (&ge)[4][4],
+                                                    lds_char* sXA, lds_char* sXM, lds_char* sY, OT* qg_out,
+                                                    OT* kd_out) {
     const int li = lane_id() & 15;
-    float qv[4][4], kv[4][4], bv[4][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        ld4_row(qb, rs, 16 * t + li, ch0, nvalid, qv[t]);
-        ld4_row(kb, rs, 16 * t + li, ch0, nvalid, kv[t]);
-        ld4_row(bb, rs, 16 * t + li, ch0, nvalid, bv[t]);
-    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int r = 16 * t + li;
@@ -147,7 +174,35 @@ __device__ __forceinline__ void scaled_factors(const OT* qb, const OT* kb, const
         if (kd_out) st4(kd_out + swz<OT, DK>(r, ch0), kd);
     }
 }
+template <class OT, int DK>
+__device__ __forceinline__ void scaled_factors(const OT* qb, const OT* kb, const OT* bb, size_t rs, int ch0,
+                                               int nvalid, const float (&gam)[4][4], const float (&g0)[4][4],
+                                               const float (&ge)[4][4], lds_char* sXA, lds_char* sXM,
+                                               lds_char* sY, OT* qg_out, OT* kd_out) {
+    const int li = lane_id() & 15;
+    float qv[4][4], kv[4][4], bv[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        ld4_row(qb, rs, 16 * t + li, ch0, nvalid, qv[t]);
+        ld4_row(kb, rs, 16 * t + li, ch0, nvalid, kv[t]);
+        ld4_row(bb, rs, 16 * t + li, ch0, nvalid, bv[t]);
+    }
+    scaled_factors_from<OT, DK>(qv, kv, bv, ch0, gam, g0, ge, sXA, sXM, sY, qg_out, kd_out);
+}
 
+// X = w * v into a swizzled LDS tile [CH][DV] at columns ch0 .. ch0 + 3
+template <class OT, int DV>
+__device__ __forceinline__ void x_tile_from(const float (&vv)[4][4], const float (&ww)[4][4], int ch0,
+                                            lds_char* sX) {
+    const int li = lane_id() & 15;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = vv[t][i] * ww[t][i];
+        lds_put4<OT>(sX + swz<OT, DV>(16 * t + li, ch0) * (int)sizeof(OT), x);
+    }
+}
 // X = w * v into a swizzled LDS tile [CH][DV] for value-channel tile jt
 template <class OT, int DV>
 __device__ __forceinline__ void chunk_x_tile(const OT* vb, const OT* wb, size_t rs, int jt, int nvalid,
