@@ -45,7 +45,31 @@ struct BwdLds {  // all matrices are swizzled tiles (see swz())
     static constexpr int BYTES = DMD + CH * 4;
 };
 
-// tile dump [DV/16][4][64 lanes][4] -> swizzled LDS tile [CH][DV]
+// tile dump [DV/16][4][64 lanes][4] -> swizzled LDS tile [CH][DV], in two steps so the
+// loads can be issued early: element group e = threadIdx.x + NTHR * u, u < NU
+template <class OT, int DV, int NTHR>
+struct Undump {
+    static constexpr int NU = (DV / 16) * 4 * 64 / NTHR;
+    static_assert((DV / 16) * 4 * 64 % NTHR == 0, "tile dump divides evenly over the threads");
+};
+template <class OT, int DV, int NTHR>
+__device__ __forceinline__ void undump_load(const OT* src, typename Raw4<OT>::type (&raw)[Undump<OT, DV, NTHR>::NU]) {
+#pragma unroll
+    for (int u = 0; u < Undump<OT, DV, NTHR>::NU; ++u)
+        raw[u] = *(const typename Raw4<OT>::type*)(src + (size_t)(threadIdx.x + NTHR * u) * 4);
+}
+template <class OT, int DV, int NTHR>
+__device__ __forceinline__ void undump_store(const typename Raw4<OT>::type (&raw)[Undump<OT, DV, NTHR>::NU],
+                                             lds_char* dst) {
+#pragma unroll
+    for (int u = 0; u < Undump<OT, DV, NTHR>::NU; ++u) {
+        const int e = threadIdx.x + NTHR * u;
+        const int lane = e & 63, t = (e >> 6) & 3, jj = e >> 8;
+        const int row = 16 * t + 4 * (lane >> 4), col = 16 * jj + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_store<OT>(dst + swz<OT, DV>(row + i, col) * (int)sizeof(OT), raw[u][i]);
+    }
+}
 template <class OT, int DV, int NTHR>
 __device__ __forceinline__ void undump_tiles(const OT* src, lds_char* dst) {
     for (int e = threadIdx.x; e < (DV / 16) * 4 * 64; e += NTHR) {
@@ -93,29 +117,71 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     const OT* kb_ = (const OT*)a.k + rowk0 * DK;
     const OT* bb = (const OT*)a.b + rowk0 * DK;
 
+    // ---- loads: every global input of the chunk this wave needs, issued up front.
+    // Wave wv owns key-channel tiles wv + NW ac and value-channel tiles wv + NW ji.
+    using RT = typename Raw4<OT>::type;
+    constexpr int NJW = (DV / 16 + NW - 1) / NW;
+    using UD = Undump<OT, DV, NTHR>;
+    const OT* Sg = (const OT*)(a.ws + L.o_s) + cid * L.s;
+    const OT* dSg = (const OT*)(a.ws + L.o_ds) + cid * L.ds;
+    RT rg[CPW][4], rq[CPW][4], rk[CPW][4], rb[CPW][4], rdo[NJW][4], rv[NJW][4], rw[NJW][4];
+    RT rdl[UD::NU], rdy[UD::NU];
+    // the saved-state fragments are fetched up front too, except for fp32 operands,
+    // where they would not fit in registers next to the rest
+    constexpr bool EARLY_S = sizeof(OT) == 2;
+    FT Sf[CPW][KV], dSf[CPW][KV];
+#pragma unroll
+    for (int ac = 0; ac < CPW; ++ac) {
+        const int at = wv + NW * ac;
+        if (at >= DK / 16) break;
+        const int ch0 = 16 * at + 4 * lq;
+        ld_rows((const OT*)a.g + rowk0 * DK, rsk, ch0, nvalid, rg[ac]);
+        ld_rows(qb, rsk, ch0, nvalid, rq[ac]);
+        ld_rows(kb_, rsk, ch0, nvalid, rk[ac]);
+        ld_rows(bb, rsk, ch0, nvalid, rb[ac]);
+        if (EARLY_S) {
+#pragma unroll
+            for (int kb = 0; kb < KV; ++kb) {
+                Sf[ac][kb] = frag_rowk<OT>(Sg, DV, 16 * at, 32 * kb);
+                dSf[ac][kb] = frag_rowk<OT>(dSg, DV, 16 * at, 32 * kb);
+            }
+        }
+    }
+#pragma unroll
+    for (int ji = 0; ji < NJW; ++ji) {
+        const int jt = wv + NW * ji;
+        if (jt >= DV / 16) break;
+        const int ch0 = 16 * jt + 4 * lq;
+        ld_rows((const OT*)a.dout + rowk0 * DV, rsv, ch0, nvalid, rdo[ji]);
+        ld_rows((const OT*)a.v + rowk0 * DV, rsv, ch0, nvalid, rv[ji]);
+        ld_rows((const OT*)a.w + rowk0 * DV, rsv, ch0, nvalid, rw[ji]);
+    }
+    undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_delta) + cid * L.delta, rdl);
+    undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_dy) + cid * L.dy, rdy);
+
     // ---- phase 1: cumulative decay and factors; dO, Delta, dY into LDS
     float gam[CPW][4][4];
 #pragma unroll
     for (int ac = 0; ac < CPW; ++ac) {
         if (wv + NW * ac >= DK / 16) break;
         const int ch0 = 16 * (wv + NW * ac) + 4 * lq;
-        float g0[4][4], ge[4][4];
-        chunk_gamma((const OT*)a.g + rowk0 * DK, rsk, ch0, nvalid, gam[ac], g0, ge);
+        float gv[4][4], g0[4][4], ge[4][4];
+        cvt_rows<OT>(rg[ac], nvalid, gv);
+        gamma_scan(gv, gam[ac], g0, ge);
         write_factors<DK>(sF, ch0, g0, ge);
     }
-    {
-        const OT* dob = (const OT*)a.dout + rowk0 * DV;
-        for (int jt = wv; jt < DV / 16; jt += NW) {
-            const int ch0 = 16 * jt + 4 * lq;
-            float x[4][4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) ld4_row(dob, rsv, 16 * t + li, ch0, nvalid, x[t]);
+    for (int ji = 0; ji < NJW; ++ji) {
+        const int jt = wv + NW * ji;
+        if (jt >= DV / 16) break;
+        const int ch0 = 16 * jt + 4 * lq;
+        float x[4][4];
+        cvt_rows<OT>(rdo[ji], nvalid, x);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) lds_put4<OT>(sDO + swz<OT, DV>(16 * t + li, ch0) * (int)sizeof(OT), x[t]);
-        }
+        for (int t = 0; t < 4; ++t) lds_put4<OT>(sDO + swz<OT, DV>(16 * t + li, ch0) * (int)sizeof(OT), x[t]);
     }
-    undump_tiles<OT, DV, NTHR>((const OT*)(a.ws + L.o_delta) + cid * L.delta, sDL);
-    undump_tiles<OT, DV, NTHR>((const OT*)(a.ws + L.o_dy) + cid * L.dy, sDY);
+    undump_store<OT, DV, NTHR>(rdl, sDL);
+    undump_store<OT, DV, NTHR>(rdy, sDY);
     for (int idx = tid; idx < CH * CH; idx += NTHR) {  // zero the upper blocks of dA, dM
         const int r = idx / CH, cc = idx % CH;
         if ((cc >> 4) > (r >> 4)) {
@@ -154,25 +220,24 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     //   Pq = exp(gam_R0) * (dO S^T)^T, Pb = -exp(gam_R0) * (dY S^T)^T,
     //   Pk = exp(gam_C - gam_Rend) * (Delta dS'^T)^T
     // The bilinear terms are accumulated into the same registers in phase 3c.
-    const OT* Sg = (const OT*)(a.ws + L.o_s) + cid * L.s;
-    const OT* dSg = (const OT*)(a.ws + L.o_ds) + cid * L.ds;
     f32x4 Pq[CPW][4], Pb[CPW][4], Pk[CPW][4];
     float rsum[CPW], kdx[CPW][4];
 #pragma unroll
     for (int ac = 0; ac < CPW; ++ac) {
         const int at = wv + NW * ac;
         if (at >= DK / 16) break;
-        FT Sf[KV], dSf[KV];
-        float pr = 0.f;
+        if (!EARLY_S) {
 #pragma unroll
-        for (int kb = 0; kb < KV; ++kb) {
-            Sf[kb] = frag_rowk<OT>(Sg, DV, 16 * at, 32 * kb);
-            dSf[kb] = frag_rowk<OT>(dSg, DV, 16 * at, 32 * kb);
+            for (int kb = 0; kb < KV; ++kb) {
+                Sf[ac][kb] = frag_rowk<OT>(Sg, DV, 16 * at, 32 * kb);
+                dSf[ac][kb] = frag_rowk<OT>(dSg, DV, 16 * at, 32 * kb);
+            }
         }
+        float pr = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KV; ++kb)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pr += to_f(Sf[kb][e]) * to_f(dSf[kb][e]);
+            for (int e = 0; e < 8; ++e) pr += to_f(Sf[ac][kb][e]) * to_f(dSf[ac][kb][e]);
         pr += __shfl_xor(pr, 16, 64);
         pr += __shfl_xor(pr, 32, 64);  // rowsum(dS' * S) of key channel 16at + li
         rsum[ac] = pr;
@@ -189,9 +254,9 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             f32x4 q4 = {0.f, 0.f, 0.f, 0.f}, b4 = q4, k4 = q4;
 #pragma unroll
             for (int kb = 0; kb < KV; ++kb) {
-                mma(q4, Sf[kb], lfrag_rowk<OT, OT>(vDO, 16 * t, 32 * kb));
-                mma(b4, Sf[kb], lfrag_rowk<OT, OT>(vDY, 16 * t, 32 * kb));
-                mma(k4, dSf[kb], lfrag_rowk<OT, OT>(vDL, 16 * t, 32 * kb));
+                mma(q4, Sf[ac][kb], lfrag_rowk<OT, OT>(vDO, 16 * t, 32 * kb));
+                mma(b4, Sf[ac][kb], lfrag_rowk<OT, OT>(vDY, 16 * t, 32 * kb));
+                mma(k4, dSf[ac][kb], lfrag_rowk<OT, OT>(vDL, 16 * t, 32 * kb));
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -202,29 +267,25 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             }
         }
         // sum over the chunk's tokens of dKd * Kd (Kd = k * exp(gam_C - gam)), per channel
-        const int ch0 = 16 * at + 4 * lq;
-        float kx[4] = {0.f, 0.f, 0.f, 0.f};
+        float kx[4] = {0.f, 0.f, 0.f, 0.f}, kv[4][4];
+        cvt_rows<OT>(rk[ac], nvalid, kv);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            float kv[4];
-            ld4_row(kb_, rsk, 16 * t + li, ch0, nvalid, kv);
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) kx[i] += Pk[ac][t][i] * kv[i] * __expf(ge[t][i] - gam[ac][t][i]);
-        }
+            for (int i = 0; i < 4; ++i) kx[i] += Pk[ac][t][i] * kv[t][i] * __expf(ge[t][i] - gam[ac][t][i]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) kdx[ac][i] = row_sum16(kx[i]);
     }
-    {  // dv = dY * w, dw = dY * v
-        const OT* vb = (const OT*)a.v + rowk0 * DV;
-        const OT* wb = (const OT*)a.w + rowk0 * DV;
-        for (int jt = wv; jt < DV / 16; jt += NW) {
+    // dv = dY * w, dw = dY * v
+#pragma unroll
+    for (int ji = 0; ji < NJW; ++ji) {
+        const int jt = wv + NW * ji;
+        if (jt >= DV / 16) break;
+        {
             const int ch0 = 16 * jt + 4 * lq;
             float vv[4][4], ww[4][4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                ld4_row(vb, rsv, 16 * t + li, ch0, nvalid, vv[t]);
-                ld4_row(wb, rsv, 16 * t + li, ch0, nvalid, ww[t]);
-            }
+            cvt_rows<OT>(rv[ji], nvalid, vv);
+            cvt_rows<OT>(rw[ji], nvalid, ww);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int r = 16 * t + li;
@@ -257,7 +318,11 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
                 g0[R][i] = row_bcast(gam[ac][R][i], 0);
                 ge[R][i] = row_bcast(gam[ac][R][i], 15);
             }
-        scaled_factors<OT, DK>(qb, kb_, bb, rsk, ch0, nvalid, gam[ac], g0, ge, sXA, sXM, sY, nullptr, nullptr);
+        float qv[4][4], kv[4][4], bv[4][4];
+        cvt_rows<OT>(rq[ac], nvalid, qv);
+        cvt_rows<OT>(rk[ac], nvalid, kv);
+        cvt_rows<OT>(rb[ac], nvalid, bv);
+        scaled_factors_from<OT, DK>(qv, kv, bv, ch0, gam[ac], g0, ge, sXA, sXM, sY, nullptr, nullptr);
     }
     __syncthreads();
 
@@ -303,12 +368,9 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
                 ge[R][i] = row_bcast(gam[ac][R][i], 15);
             }
         float qv[4][4], kv[4][4], bv[4][4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            ld4_row(qb, rsk, 16 * t + li, ch0, nvalid, qv[t]);
-            ld4_row(kb_, rsk, 16 * t + li, ch0, nvalid, kv[t]);
-            ld4_row(bb, rsk, 16 * t + li, ch0, nvalid, bv[t]);
-        }
+        cvt_rows<OT>(rq[ac], nvalid, qv);
+        cvt_rows<OT>(rk[ac], nvalid, kv);
+        cvt_rows<OT>(rb[ac], nvalid, bv);
         float dgam[4][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
