@@ -9,26 +9,34 @@
 //   backward : dDelta = M^T dO + Kd dS' ; dY = T^T dDelta ;
 //              dS = diag(exp gam_C) dS' + Qg^T dO - Wm^T dDelta
 //
-// One workgroup per chain: NW = d_k / 32 compute waves and one producer wave.
+// One workgroup per chain: NW = d_k / 32 compute waves and NP = 2 producer waves.
 //
 // Compute waves split the key axis of the state. Wave w keeps rows 32w .. 32w + 31
-// of the state slice in MFMA accumulator registers for the whole walk and feeds
-// them straight back into the next MFMA (see the K-slot convention in
-// gdr2_device.hpp). Products that contract over the key axis (Wm S, Kd dS',
-// S^T Qg^T) are split over K: each wave forms the partial product of its own rows,
-// the partials meet in LDS behind a barrier, and each wave then updates its own
-// rows and 4 / NW token tiles of the outputs.
+// of the state slice in MFMA accumulator registers, in fp32, for the whole walk
+// (see the K-slot convention in gdr2_device.hpp). What the products need of the
+// state is its operand-type copy, so at the end of every step each wave publishes
+// its rows as one MFMA fragment in LDS; after the next barrier every wave has the
+// whole slice as operands and computes its own 4 / NW token tiles of the
+// contractions over the key axis (Wm S, S^T Qg^T, Kd dS') in full. Those tiles
+// (Delta, dDelta) are published the same way, in the operand type, behind a
+// second barrier; then each wave updates its own rows and finishes its tiles. The
+// values exchanged are exactly the operands the MFMAs consume, so the split does
+// not change the arithmetic.
 //
-// The producer wave streams the per-chunk operands (swizzled tiles written by the
+// The producer waves stream the per-chunk operands (swizzled tiles written by the
 // intra-chunk kernels) into LDS with asynchronous global->LDS DMA, 16 bytes per
-// lane, into two buffers. A chunk step has two phases separated by the exchange
-// barrier, and each phase reads only some of the operands (group 1 before the
-// barrier, group 2 after it), so the producer refills each group as soon as the
-// phase that reads it is over everywhere: group 2 of chunk n + 1 after barrier A of
-// step n, group 1 of chunk n + 2 after barrier B of step n. Before each barrier A it
-// waits for everything but the newest group. The compute waves issue no DMA, so
-// their LDS reads never wait for the transfers in flight, and the transfer time
-// overlaps the whole step.
+// lane, into two buffers (two waves move about 1.5x the bytes per cycle of one). A
+// chunk step has two phases separated by the exchange barrier, and each phase reads
+// only some of the operands (group 1 before the barrier, group 2 after it), so the
+// producers refill each group as soon as the phase that reads it is over everywhere:
+// group 2 of chunk n + 1 after barrier A of step n, group 1 of chunk n + 2 after
+// barrier B of step n. Before each barrier A a producer waits for everything it
+// issued but the newest group. The compute waves issue no DMA, so their LDS reads
+// never wait for the transfers in flight, and the transfers overlap the whole step.
+// Most of these operands were written long before and are no longer in L2, so the
+// producers also pull the operands of the chunk PFD steps ahead into L2, with 4-byte
+// DMAs (one cache line per lane) into a scratch word of LDS; the NJ workgroups of a
+// sequence, which share one XCD's L2, split those lines between them.
 #include "gdr2_device.hpp"
 #include "gdr2_kernels.hpp"
 
@@ -48,24 +56,36 @@ __device__ __forceinline__ void wait_vm() {
 // this wave's index in the workgroup, as a wave-uniform (scalar) value
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// Copy BYTES (a multiple of 1024) from global memory into LDS, 16 bytes per lane:
-// BYTES / 1024 DMA instructions.
+constexpr int NP = 2;  // producer waves per workgroup
+
+// Producer pi's share of a copy of BYTES (a multiple of 1024) from global memory into
+// LDS, 16 bytes per lane: the 1 KB pieces pi, pi + NP, ... (one DMA instruction each).
 template <int BYTES>
-__device__ __forceinline__ void dma16(const void* src, lds_char* dst) {
+__device__ __forceinline__ void dma16(const void* src, lds_char* dst, int pi) {
     static_assert(BYTES % 1024 == 0, "16-byte DMA copies whole 1 KB pieces");
+    constexpr int P = BYTES / 1024;
     const int l = lane_id();
 #pragma unroll
-    for (int k = 0; k < BYTES / 1024; ++k)
-        __builtin_amdgcn_global_load_lds((const char*)src + k * 1024 + l * 16, (lds_void*)(dst + k * 1024), 16, 0, 0);
+    for (int i = 0; i < (P + NP - 1) / NP; ++i) {
+        const int k = i * NP + pi;
+        if (P % NP == 0 || k < P)
+            __builtin_amdgcn_global_load_lds((const char*)src + k * 1024 + l * 16, (lds_void*)(dst + k * 1024), 16,
+                                             0, 0);
+    }
 }
-// Copy BYTES (a multiple of 256), 4 bytes per lane: BYTES / 256 DMA instructions.
+// Producer pi's share of a copy of BYTES (a multiple of 256), 4 bytes per lane.
 template <int BYTES>
-__device__ __forceinline__ void dma4(const void* src, lds_char* dst) {
+__device__ __forceinline__ void dma4(const void* src, lds_char* dst, int pi) {
     static_assert(BYTES % 256 == 0, "4-byte DMA copies whole 256-byte pieces");
+    constexpr int P = BYTES / 256;
     const int l = lane_id();
 #pragma unroll
-    for (int k = 0; k < BYTES / 256; ++k)
-        __builtin_amdgcn_global_load_lds((const char*)src + k * 256 + l * 4, (lds_void*)(dst + k * 256), 4, 0, 0);
+    for (int i = 0; i < (P + NP - 1) / NP; ++i) {
+        const int k = i * NP + pi;
+        if (P % NP == 0 || k < P)
+            __builtin_amdgcn_global_load_lds((const char*)src + k * 256 + l * 4, (lds_void*)(dst + k * 256), 4, 0,
+                                             0);
+    }
 }
 
 // Sequence/slice mapping. Workgroups go to the 8 XCDs round-robin (XCD = id % 8);
@@ -123,23 +143,73 @@ __device__ __forceinline__ void store_rows(OT* dst, int row0, int j, const f32x4
     }
 }
 
-// Exchange area for the split-K partial products: accumulator tiles, one 1 KB slot each.
-__device__ __forceinline__ void xput(lds_char* x, int slot, const f32x4& v) {
-    lds_store<f32x4>(x + (slot * 64 + lane_id()) * 16, v);
+// Exchange areas in LDS, in the operand type OT:
+//   state blocks: slot w holds wave w's 32 state rows as one MFMA fragment
+//                 (64 lanes x 8 elements);
+//   token tiles : slot t holds accumulator tile t (64 lanes x 4 elements).
+template <class OT>
+struct Xch {
+    static constexpr int FRAG = 64 * 8 * (int)sizeof(OT);
+    static constexpr int TILE = 64 * 4 * (int)sizeof(OT);
+    static constexpr int bytes(int nw) { return nw * FRAG + 4 * TILE; }
+};
+template <class OT>
+__device__ __forceinline__ void put_block(lds_char* xs, int w, const f32x4& s0, const f32x4& s1) {
+    using FT = typename Frag<OT>::type;
+    lds_store<FT>(xs + w * Xch<OT>::FRAG + lane_id() * 8 * (int)sizeof(OT), frag_of<OT>(s0, s1));
 }
-__device__ __forceinline__ f32x4 xget(const lds_char* x, int slot) {
-    return lds_load<f32x4>(x + (slot * 64 + lane_id()) * 16);
+template <class OT>
+__device__ __forceinline__ typename Frag<OT>::type get_block(const lds_char* xs, int w) {
+    using FT = typename Frag<OT>::type;
+    return lds_load<FT>(xs + w * Xch<OT>::FRAG + lane_id() * 8 * (int)sizeof(OT));
+}
+template <class OT>
+__device__ __forceinline__ void put_tile(lds_char* xt, int t, const f32x4& d) {
+    typedef typename Raw4<OT>::type R4;
+    R4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = to_ot<OT>(d[i]);
+    lds_store<R4>(xt + t * Xch<OT>::TILE + lane_id() * 4 * (int)sizeof(OT), v);
+}
+// the fragment of token tiles 2 kb and 2 kb + 1 (a 32-token K block)
+template <class OT>
+__device__ __forceinline__ typename Frag<OT>::type get_tiles(const lds_char* xt, int kb) {
+    typedef typename Raw4<OT>::type R4;
+    const R4 lo = lds_load<R4>(xt + (2 * kb) * Xch<OT>::TILE + lane_id() * 4 * (int)sizeof(OT));
+    const R4 hi = lds_load<R4>(xt + (2 * kb + 1) * Xch<OT>::TILE + lane_id() * 4 * (int)sizeof(OT));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 constexpr int LDS_LIMIT = 160 * 1024;
 
-// The producer's side of a walk over NT chunks (walk index n = 0 .. NT - 1). G1(n, buf)
-// and G2(n, buf) issue the DMA of operand groups 1 and 2 of the chunk at walk index n;
-// G1N is the number of DMA instructions G1 issues. Two buffers: barriers A_n and
-// B_n of every step, as the compute waves have them. One buffer: a third barrier C_n
-// ends every step and the transfers do not overlap compute.
-template <bool DBUF, int G1N, class F1, class F2>
-__device__ __forceinline__ void produce(int NT, lds_char* b0, lds_char* b1, F1 G1, F2 G2) {
+constexpr int PFD = 3;  // L2 prefetch distance in chunk steps
+
+// L2 prefetch of one chunk's operands: the lines of a list of regions are numbered
+// 0 .. LINES - 1 in order; workgroup j of NJ, producer pi touches lines
+// (( i * NP + pi) * 64 + lane) * NJ + j, i < NPF (lines past the end repeat the last).
+// line(v) returns the address of line v. NPF DMA instructions, always.
+template <int LINES, int NJ, class FL>
+__device__ __forceinline__ void prefetch_lines(FL line, int j, int pi, lds_char* slot) {
+    constexpr int NPF = (LINES + NJ * 64 * NP - 1) / (NJ * 64 * NP);
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+        int v = ((i * NP + pi) * 64 + l) * NJ + j;
+        v = v < LINES ? v : LINES - 1;
+        __builtin_amdgcn_global_load_lds(line(v), (lds_void*)slot, 4, 0, 0);
+    }
+}
+template <int LINES, int NJ>
+constexpr int prefetch_count() { return (LINES + NJ * 64 * NP - 1) / (NJ * 64 * NP); }
+
+// A producer's side of a walk over NT chunks (walk index n = 0 .. NT - 1). G1(n, buf)
+// and G2(n, buf) issue its share of the DMA of operand groups 1 and 2 of the chunk at
+// walk index n; G1N is the number of DMA instructions in its share of G1. PF(n) issues
+// the NPF prefetch DMAs for the chunk at walk index min(n, NT - 1). Two buffers:
+// barriers A_n and B_n of every step, as the compute waves have them. One buffer: a
+// third barrier C_n ends every step and the transfers do not overlap compute.
+template <bool DBUF, int G1N, int NPF, class F1, class F2, class FP>
+__device__ __forceinline__ void produce(int NT, lds_char* b0, lds_char* b1, F1 G1, F2 G2, FP PF) {
     if (DBUF) {
         G1(0, b0);
         G2(0, b0);
@@ -155,7 +225,8 @@ __device__ __forceinline__ void produce(int NT, lds_char* b0, lds_char* b1, F1 G
             sync_lds();  // B_n: group 1 of b0 is no longer read
             if (n + 2 < NT) {
                 G1(n + 2, b0);
-                wait_vm<G1N>();
+                PF(n + PFD);
+                wait_vm<G1N + NPF>();
             } else {
                 wait_vm<0>();
             }
@@ -165,7 +236,8 @@ __device__ __forceinline__ void produce(int NT, lds_char* b0, lds_char* b1, F1 G
             sync_lds();  // B_{n+1}
             if (n + 3 < NT) {
                 G1(n + 3, b1);
-                wait_vm<G1N>();
+                PF(n + 1 + PFD);
+                wait_vm<G1N + NPF>();
             } else {
                 wait_vm<0>();
             }
@@ -174,6 +246,7 @@ __device__ __forceinline__ void produce(int NT, lds_char* b0, lds_char* b1, F1 G
         G1(0, b0);
         G2(0, b0);
         wait_vm<0>();
+        (void)PF;
         for (int n = 0; n < NT; ++n) {
             sync_lds();  // A_n
             sync_lds();  // B_n
@@ -191,10 +264,10 @@ struct FwdChainBuf {
     static constexpr int ES = sizeof(OT);
     static constexpr int WM = 0;                  // group 1: Wm [64][DK] swizzled
     static constexpr int QG = WM + CH * DK * ES;  // group 1: Qg [64][DK]
-    static constexpr int KD = QG + CH * DK * ES;  // group 2: Kd [64][DK]
+    static constexpr int U = QG + CH * DK * ES;   // group 1: the 4 U tiles of this slice
+    static constexpr int KD = U + 4 * 256 * ES;   // group 2: Kd [64][DK]
     static constexpr int M = KD + CH * DK * ES;   // group 2: M [64][64]
-    static constexpr int U = M + CH * CH * ES;    // group 2: the 4 U tiles of this slice
-    static constexpr int GC = U + 4 * 256 * ES;   // group 2: exp(gam_C), DK floats
+    static constexpr int GC = M + CH * CH * ES;   // group 2: exp(gam_C), DK floats
     static constexpr int BYTES = GC + DK * 4;
 };
 
@@ -233,10 +306,11 @@ __device__ __forceinline__ void fwd_flush(const Args& a, int s, int j, FwdPend<O
     }
 }
 
-// One chunk step of a compute wave; contains barrier B of the step.
+// One chunk step of a compute wave; contains barrier B of the step. On entry the
+// state blocks of all waves are in xs; on exit this wave's new block is.
 template <class OT, int DK, int DV, bool TRAIN, bool OUT, int NW>
 __device__ __forceinline__ void fwd_step(int c, const lds_char* buf, f32x4& S0, f32x4& S1, lds_char* stage,
-                                         lds_char* xch, FwdPend<OT, NW>& pd) {
+                                         lds_char* xs, lds_char* xt, FwdPend<OT, NW>& pd) {
     using B = FwdChainBuf<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
     constexpr int TPW = FwdPend<OT, NW>::TPW;
@@ -244,49 +318,37 @@ __device__ __forceinline__ void fwd_step(int c, const lds_char* buf, f32x4& S0, 
     const LSwz<OT, DK> vWM{buf + B::WM}, vKD{buf + B::KD}, vQG{buf + B::QG};
     const LSwz<OT, CH> vM{buf + B::M};
     if (TRAIN) stage_rows<OT>(stage, S0, S1, pd.st);  // chunk start state -> pending row-major store
-    const FT SB = frag_of<OT>(S0, S1);                  // this wave's 32-row K block of the state
-    // phase 1 (group 1): split-K partials over this wave's key rows,
-    // Wm S into slots 8w + t, S^T Qg^T into slots 8w + 4 + t
+    // phase 1 (group 1): Delta = U - Wm S and S^T Qg^T on this wave's token tiles
+    FT SB[NW];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        f32x4 p = {0.f, 0.f, 0.f, 0.f};
-        mma(p, lfrag_rowk<OT, OT>(vWM, 16 * t, 32 * wv), SB);
-        xput(xch, 8 * wv + t, p);
-        if (OUT) {
-            f32x4 po = {0.f, 0.f, 0.f, 0.f};
-            mma(po, SB, lfrag_rowk<OT, OT>(vQG, 16 * t, 32 * wv));
-            xput(xch, 8 * wv + 4 + t, po);
+    for (int kb = 0; kb < NW; ++kb) SB[kb] = get_block<OT>(xs, kb);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int t = wv * TPW + u;
+        f32x4 ws = {0.f, 0.f, 0.f, 0.f}, po = ws;
+#pragma unroll
+        for (int kb = 0; kb < NW; ++kb) {
+            mma(ws, lfrag_rowk<OT, OT>(vWM, 16 * t, 32 * kb), SB[kb]);
+            if (OUT) mma(po, SB[kb], lfrag_rowk<OT, OT>(vQG, 16 * t, 32 * kb));
         }
+        float uu[4];
+        lds_get4<OT>(buf + B::U + (t * 256 + l * 4) * (int)sizeof(OT), uu);
+        const f32x4 d = {uu[0] - ws[0], uu[1] - ws[1], uu[2] - ws[2], uu[3] - ws[3]};
+        put_tile<OT>(xt, t, d);
+        pd.D[u] = d;
+        pd.O[u] = po;
     }
     sync_lds();  // B
-    // phase 2 (group 2): Delta = U - Wm S, all four token tiles in every wave
-    f32x4 D[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        float u[4];
-        lds_get4<OT>(buf + B::U + (t * 256 + l * 4) * (int)sizeof(OT), u);
-        f32x4 acc = {u[0], u[1], u[2], u[3]};
-#pragma unroll
-        for (int w = 0; w < NW; ++w) acc -= xget(xch, 8 * w + t);
-        D[t] = acc;
-    }
+    // phase 2 (group 2): Delta as operands; O^T += Delta^T M^T; S' on this wave's rows
     FT DB[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) DB[kb] = frag_of<OT>(D[2 * kb], D[2 * kb + 1]);
-    // O^T tiles of this wave: S^T Qg^T (summed partials) + Delta^T M^T
+    for (int kb = 0; kb < 2; ++kb) DB[kb] = get_tiles<OT>(xt, kb);
     if (OUT) {
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int t = wv * TPW + u;
-            f32x4 acc = xget(xch, 4 + t);
+        for (int u = 0; u < TPW; ++u)
 #pragma unroll
-            for (int w = 1; w < NW; ++w) acc += xget(xch, 8 * w + 4 + t);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) mma(acc, DB[kb], lfrag_rowk<OT, OT>(vM, 16 * t, 32 * kb));
-            pd.O[u] = acc;
-        }
+            for (int kb = 0; kb < 2; ++kb) mma(pd.O[u], DB[kb], lfrag_rowk<OT, OT>(vM, 16 * (wv * TPW + u), 32 * kb));
     }
-    // S' = diag(exp gam_C) S + Kd^T Delta on this wave's rows
     {
         float g0[4], g1[4];
         lds_get4<float>(buf + B::GC + (32 * wv + 4 * lq) * 4, g0);
@@ -301,34 +363,65 @@ __device__ __forceinline__ void fwd_step(int c, const lds_char* buf, f32x4& S0, 
         S0 = a0;
         S1 = a1;
     }
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) pd.D[u] = D[wv * TPW + u];
+    put_block<OT>(xs, wv, S0, S1);  // every wave has read xs before barrier B
     pd.c = c;
 }
 
 template <class OT, int DK, int DV, bool TRAIN, bool OUT, int NW, bool DBUF>
-__device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, lds_char* b0, lds_char* b1, lds_char* xch,
-                                         lds_char* stage_base) {
+__device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, lds_char* b0, lds_char* b1, lds_char* xs,
+                                         lds_char* stage_base, lds_char* pfslot) {
     using B = FwdChainBuf<OT, DK, DV>;
     const int wv = wave_id();
     const int NT = a.NT;
     const long long base = (long long)s * NT;
-    if (wv == NW) {  // producer
+    if (wv >= NW) {  // producer
         const Layout& L = a.L;
+        const int pi = wv - NW;
         auto G1 = [&](int n, lds_char* buf) {
             const long long cid = base + n;
-            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM);
-            if (OUT) dma16<CH * DK * sizeof(OT)>(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG);
+            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM, pi);
+            if (OUT) dma16<CH * DK * sizeof(OT)>(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG, pi);
+            dma16<4 * 256 * sizeof(OT)>(a.ws + L.o_u + (cid * L.u + (size_t)j * 4 * 256) * sizeof(OT), buf + B::U,
+                                        pi);
         };
         auto G2 = [&](int n, lds_char* buf) {
             const long long cid = base + n;
-            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_kd + cid * L.kd * sizeof(OT), buf + B::KD);
-            if (OUT) dma16<CH * CH * sizeof(OT)>(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M);
-            dma16<4 * 256 * sizeof(OT)>(a.ws + L.o_u + (cid * L.u + (size_t)j * 4 * 256) * sizeof(OT), buf + B::U);
-            dma4<DK * 4>(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC);
+            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_kd + cid * L.kd * sizeof(OT), buf + B::KD, pi);
+            if (OUT) dma16<CH * CH * sizeof(OT)>(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M, pi);
+            dma4<DK * 4>(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC, pi);
         };
-        constexpr int G1N = (OUT ? 2 : 1) * CH * DK * (int)sizeof(OT) / 1024;
-        produce<DBUF, G1N>(NT, b0, b1, G1, G2);
+        constexpr int P1 = CH * DK * (int)sizeof(OT) / 1024;  // pieces of Wm and Qg
+        constexpr int PU = 4 * 256 * (int)sizeof(OT) / 1024;  // pieces of the U tiles
+        static_assert(P1 % NP == 0 && PU % NP == 0, "group 1 splits evenly over the producers");
+        constexpr int G1N = ((OUT ? 2 : 1) * P1 + PU) / NP;
+        // prefetch regions: Wm, Kd, U (all slices), exp(gam_C) [, Qg, M]
+        constexpr int LK = CH * DK * (int)sizeof(OT) / 128, LU = CH * DV * (int)sizeof(OT) / 128;
+        constexpr int LM = CH * CH * (int)sizeof(OT) / 128, LG = DK * 4 / 128;
+        constexpr int LINES = 2 * LK + LU + LG + (OUT ? LK + LM : 0);
+        constexpr int NJ = DV / 16;
+        auto PF = [&](int n) {
+            const long long cid = base + (n < NT ? n : NT - 1);
+            const char* wm = a.ws + L.o_wm + cid * L.wm * sizeof(OT);
+            const char* kd = a.ws + L.o_kd + cid * L.kd * sizeof(OT);
+            const char* u = a.ws + L.o_u + cid * L.u * sizeof(OT);
+            const char* gc = a.ws + L.o_gc + cid * L.gc * 4;
+            const char* qg = a.ws + L.o_qg + cid * L.qg * sizeof(OT);
+            const char* m = a.ws + L.o_m + cid * L.m * sizeof(OT);
+            auto line = [&](int v) -> const char* {
+                if (v < LK) return wm + v * 128;
+                v -= LK;
+                if (v < LK) return kd + v * 128;
+                v -= LK;
+                if (v < LU) return u + v * 128;
+                v -= LU;
+                if (v < LG) return gc + v * 128;
+                v -= LG;
+                if (v < LK) return qg + v * 128;
+                return m + (v - LK) * 128;
+            };
+            prefetch_lines<LINES, NJ>(line, j, pi, pfslot);
+        };
+        produce<DBUF, G1N, prefetch_count<LINES, NJ>()>(NT, b0, b1, G1, G2, PF);
         return;
     }
     // compute waves: state rows 32 wv + 4 lq + i (S0) and 32 wv + 16 + 4 lq + i (S1),
@@ -342,23 +435,25 @@ __device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, lds_char* 
         S0[i] = a.h0 ? a.h0[r0 + (size_t)i * DV] : 0.f;
         S1[i] = a.h0 ? a.h0[r0 + (size_t)(16 + i) * DV] : 0.f;
     }
+    lds_char* xt = xs + NW * Xch<OT>::FRAG;
+    put_block<OT>(xs, wv, S0, S1);
     FwdPend<OT, NW> pd;
     pd.c = -1;
     if (DBUF) {
         for (int n = 0; n < NT; n += 2) {
             sync_lds();  // A_n
             fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
-            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n, b0, S0, S1, stage, xch, pd);
+            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n, b0, S0, S1, stage, xs, xt, pd);
             if (n + 1 >= NT) break;
             sync_lds();  // A_{n+1}
             fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
-            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n + 1, b1, S0, S1, stage, xch, pd);
+            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n + 1, b1, S0, S1, stage, xs, xt, pd);
         }
     } else {
         for (int n = 0; n < NT; ++n) {
             sync_lds();  // A_n
             fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
-            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n, b0, S0, S1, stage, xch, pd);
+            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n, b0, S0, S1, stage, xs, xt, pd);
             sync_lds();  // C_n
         }
     }
@@ -373,24 +468,25 @@ __device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, lds_char* 
 }
 
 template <class OT, int DK, int DV, bool TRAIN>
-__global__ __launch_bounds__(64 * (DK / 32 + 1)) void k_fwd_chain(Args a) {
+__global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_fwd_chain(Args a) {
     using B = FwdChainBuf<OT, DK, DV>;
     constexpr int NW = DK / 32, NJ = DV / 16;
-    constexpr int XBYTES = NW * 8 * 1024;
+    constexpr int XBYTES = Xch<OT>::bytes(NW);
     constexpr int SBYTES = NW * RowStore<OT>::BYTES;
-    constexpr bool DBUF = 2 * B::BYTES + XBYTES + SBYTES <= LDS_LIMIT;
+    constexpr bool DBUF = 2 * B::BYTES + XBYTES + SBYTES + 256 <= LDS_LIMIT;
     __shared__ __align__(16) char buf0[B::BYTES];
     __shared__ __align__(16) char buf1[DBUF ? B::BYTES : 16];
     __shared__ __align__(16) char xch[XBYTES];
     __shared__ __align__(16) char stage[SBYTES];
+    __shared__ __align__(16) char pfslot[256];  // target of the L2 prefetch DMAs, never read
     int s, j;
     chain_map(blockIdx.x, a.B * a.H, NJ, s, j);
     if (a.o)
         fwd_walk<OT, DK, DV, TRAIN, true, NW, DBUF>(a, s, j, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch,
-                                                    (lds_char*)stage);
+                                                    (lds_char*)stage, (lds_char*)pfslot);
     else
         fwd_walk<OT, DK, DV, TRAIN, false, NW, DBUF>(a, s, j, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch,
-                                                     (lds_char*)stage);
+                                                     (lds_char*)stage, (lds_char*)pfslot);
 }
 
 // ============================================================================ backward chain
@@ -428,10 +524,11 @@ __device__ __forceinline__ void bwd_flush(const Args& a, int s, int j, BwdPend<O
     for (int u = 0; u < TPW; ++u) store_tile<OT>(dy + (wv * TPW + u) * 256, pd.Y[u]);
 }
 
-// One chunk step of a compute wave; contains barrier B of the step.
+// One chunk step of a compute wave; contains barrier B of the step. On entry the
+// gradient blocks of all waves are in xs; on exit this wave's new block is.
 template <class OT, int DK, int DV, int NW>
 __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0, f32x4& dS1, lds_char* stage,
-                                         lds_char* xch, BwdPend<OT, NW>& pd) {
+                                         lds_char* xs, lds_char* xt, BwdPend<OT, NW>& pd) {
     using B = BwdChainBuf<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
     constexpr int TPW = BwdPend<OT, NW>::TPW;
@@ -444,39 +541,25 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0,
     FT dOB[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) dOB[kb] = lfrag_colk<OT, OT>(vDO, 0, 32 * kb);
-    const FT dSB = frag_of<OT>(dS0, dS1);
-    // M^T dO on this wave's token tiles
-    f32x4 pm[TPW];
+    FT dSB[NW];
+#pragma unroll
+    for (int kb = 0; kb < NW; ++kb) dSB[kb] = get_block<OT>(xs, kb);
+    // dDelta = M^T dO + Kd dS' on this wave's token tiles
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-        pm[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int t = wv * TPW + u;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(pm[u], lfrag_colk<OT, OT>(vM, 16 * (wv * TPW + u), 32 * kb), dOB[kb]);
-    }
-    // split-K partials of Kd dS' over this wave's key rows (slot 4w + t), plus M^T dO
-    // on the tiles this wave owns
+        for (int kb = 0; kb < NW; ++kb) mma(acc, lfrag_rowk<OT, OT>(vKD, 16 * t, 32 * kb), dSB[kb]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        f32x4 p = {0.f, 0.f, 0.f, 0.f};
-        mma(p, lfrag_rowk<OT, OT>(vKD, 16 * t, 32 * wv), dSB);
-        const bool own = t / TPW == wv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] += own ? pm[t % TPW][i] : 0.f;
-        xput(xch, 4 * wv + t, p);
+        for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vM, 16 * t, 32 * kb), dOB[kb]);
+        put_tile<OT>(xt, t, acc);
     }
     sync_lds();  // B
-    // phase 2 (group 2)
-    f32x4 dD[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        f32x4 acc = xget(xch, t);
-#pragma unroll
-        for (int w = 1; w < NW; ++w) acc += xget(xch, 4 * w + t);
-        dD[t] = acc;
-    }
+    // phase 2 (group 2): dDelta as operands
     FT dDB[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) dDB[kb] = frag_of<OT>(dD[2 * kb], dD[2 * kb + 1]);
+    for (int kb = 0; kb < 2; ++kb) dDB[kb] = get_tiles<OT>(xt, kb);
     // dS = diag(exp gam_C) dS' + Qg^T dO - Wm^T dDelta on this wave's rows
     {
         float g0[4], g1[4];
@@ -504,18 +587,20 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0,
         for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vT, 16 * t, 32 * kb), dDB[kb]);
         pd.Y[u] = acc;
     }
+    put_block<OT>(xs, wv, dS0, dS1);  // every wave has read xs before barrier B
     pd.c = c;
 }
 
 template <class OT, int DK, int DV, int NW, bool DBUF>
-__device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* b0, lds_char* b1, lds_char* xch,
-                                         lds_char* stage_base) {
+__device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* b0, lds_char* b1, lds_char* xs,
+                                         lds_char* stage_base, lds_char* pfslot) {
     using B = BwdChainBuf<OT, DK, DV>;
     const int wv = wave_id();
     const int NT = a.NT, last = NT - 1;
     const long long base = (long long)s * NT;
-    if (wv == NW) {  // producer; walk index n is chunk last - n
+    if (wv >= NW) {  // producer; walk index n is chunk last - n
         const Layout& L = a.L;
+        const int pi = wv - NW;
         const int l = lane_id();
         const int bidx = s / a.H, h = s % a.H;
         constexpr int EPL = 4 / sizeof(OT);           // dO elements per lane and instruction
@@ -523,13 +608,14 @@ __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* 
         auto G1 = [&](int n, lds_char* buf) {
             const int c = last - n;
             const long long cid = base + c;
-            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_kd + cid * L.kd * sizeof(OT), buf + B::KD);
-            dma16<CH * CH * sizeof(OT)>(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M);
+            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_kd + cid * L.kd * sizeof(OT), buf + B::KD, pi);
+            dma16<CH * CH * sizeof(OT)>(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M, pi);
             // dO rows of this slice. Rows past the end of the sequence repeat its last row:
             // every product that reads dO (M^T dO, Qg^T dO) multiplies those rows by rows of
             // M and Qg that the intra-chunk kernel wrote as exact zeros.
 #pragma unroll
-            for (int k = 0; k < 64 / RPI; ++k) {
+            for (int i = 0; i < 64 / RPI / NP; ++i) {
+                const int k = i * NP + pi;
                 const int r = k * RPI + l / (16 / EPL);
                 const int col = (l % (16 / EPL)) * EPL;
                 const int row = min(c * CH + r, a.T - 1);
@@ -539,13 +625,49 @@ __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* 
         };
         auto G2 = [&](int n, lds_char* buf) {
             const long long cid = base + (last - n);
-            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM);
-            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG);
-            dma16<CH * CH * sizeof(OT)>(a.ws + L.o_t + cid * L.t * sizeof(OT), buf + B::T);
-            dma4<DK * 4>(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC);
+            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM, pi);
+            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG, pi);
+            dma16<CH * CH * sizeof(OT)>(a.ws + L.o_t + cid * L.t * sizeof(OT), buf + B::T, pi);
+            dma4<DK * 4>(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC, pi);
         };
-        constexpr int G1N = (CH * DK + CH * CH) * (int)sizeof(OT) / 1024 + 64 / RPI;
-        produce<DBUF, G1N>(NT, b0, b1, G1, G2);
+        constexpr int PK = CH * DK * (int)sizeof(OT) / 1024, PM = CH * CH * (int)sizeof(OT) / 1024;
+        static_assert(PK % NP == 0 && PM % NP == 0 && (64 / RPI) % NP == 0,
+                      "group 1 splits evenly over the producers");
+        constexpr int G1N = (PK + PM + 64 / RPI) / NP;
+        // prefetch regions: Kd, Qg, Wm, M, T, exp(gam_C), dO rows (all slices)
+        constexpr int LK = CH * DK * (int)sizeof(OT) / 128, LM = CH * CH * (int)sizeof(OT) / 128;
+        constexpr int LG = DK * 4 / 128, LR = DV * (int)sizeof(OT) / 128;  // lines per dO row
+        constexpr int LINES = 3 * LK + 2 * LM + LG + CH * LR;
+        constexpr int NJ = DV / 16;
+        auto PF = [&](int n) {
+            const int c = last - (n < NT ? n : NT - 1);
+            const long long cid = base + c;
+            const char* kd = a.ws + L.o_kd + cid * L.kd * sizeof(OT);
+            const char* qg = a.ws + L.o_qg + cid * L.qg * sizeof(OT);
+            const char* wm = a.ws + L.o_wm + cid * L.wm * sizeof(OT);
+            const char* m = a.ws + L.o_m + cid * L.m * sizeof(OT);
+            const char* t = a.ws + L.o_t + cid * L.t * sizeof(OT);
+            const char* gc = a.ws + L.o_gc + cid * L.gc * 4;
+            auto line = [&](int v) -> const char* {
+                if (v < LK) return kd + v * 128;
+                v -= LK;
+                if (v < LK) return qg + v * 128;
+                v -= LK;
+                if (v < LK) return wm + v * 128;
+                v -= LK;
+                if (v < LM) return m + v * 128;
+                v -= LM;
+                if (v < LM) return t + v * 128;
+                v -= LM;
+                if (v < LG) return gc + v * 128;
+                v -= LG;
+                const int row = min(c * CH + v / LR, a.T - 1);
+                return (const char*)a.dout + ((((size_t)bidx * a.T + row) * a.H + h) * DV) * sizeof(OT) +
+                       (v % LR) * 128;
+            };
+            prefetch_lines<LINES, NJ>(line, j, pi, pfslot);
+        };
+        produce<DBUF, G1N, prefetch_count<LINES, NJ>()>(NT, b0, b1, G1, G2, PF);
         return;
     }
     const int l = lane_id(), li = l & 15, lq = l >> 4;
@@ -557,23 +679,25 @@ __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* 
         dS0[i] = a.dht ? a.dht[r0 + (size_t)i * DV] : 0.f;
         dS1[i] = a.dht ? a.dht[r0 + (size_t)(16 + i) * DV] : 0.f;
     }
+    lds_char* xt = xs + NW * Xch<OT>::FRAG;
+    put_block<OT>(xs, wv, dS0, dS1);
     BwdPend<OT, NW> pd;
     pd.c = -1;
     if (DBUF) {
         for (int n = 0; n < NT; n += 2) {
             sync_lds();  // A_n
             bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
-            bwd_step<OT, DK, DV, NW>(last - n, b0, dS0, dS1, stage, xch, pd);
+            bwd_step<OT, DK, DV, NW>(last - n, b0, dS0, dS1, stage, xs, xt, pd);
             if (n + 1 >= NT) break;
             sync_lds();  // A_{n+1}
             bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
-            bwd_step<OT, DK, DV, NW>(last - n - 1, b1, dS0, dS1, stage, xch, pd);
+            bwd_step<OT, DK, DV, NW>(last - n - 1, b1, dS0, dS1, stage, xs, xt, pd);
         }
     } else {
         for (int n = 0; n < NT; ++n) {
             sync_lds();  // A_n
             bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
-            bwd_step<OT, DK, DV, NW>(last - n, b0, dS0, dS1, stage, xch, pd);
+            bwd_step<OT, DK, DV, NW>(last - n, b0, dS0, dS1, stage, xs, xt, pd);
             sync_lds();  // C_n
         }
     }
@@ -588,25 +712,27 @@ __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* 
 }
 
 template <class OT, int DK, int DV>
-__global__ __launch_bounds__(64 * (DK / 32 + 1)) void k_bwd_chain(Args a) {
+__global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_bwd_chain(Args a) {
     using B = BwdChainBuf<OT, DK, DV>;
     constexpr int NW = DK / 32, NJ = DV / 16;
-    constexpr int XBYTES = NW * 4 * 1024;
+    constexpr int XBYTES = Xch<OT>::bytes(NW);
     constexpr int SBYTES = NW * RowStore<OT>::BYTES;
-    constexpr bool DBUF = 2 * B::BYTES + XBYTES + SBYTES <= LDS_LIMIT;
+    constexpr bool DBUF = 2 * B::BYTES + XBYTES + SBYTES + 256 <= LDS_LIMIT;
     __shared__ __align__(16) char buf0[B::BYTES];
     __shared__ __align__(16) char buf1[DBUF ? B::BYTES : 16];
     __shared__ __align__(16) char xch[XBYTES];
     __shared__ __align__(16) char stage[SBYTES];
+    __shared__ __align__(16) char pfslot[256];  // target of the L2 prefetch DMAs, never read
     int s, j;
     chain_map(blockIdx.x, a.B * a.H, NJ, s, j);
-    bwd_walk<OT, DK, DV, NW, DBUF>(a, s, j, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch, (lds_char*)stage);
+    bwd_walk<OT, DK, DV, NW, DBUF>(a, s, j, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch, (lds_char*)stage,
+                                   (lds_char*)pfslot);
 }
 
 // ============================================================================ launchers
 template <class OT, int DK, int DV>
 hipError_t launch_fwd_chain_t(const Args& a, bool train, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.B * a.H * (DV / 16))), block(64 * (DK / 32 + 1));
+    const dim3 grid((unsigned)(a.B * a.H * (DV / 16))), block(64 * (DK / 32 + NP));
     if (train)
         hipLaunchKernelGGL((k_fwd_chain<OT, DK, DV, true>), grid, block, 0, stream, a);
     else
@@ -615,7 +741,7 @@ hipError_t launch_fwd_chain_t(const Args& a, bool train, hipStream_t stream) {
 }
 template <class OT, int DK, int DV>
 hipError_t launch_bwd_chain_t(const Args& a, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.B * a.H * (DV / 16))), block(64 * (DK / 32 + 1));
+    const dim3 grid((unsigned)(a.B * a.H * (DV / 16))), block(64 * (DK / 32 + NP));
     hipLaunchKernelGGL((k_bwd_chain<OT, DK, DV>), grid, block, 0, stream, a);
     return hipGetLastError();
 }

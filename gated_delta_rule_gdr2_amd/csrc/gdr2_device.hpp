@@ -37,6 +37,11 @@ constexpr int NPAIR = NBLK * (NBLK + 1) / 2;  // lower-triangular 16x16 block pa
 template <class OT> struct Frag;
 template <> struct Frag<bf16> { typedef bf16x8 type; };
 template <> struct Frag<float> { typedef f32x8 type; };
+// four consecutive elements in the operand type (half a fragment, or one lane's share
+// of an accumulator tile)
+template <class OT> struct Raw4;
+template <> struct Raw4<bf16> { typedef bf16x4 type; };
+template <> struct Raw4<float> { typedef f32x4 type; };
 
 __device__ __forceinline__ int kmap(int lq, int e) { return 16 * (e >> 2) + 4 * lq + (e & 3); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

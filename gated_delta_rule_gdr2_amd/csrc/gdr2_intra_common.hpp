@@ -43,11 +43,8 @@ __device__ __forceinline__ void ld4_row(const IT* base, size_t rs, int r, int ch
     for (int i = 0; i < 4; ++i) out[i] = ok ? out[i] : 0.f;
 }
 
-// Raw 4-element row pieces: loads are issued for a whole phase before any of them
-// is used, so a wave has all of its HBM requests in flight at once.
-template <class OT> struct Raw4;
-template <> struct Raw4<bf16> { typedef bf16x4 type; };
-template <> struct Raw4<float> { typedef f32x4 type; };
+// Raw 4-element row pieces (Raw4, gdr2_device.hpp): loads are issued for a whole
+// phase before any of them is used, so a wave has all of its HBM requests in flight.
 
 // raw[t] = elements ch .. ch + 3 of token row 16 t + li (row clamped to nvalid - 1)
 template <class OT>
