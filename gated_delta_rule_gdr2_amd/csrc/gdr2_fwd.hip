@@ -128,51 +128,65 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
     float* gc_out = (float*)(a.ws + L.o_gc) + cid * L.gc;
 
     // ---- phase 1: cumulative decay, factors, Qg / Kd / exp(gam_C) out, X = w*v.
-    // Wave wv owns key-channel tiles wv + 4 ai and value-channel tiles wv + 4 ji; all of
-    // its input loads are issued before any is used.
+    // Inputs are read 16 bytes per lane: lane (li, lq) of a wave takes rows 16 t + li and
+    // W consecutive channels of a GC = 4 W channel group; wave wv owns key-channel groups
+    // wv + 4 ai and value-channel groups wv + 4 ji. All loads are issued before any use;
+    // the arithmetic then runs on 4-channel quarters.
     {
-        constexpr int NA = DK / 64, NJ = DV / 64;
-        using RT = typename Raw4<OT>::type;
+        constexpr int W = 16 / (int)sizeof(OT), GC = 4 * W;
+        constexpr int NGK = DK / GC, NGV = DV / GC;
+        constexpr int NA = (NGK + 3) / 4, NJ = (NGV + 3) / 4;
+        using RT = typename Raw16<OT>::type;
         RT rg[NA][4], rq[NA][4], rk[NA][4], rb[NA][4], rv[NJ][4], rw[NJ][4];
 #pragma unroll
         for (int ai = 0; ai < NA; ++ai) {
-            const int ch0 = 16 * (wv + 4 * ai) + 4 * lq;
-            ld_rows((const OT*)a.g + rowk0 * DK, rsk, ch0, nvalid, rg[ai]);
-            ld_rows((const OT*)a.q + rowk0 * DK, rsk, ch0, nvalid, rq[ai]);
-            ld_rows((const OT*)a.k + rowk0 * DK, rsk, ch0, nvalid, rk[ai]);
-            ld_rows((const OT*)a.b + rowk0 * DK, rsk, ch0, nvalid, rb[ai]);
+            if (wv + 4 * ai >= NGK) break;
+            const int ch = GC * (wv + 4 * ai) + W * lq;
+            ld_rows16((const OT*)a.g + rowk0 * DK, rsk, ch, nvalid, rg[ai]);
+            ld_rows16((const OT*)a.q + rowk0 * DK, rsk, ch, nvalid, rq[ai]);
+            ld_rows16((const OT*)a.k + rowk0 * DK, rsk, ch, nvalid, rk[ai]);
+            ld_rows16((const OT*)a.b + rowk0 * DK, rsk, ch, nvalid, rb[ai]);
         }
 #pragma unroll
         for (int ji = 0; ji < NJ; ++ji) {
-            const int ch0 = 16 * (wv + 4 * ji) + 4 * lq;
-            ld_rows((const OT*)a.v + rowk0 * DV, rsv, ch0, nvalid, rv[ji]);
-            ld_rows((const OT*)a.w + rowk0 * DV, rsv, ch0, nvalid, rw[ji]);
+            if (wv + 4 * ji >= NGV) break;
+            const int ch = GC * (wv + 4 * ji) + W * lq;
+            ld_rows16((const OT*)a.v + rowk0 * DV, rsv, ch, nvalid, rv[ji]);
+            ld_rows16((const OT*)a.w + rowk0 * DV, rsv, ch, nvalid, rw[ji]);
         }
 #pragma unroll
         for (int ai = 0; ai < NA; ++ai) {
-            const int ch0 = 16 * (wv + 4 * ai) + 4 * lq;
-            float gv[4][4], gam[4][4], g0[4][4], ge[4][4];
-            cvt_rows<OT>(rg[ai], nvalid, gv);
-            gamma_scan(gv, gam, g0, ge);
-            write_factors<DK>(sF, ch0, g0, ge);
-            if (li == 0) {
-                float gcv[4];
+            if (wv + 4 * ai >= NGK) break;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) gcv[i] = __expf(ge[3][i]);
-                st4(gc_out + ch0, gcv);
+            for (int hq = 0; hq < W / 4; ++hq) {
+                const int ch0 = GC * (wv + 4 * ai) + W * lq + 4 * hq;
+                float gv[4][4], gam[4][4], g0[4][4], ge[4][4];
+                cvt_rows16<OT>(rg[ai], hq, nvalid, gv);
+                gamma_scan(gv, gam, g0, ge);
+                write_factors<DK>(sF, ch0, g0, ge);
+                if (li == 0) {
+                    float gcv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) gcv[i] = __expf(ge[3][i]);
+                    st4(gc_out + ch0, gcv);
+                }
+                float qv[4][4], kv[4][4], bv[4][4];
+                cvt_rows16<OT>(rq[ai], hq, nvalid, qv);
+                cvt_rows16<OT>(rk[ai], hq, nvalid, kv);
+                cvt_rows16<OT>(rb[ai], hq, nvalid, bv);
+                scaled_factors_from<OT, DK>(qv, kv, bv, ch0, gam, g0, ge, sXA, sXM, sY, qg_out, kd_out);
             }
-            float qv[4][4], kv[4][4], bv[4][4];
-            cvt_rows<OT>(rq[ai], nvalid, qv);
-            cvt_rows<OT>(rk[ai], nvalid, kv);
-            cvt_rows<OT>(rb[ai], nvalid, bv);
-            scaled_factors_from<OT, DK>(qv, kv, bv, ch0, gam, g0, ge, sXA, sXM, sY, qg_out, kd_out);
         }
 #pragma unroll
         for (int ji = 0; ji < NJ; ++ji) {
-            float vv[4][4], ww[4][4];
-            cvt_rows<OT>(rv[ji], nvalid, vv);
-            cvt_rows<OT>(rw[ji], nvalid, ww);
-            x_tile_from<OT, DV>(vv, ww, 16 * (wv + 4 * ji) + 4 * lq, sX);
+            if (wv + 4 * ji >= NGV) break;
+#pragma unroll
+            for (int hq = 0; hq < W / 4; ++hq) {
+                float vv[4][4], ww[4][4];
+                cvt_rows16<OT>(rv[ji], hq, nvalid, vv);
+                cvt_rows16<OT>(rw[ji], hq, nvalid, ww);
+                x_tile_from<OT, DV>(vv, ww, GC * (wv + 4 * ji) + W * lq + 4 * hq, sX);
+            }
         }
     }
     __syncthreads();

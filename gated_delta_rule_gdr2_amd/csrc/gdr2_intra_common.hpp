@@ -69,6 +69,35 @@ __device__ __forceinline__ void cvt_rows(const typename Raw4<OT>::type (&raw)[4]
     }
 }
 
+// 16-byte row pieces: raw[t] = elements ch .. ch + 16 / sizeof(OT) - 1 of token row
+// 16 t + li (row clamped to nvalid - 1)
+template <class OT> struct Raw16;
+template <> struct Raw16<bf16> { typedef bf16x8 type; };
+template <> struct Raw16<float> { typedef f32x4 type; };
+template <class OT>
+__device__ __forceinline__ void ld_rows16(const OT* base, size_t rs, int ch, int nvalid,
+                                          typename Raw16<OT>::type (&raw)[4]) {
+    const int li = lane_id() & 15;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int r = 16 * t + li, rr = r < nvalid ? r : nvalid - 1;
+        raw[t] = *(const typename Raw16<OT>::type*)(base + (size_t)rr * rs + ch);
+    }
+}
+// quarter hq (elements 4 hq .. 4 hq + 3) of 16-byte row pieces, to fp32; rows at or past
+// nvalid read as zero
+template <class OT>
+__device__ __forceinline__ void cvt_rows16(const typename Raw16<OT>::type (&raw)[4], int hq, int nvalid,
+                                           float (&out)[4][4]) {
+    const int li = lane_id() & 15;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const bool ok = 16 * t + li < nvalid;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[t][i] = ok ? (float)raw[t][4 * hq + i] : 0.f;
+    }
+}
+
 template <class OT>
 __device__ __forceinline__ void lds_put4(lds_char* p, const float v[4]) {
     if constexpr (sizeof(OT) == 2) {
