@@ -66,8 +66,28 @@ __device__ __forceinline__ void undump_store(const typename Raw4<OT>::type (&raw
         const int e = threadIdx.x + NTHR * u;
         const int lane = e & 63, t = (e >> 6) & 3, jj = e >> 8;
         const int row = 16 * t + 4 * (lane >> 4), col = 16 * jj + (lane & 15);
+        if constexpr (sizeof(OT) == 2) {
+            // Lanes col and col ^ 1 (a DPP pair) hold rows row .. row + 3 of adjacent columns;
+            // they swap halves so that each stores two rows as 4-byte column pairs.
+            typedef __attribute__((address_space(3))) uint32_t U32;
+            const bool odd = lane & 1;
+            const bf16x4 v = raw[u];
+            const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v, v, 0, 1));
+            const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v, v, 2, 3));
+            const uint32_t send = odd ? lo : hi;
+            const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+            const uint32_t mine = odd ? hi : lo;  // rows row + 2, 3 (odd) or row + 0, 1 (even) of this column
+            // the column-c0 and column-c0 + 1 halves; w0 / w1 = first / second row, low half = column c0
+            const uint32_t lowsrc = odd ? recv : mine, highsrc = odd ? mine : recv;
+            const uint32_t w0 = __builtin_amdgcn_perm(highsrc, lowsrc, 0x05040100);
+            const uint32_t w1 = __builtin_amdgcn_perm(highsrc, lowsrc, 0x07060302);
+            const int r0 = row + (odd ? 2 : 0), c0 = col & ~1;
+            *(U32*)(dst + swz<OT, DV>(r0, c0) * 2) = w0;
+            *(U32*)(dst + swz<OT, DV>(r0 + 1, c0) * 2) = w1;
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_store<OT>(dst + swz<OT, DV>(row + i, col) * (int)sizeof(OT), raw[u][i]);
+            for (int i = 0; i < 4; ++i) lds_store<OT>(dst + swz<OT, DV>(row + i, col) * (int)sizeof(OT), raw[u][i]);
+        }
     }
 }
 template <class OT, int DV, int NTHR>
@@ -120,11 +140,16 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     // ---- loads: every global input of the chunk this wave needs, issued up front.
     // Wave wv owns key-channel tiles wv + NW ac and value-channel tiles wv + NW ji.
     using RT = typename Raw4<OT>::type;
-    constexpr int NJW = (DV / 16 + NW - 1) / NW;
     using UD = Undump<OT, DV, NTHR>;
     const OT* Sg = (const OT*)(a.ws + L.o_s) + cid * L.s;
     const OT* dSg = (const OT*)(a.ws + L.o_ds) + cid * L.ds;
-    RT rg[CPW][4], rq[CPW][4], rk[CPW][4], rb[CPW][4], rdo[NJW][4], rv[NJW][4], rw[NJW][4];
+    // value-side inputs (dO, v, w) are read 16 bytes per lane: piece p = wv + NW i covers
+    // row tile p % 4 and the GV = 4 WV channel group p / 4 (lane: WV channels)
+    constexpr int WV = 16 / (int)sizeof(OT), GV = 4 * WV, NPV = 4 * (DV / GV);
+    constexpr int NPW = (NPV + NW - 1) / NW;
+    using RW = typename Raw16<OT>::type;
+    RT rg[CPW][4], rq[CPW][4], rk[CPW][4], rb[CPW][4];
+    RW rdo[NPW], rv[NPW], rw[NPW];
     RT rdl[UD::NU], rdy[UD::NU];
     // the saved-state fragments are fetched up front too, except for fp32 operands,
     // where they would not fit in registers next to the rest
@@ -142,19 +167,20 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         if (EARLY_S) {
 #pragma unroll
             for (int kb = 0; kb < KV; ++kb) {
-                Sf[ac][kb] = frag_rowk<OT>(Sg, DV, 16 * at, 32 * kb);
-                dSf[ac][kb] = frag_rowk<OT>(dSg, DV, 16 * at, 32 * kb);
+                Sf[ac][kb] = frag_rowk8<OT>(Sg, DV, 16 * at, 32 * kb);
+                dSf[ac][kb] = frag_rowk8<OT>(dSg, DV, 16 * at, 32 * kb);
             }
         }
     }
 #pragma unroll
-    for (int ji = 0; ji < NJW; ++ji) {
-        const int jt = wv + NW * ji;
-        if (jt >= DV / 16) break;
-        const int ch0 = 16 * jt + 4 * lq;
-        ld_rows((const OT*)a.dout + rowk0 * DV, rsv, ch0, nvalid, rdo[ji]);
-        ld_rows((const OT*)a.v + rowk0 * DV, rsv, ch0, nvalid, rv[ji]);
-        ld_rows((const OT*)a.w + rowk0 * DV, rsv, ch0, nvalid, rw[ji]);
+    for (int i = 0; i < NPW; ++i) {
+        const int pc = wv + NW * i;
+        if (pc >= NPV) break;
+        const int r = 16 * (pc & 3) + li, rr = r < nvalid ? r : nvalid - 1;
+        const size_t off = (rowk0 + (size_t)rr * a.H) * DV + GV * (pc >> 2) + WV * lq;
+        rdo[i] = *(const RW*)((const OT*)a.dout + off);
+        rv[i] = *(const RW*)((const OT*)a.v + off);
+        rw[i] = *(const RW*)((const OT*)a.w + off);
     }
     undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_delta) + cid * L.delta, rdl);
     undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_dy) + cid * L.dy, rdy);
@@ -171,14 +197,13 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         write_factors<DK>(sF, ch0, g0, ge);
     }
 #pragma unroll
-    for (int ji = 0; ji < NJW; ++ji) {
-        const int jt = wv + NW * ji;
-        if (jt >= DV / 16) break;
-        const int ch0 = 16 * jt + 4 * lq;
-        float x[4][4];
-        cvt_rows<OT>(rdo[ji], nvalid, x);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) lds_put4<OT>(sDO + swz<OT, DV>(16 * t + li, ch0) * (int)sizeof(OT), x[t]);
+    for (int i = 0; i < NPW; ++i) {
+        const int pc = wv + NW * i;
+        if (pc >= NPV) break;
+        const int r = 16 * (pc & 3) + li;
+        RW x = rdo[i];
+        if (r >= nvalid) x = RW{};
+        lds_store<RW>(sDO + swz<OT, DV>(r, GV * (pc >> 2) + WV * lq) * (int)sizeof(OT), x);
     }
     undump_store<OT, DV, NTHR>(rdl, sDL);
     undump_store<OT, DV, NTHR>(rdy, sDY);
@@ -196,6 +221,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     // kept apart in fp32 (sDMd) so that its query-side and key-side terms cancel
     // exactly in the log-decay gradient instead of up to bf16 rounding.
     const LSwz<OT, DV> vDO{sDO}, vDL{sDL}, vDY{sDY};
+    // Computed as transposed tiles (Delta rows as the A operand), so that each lane holds
+    // four consecutive columns of one row and stores them as one 4-element piece.
     for (int p = wv; p < 2 * NPAIR; p += NW) {
         const bool isM = p >= NPAIR;
         int R, I;
@@ -203,15 +230,17 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KV; ++kb)
-            mma(acc, lfrag_rowk<OT, OT>(isM ? vDO : vDY, 16 * R, 32 * kb), lfrag_rowk<OT, OT>(vDL, 16 * I, 32 * kb));
+            mma(acc, lfrag_rowk8<OT>(vDL, 16 * I, 32 * kb), lfrag_rowk8<OT>(isM ? vDO : vDY, 16 * R, 32 * kb));
+        const int row = 16 * R + li, col0 = 16 * I + 4 * lq;  // acc[i]: (row, col0 + i)
+        float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * R + 4 * lq + i, col = 16 * I + li;
-            float v = isM ? acc[i] : -acc[i];
-            if (isM && col == row) lds_store<float>(sDMd + row * 4, v);
-            if (R == I && col >= row) v = 0.f;  // dA strictly lower; dM diagonal kept in sDMd
-            lds_store<OT>((isM ? sDM : sDA) + swz<OT, CH>(row, col) * (int)sizeof(OT), to_ot<OT>(v));
+            const int col = col0 + i;
+            v[i] = isM ? acc[i] : -acc[i];
+            if (isM && col == row) lds_store<float>(sDMd + row * 4, v[i]);
+            if (R == I && col >= row) v[i] = 0.f;  // dA strictly lower; dM diagonal kept in sDMd
         }
+        lds_put4<OT>((isM ? sDM : sDA) + swz<OT, CH>(row, col0) * (int)sizeof(OT), v);
     }
     __syncthreads();
 
@@ -229,8 +258,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         if (!EARLY_S) {
 #pragma unroll
             for (int kb = 0; kb < KV; ++kb) {
-                Sf[ac][kb] = frag_rowk<OT>(Sg, DV, 16 * at, 32 * kb);
-                dSf[ac][kb] = frag_rowk<OT>(dSg, DV, 16 * at, 32 * kb);
+                Sf[ac][kb] = frag_rowk8<OT>(Sg, DV, 16 * at, 32 * kb);
+                dSf[ac][kb] = frag_rowk8<OT>(dSg, DV, 16 * at, 32 * kb);
             }
         }
         float pr = 0.f;
@@ -254,9 +283,9 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             f32x4 q4 = {0.f, 0.f, 0.f, 0.f}, b4 = q4, k4 = q4;
 #pragma unroll
             for (int kb = 0; kb < KV; ++kb) {
-                mma(q4, Sf[ac][kb], lfrag_rowk<OT, OT>(vDO, 16 * t, 32 * kb));
-                mma(b4, Sf[ac][kb], lfrag_rowk<OT, OT>(vDY, 16 * t, 32 * kb));
-                mma(k4, dSf[ac][kb], lfrag_rowk<OT, OT>(vDL, 16 * t, 32 * kb));
+                mma(q4, Sf[ac][kb], lfrag_rowk8<OT>(vDO, 16 * t, 32 * kb));
+                mma(b4, Sf[ac][kb], lfrag_rowk8<OT>(vDY, 16 * t, 32 * kb));
+                mma(k4, dSf[ac][kb], lfrag_rowk8<OT>(vDL, 16 * t, 32 * kb));
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -276,31 +305,22 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) kdx[ac][i] = row_sum16(kx[i]);
     }
-    // dv = dY * w, dw = dY * v
+    // dv = dY * w, dw = dY * v, 16 bytes per lane
 #pragma unroll
-    for (int ji = 0; ji < NJW; ++ji) {
-        const int jt = wv + NW * ji;
-        if (jt >= DV / 16) break;
-        {
-            const int ch0 = 16 * jt + 4 * lq;
-            float vv[4][4], ww[4][4];
-            cvt_rows<OT>(rv[ji], nvalid, vv);
-            cvt_rows<OT>(rw[ji], nvalid, ww);
+    for (int i = 0; i < NPW; ++i) {
+        const int pc = wv + NW * i;
+        if (pc >= NPV) break;
+        const int r = 16 * (pc & 3) + li, ch = GV * (pc >> 2) + WV * lq;
+        const RW dy = lds_load<RW>(sDY + swz<OT, DV>(r, ch) * (int)sizeof(OT));
+        RW dvv, dww;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int r = 16 * t + li;
-                float dy[4], dvv[4], dww[4];
-                lds_get4<OT>(sDY + swz<OT, DV>(r, ch0) * (int)sizeof(OT), dy);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    dvv[i] = dy[i] * ww[t][i];
-                    dww[i] = dy[i] * vv[t][i];
-                }
-                if (r < nvalid) {
-                    st4((OT*)a.dv + rowk0 * DV + (size_t)r * rsv + ch0, dvv);
-                    st4((OT*)a.dw + rowk0 * DV + (size_t)r * rsv + ch0, dww);
-                }
-            }
+        for (int e = 0; e < WV; ++e) {
+            dvv[e] = to_ot<OT>(to_f(dy[e]) * to_f(rw[i][e]));
+            dww[e] = to_ot<OT>(to_f(dy[e]) * to_f(rv[i][e]));
+        }
+        if (r < nvalid) {
+            *(RW*)((OT*)a.dv + rowk0 * DV + (size_t)r * rsv + ch) = dvv;
+            *(RW*)((OT*)a.dw + rowk0 * DV + (size_t)r * rsv + ch) = dww;
         }
     }
     __syncthreads();  // dO, Delta, dY are dead; their slots take the key/query factors

@@ -126,6 +126,21 @@ __device__ __forceinline__ typename Frag<OT>::type frag_rowk(const OT* X, int ld
         return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 }
+// "rowk8": the contiguous K-slot map k = k0 + 8*lq + e. Usable for a product only when
+// both operands are read from memory with it (never with an accumulator-derived
+// operand): lane (li, lq) reads X[row0 + li][k0 + 8*lq .. + 7], one 16-byte piece for
+// bf16.
+template <class OT>
+__device__ __forceinline__ typename Frag<OT>::type frag_rowk8(const OT* X, int ld, int row0, int k0) {
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    const OT* p = X + (size_t)(row0 + li) * ld + k0 + 8 * lq;
+    if constexpr (sizeof(OT) == 2) {
+        return *(const bf16x8*)p;
+    } else {
+        f32x4 x0 = *(const f32x4*)p, x1 = *(const f32x4*)(p + 4);
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
 // rowk from an fp32 matrix, converted to the operand type
 template <class OT>
 __device__ __forceinline__ typename Frag<OT>::type frag_rowk_f32(const float* X, int ld, int row0, int k0) {
@@ -300,6 +315,19 @@ __device__ __forceinline__ typename Frag<OT>::type lfrag_rowk(const V& m, int ro
         f[4 + i] = to_ot<OT>(b[i]);
     }
     return f;
+}
+// rowk8 (contiguous K-slot map, see frag_rowk8) from a matrix in LDS of the operand type
+template <class OT, class V>
+__device__ __forceinline__ typename Frag<OT>::type lfrag_rowk8(const V& m, int row0, int k0) {
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    const lds_char* p0 = m.p + m.off(row0 + li, k0 + 8 * lq);
+    if constexpr (sizeof(OT) == 2) {
+        return lds_load<bf16x8>(p0);
+    } else {
+        const lds_char* p1 = m.p + m.off(row0 + li, k0 + 8 * lq + 4);
+        f32x4 x0 = lds_load<f32x4>(p0), x1 = lds_load<f32x4>(p1);
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
 }
 // colk: lane (li, lq) gets X[k0 + kmap(lq, e)][col0 + li], optionally scaled by rs0 (e < 4)
 // and rs1 (e >= 4). bf16: two transposing reads; fp32: eight scalar reads.
