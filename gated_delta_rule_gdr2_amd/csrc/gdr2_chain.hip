@@ -14,25 +14,20 @@
 // Compute waves split the key axis of the state. Wave w keeps rows 32w .. 32w + 31
 // of the state slice in MFMA accumulator registers, in fp32, for the whole walk
 // (see the K-slot convention in gdr2_device.hpp). What the products need of the
-// state is its operand-type copy, so at the end of every step each wave publishes
-// its rows as one MFMA fragment in LDS; after the next barrier every wave has the
-// whole slice as operands and computes its own 4 / NW token tiles of the
-// contractions over the key axis (Wm S, S^T Qg^T, Kd dS') in full. Those tiles
-// (Delta, dDelta) are published the same way, in the operand type, behind a
-// second barrier; then each wave updates its own rows and finishes its tiles. The
-// values exchanged are exactly the operands the MFMAs consume, so the split does
-// not change the arithmetic.
+// state is its operand-type copy: at the end of every step each wave publishes its
+// rows as one MFMA fragment in LDS (two alternating copies), and after the step's
+// barrier every wave has the whole slice as operands. Each wave then forms all four
+// token tiles of Delta (or dDelta) itself -- the contraction over the key axis is
+// repeated in every wave, which costs MFMA issue slots but no exchange and no second
+// barrier -- and uses them, still in registers, to update its own rows and to finish
+// its own token tiles of the outputs. One barrier per chunk step.
 //
 // The producer waves stream the per-chunk operands (swizzled tiles written by the
 // intra-chunk kernels) into LDS with asynchronous global->LDS DMA, 16 bytes per
-// lane, into two buffers (two waves move about 1.5x the bytes per cycle of one). A
-// chunk step has two phases separated by the exchange barrier, and each phase reads
-// only some of the operands (group 1 before the barrier, group 2 after it), so the
-// producers refill each group as soon as the phase that reads it is over everywhere:
-// group 2 of chunk n + 1 after barrier A of step n, group 1 of chunk n + 2 after
-// barrier B of step n. Before each barrier A a producer waits for everything it
-// issued but the newest group. The compute waves issue no DMA, so their LDS reads
-// never wait for the transfers in flight, and the transfers overlap the whole step.
+// lane, into two buffers (two waves move about 1.5x the bytes per cycle of one):
+// the operands of chunk n + 1 are fetched during step n, into the buffer that step
+// n - 1 used, and waited for before the barrier that opens step n + 1. The compute
+// waves issue no DMA, so their LDS reads never wait for the transfers in flight.
 // Most of these operands were written long before and are no longer in L2, so the
 // producers also pull the operands of the chunk PFD steps ahead into L2, with 4-byte
 // DMAs (one cache line per lane) into a scratch word of LDS; the NJ workgroups of a
@@ -143,15 +138,13 @@ __device__ __forceinline__ void store_rows(OT* dst, int row0, int j, const f32x4
     }
 }
 
-// Exchange areas in LDS, in the operand type OT:
-//   state blocks: slot w holds wave w's 32 state rows as one MFMA fragment
-//                 (64 lanes x 8 elements);
-//   token tiles : slot t holds accumulator tile t (64 lanes x 4 elements).
+// Exchange area in LDS: two alternating copies of the state blocks, in the operand
+// type; slot w of a copy holds wave w's 32 state rows as one MFMA fragment
+// (64 lanes x 8 elements).
 template <class OT>
 struct Xch {
     static constexpr int FRAG = 64 * 8 * (int)sizeof(OT);
-    static constexpr int TILE = 64 * 4 * (int)sizeof(OT);
-    static constexpr int bytes(int nw) { return nw * FRAG + 4 * TILE; }
+    static constexpr int bytes(int nw) { return 2 * nw * FRAG; }
 };
 template <class OT>
 __device__ __forceinline__ void put_block(lds_char* xs, int w, const f32x4& s0, const f32x4& s1) {
@@ -162,22 +155,6 @@ template <class OT>
 __device__ __forceinline__ typename Frag<OT>::type get_block(const lds_char* xs, int w) {
     using FT = typename Frag<OT>::type;
     return lds_load<FT>(xs + w * Xch<OT>::FRAG + lane_id() * 8 * (int)sizeof(OT));
-}
-template <class OT>
-__device__ __forceinline__ void put_tile(lds_char* xt, int t, const f32x4& d) {
-    typedef typename Raw4<OT>::type R4;
-    R4 v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = to_ot<OT>(d[i]);
-    lds_store<R4>(xt + t * Xch<OT>::TILE + lane_id() * 4 * (int)sizeof(OT), v);
-}
-// the fragment of token tiles 2 kb and 2 kb + 1 (a 32-token K block)
-template <class OT>
-__device__ __forceinline__ typename Frag<OT>::type get_tiles(const lds_char* xt, int kb) {
-    typedef typename Raw4<OT>::type R4;
-    const R4 lo = lds_load<R4>(xt + (2 * kb) * Xch<OT>::TILE + lane_id() * 4 * (int)sizeof(OT));
-    const R4 hi = lds_load<R4>(xt + (2 * kb + 1) * Xch<OT>::TILE + lane_id() * 4 * (int)sizeof(OT));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 constexpr int LDS_LIMIT = 160 * 1024;
@@ -202,58 +179,43 @@ __device__ __forceinline__ void prefetch_lines(FL line, int j, int pi, lds_char*
 template <int LINES, int NJ>
 constexpr int prefetch_count() { return (LINES + NJ * 64 * NP - 1) / (NJ * 64 * NP); }
 
-// A producer's side of a walk over NT chunks (walk index n = 0 .. NT - 1). G1(n, buf)
-// and G2(n, buf) issue its share of the DMA of operand groups 1 and 2 of the chunk at
-// walk index n; G1N is the number of DMA instructions in its share of G1. PF(n) issues
-// the NPF prefetch DMAs for the chunk at walk index min(n, NT - 1). Two buffers:
-// barriers A_n and B_n of every step, as the compute waves have them. One buffer: a
-// third barrier C_n ends every step and the transfers do not overlap compute.
-template <bool DBUF, int G1N, int NPF, class F1, class F2, class FP>
-__device__ __forceinline__ void produce(int NT, lds_char* b0, lds_char* b1, F1 G1, F2 G2, FP PF) {
+// A producer's side of a walk over NT chunks (walk index n = 0 .. NT - 1). G(n, buf)
+// issues its share of the DMA of all operands of the chunk at walk index n; PF(n)
+// issues the NPF prefetch DMAs for the chunk at walk index min(n, NT - 1). Two
+// buffers: one barrier per step, as the compute waves have it (A_n opens step n).
+// One buffer: a second barrier C_n closes every step, and the transfers do not
+// overlap compute.
+template <bool DBUF, int NPF, class FG, class FP>
+__device__ __forceinline__ void produce(int NT, lds_char* b0, lds_char* b1, FG G, FP PF) {
     if (DBUF) {
-        G1(0, b0);
-        G2(0, b0);
-        if (NT > 1) {
-            G1(1, b1);
-            wait_vm<G1N>();
-        } else {
-            wait_vm<0>();
-        }
+        G(0, b0);
+        wait_vm<0>();
         for (int n = 0; n < NT; n += 2) {
-            sync_lds();  // A_n: chunk n is in b0, b1 is no longer read after phase 2
-            if (n + 1 < NT) G2(n + 1, b1);
-            sync_lds();  // B_n: group 1 of b0 is no longer read
-            if (n + 2 < NT) {
-                G1(n + 2, b0);
+            sync_lds();  // A_n: chunk n is in b0; b1 is free (step n - 1 is over)
+            if (n + 1 < NT) {
+                G(n + 1, b1);
                 PF(n + PFD);
-                wait_vm<G1N + NPF>();
-            } else {
-                wait_vm<0>();
+                wait_vm<NPF>();
             }
             if (n + 1 >= NT) break;
-            sync_lds();  // A_{n+1}
-            if (n + 2 < NT) G2(n + 2, b0);
-            sync_lds();  // B_{n+1}
-            if (n + 3 < NT) {
-                G1(n + 3, b1);
+            sync_lds();  // A_{n+1}: chunk n + 1 is in b1; b0 is free
+            if (n + 2 < NT) {
+                G(n + 2, b0);
                 PF(n + 1 + PFD);
-                wait_vm<G1N + NPF>();
-            } else {
-                wait_vm<0>();
+                wait_vm<NPF>();
             }
         }
     } else {
-        G1(0, b0);
-        G2(0, b0);
+        G(0, b0);
         wait_vm<0>();
         (void)PF;
         for (int n = 0; n < NT; ++n) {
             sync_lds();  // A_n
-            sync_lds();  // B_n
-            if (n + 1 < NT) G1(n + 1, b0);
             sync_lds();  // C_n
-            if (n + 1 < NT) G2(n + 1, b0);
-            wait_vm<0>();
+            if (n + 1 < NT) {
+                G(n + 1, b0);
+                wait_vm<0>();
+            }
         }
     }
 }
@@ -262,12 +224,12 @@ __device__ __forceinline__ void produce(int NT, lds_char* b0, lds_char* b1, F1 G
 template <class OT, int DK, int DV>
 struct FwdChainBuf {
     static constexpr int ES = sizeof(OT);
-    static constexpr int WM = 0;                  // group 1: Wm [64][DK] swizzled
-    static constexpr int QG = WM + CH * DK * ES;  // group 1: Qg [64][DK]
-    static constexpr int U = QG + CH * DK * ES;   // group 1: the 4 U tiles of this slice
-    static constexpr int KD = U + 4 * 256 * ES;   // group 2: Kd [64][DK]
-    static constexpr int M = KD + CH * DK * ES;   // group 2: M [64][64]
-    static constexpr int GC = M + CH * CH * ES;   // group 2: exp(gam_C), DK floats
+    static constexpr int WM = 0;                  // Wm [64][DK] swizzled
+    static constexpr int QG = WM + CH * DK * ES;  // Qg [64][DK]
+    static constexpr int U = QG + CH * DK * ES;   // the 4 U tiles of this slice
+    static constexpr int KD = U + 4 * 256 * ES;   // Kd [64][DK]
+    static constexpr int M = KD + CH * DK * ES;   // M [64][64]
+    static constexpr int GC = M + CH * CH * ES;   // exp(gam_C), DK floats
     static constexpr int BYTES = GC + DK * 4;
 };
 
@@ -306,49 +268,53 @@ __device__ __forceinline__ void fwd_flush(const Args& a, int s, int j, FwdPend<O
     }
 }
 
-// One chunk step of a compute wave; contains barrier B of the step. On entry the
-// state blocks of all waves are in xs; on exit this wave's new block is.
+// One chunk step of a compute wave. On entry the state blocks of all waves are in xr;
+// on exit this wave's new block is in xw (the other copy).
 template <class OT, int DK, int DV, bool TRAIN, bool OUT, int NW>
 __device__ __forceinline__ void fwd_step(int c, const lds_char* buf, f32x4& S0, f32x4& S1, lds_char* stage,
-                                         lds_char* xs, lds_char* xt, FwdPend<OT, NW>& pd) {
+                                         const lds_char* xr, lds_char* xw, FwdPend<OT, NW>& pd) {
     using B = FwdChainBuf<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
     constexpr int TPW = FwdPend<OT, NW>::TPW;
     const int l = lane_id(), lq = l >> 4, wv = wave_id();
     const LSwz<OT, DK> vWM{buf + B::WM}, vKD{buf + B::KD}, vQG{buf + B::QG};
     const LSwz<OT, CH> vM{buf + B::M};
-    if (TRAIN) stage_rows<OT>(stage, S0, S1, pd.st);  // chunk start state -> pending row-major store
-    // phase 1 (group 1): Delta = U - Wm S and S^T Qg^T on this wave's token tiles
     FT SB[NW];
 #pragma unroll
-    for (int kb = 0; kb < NW; ++kb) SB[kb] = get_block<OT>(xs, kb);
+    for (int kb = 0; kb < NW; ++kb) SB[kb] = get_block<OT>(xr, kb);
+    if (TRAIN) stage_rows<OT>(stage, S0, S1, pd.st);  // chunk start state -> pending row-major store
+    // Delta = U - Wm S, all four token tiles
+    f32x4 D[4];
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int t = wv * TPW + u;
-        f32x4 ws = {0.f, 0.f, 0.f, 0.f}, po = ws;
+    for (int t = 0; t < 4; ++t) D[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < NW; ++kb) {
-            mma(ws, lfrag_rowk<OT, OT>(vWM, 16 * t, 32 * kb), SB[kb]);
-            if (OUT) mma(po, SB[kb], lfrag_rowk<OT, OT>(vQG, 16 * t, 32 * kb));
-        }
+    for (int kb = 0; kb < NW; ++kb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) mma(D[t], lfrag_rowk<OT, OT>(vWM, 16 * t, 32 * kb), SB[kb]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
         float uu[4];
         lds_get4<OT>(buf + B::U + (t * 256 + l * 4) * (int)sizeof(OT), uu);
-        const f32x4 d = {uu[0] - ws[0], uu[1] - ws[1], uu[2] - ws[2], uu[3] - ws[3]};
-        put_tile<OT>(xt, t, d);
-        pd.D[u] = d;
-        pd.O[u] = po;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) D[t][i] = uu[i] - D[t][i];
     }
-    sync_lds();  // B
-    // phase 2 (group 2): Delta as operands; O^T += Delta^T M^T; S' on this wave's rows
     FT DB[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) DB[kb] = get_tiles<OT>(xt, kb);
+    for (int kb = 0; kb < 2; ++kb) DB[kb] = frag_of<OT>(D[2 * kb], D[2 * kb + 1]);
+    // O^T = S^T Qg^T + Delta^T M^T on this wave's token tiles
     if (OUT) {
 #pragma unroll
-        for (int u = 0; u < TPW; ++u)
+        for (int u = 0; u < TPW; ++u) {
+            const int t = wv * TPW + u;
+            f32x4 po = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) mma(pd.O[u], DB[kb], lfrag_rowk<OT, OT>(vM, 16 * (wv * TPW + u), 32 * kb));
+            for (int kb = 0; kb < NW; ++kb) mma(po, SB[kb], lfrag_rowk<OT, OT>(vQG, 16 * t, 32 * kb));
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) mma(po, DB[kb], lfrag_rowk<OT, OT>(vM, 16 * t, 32 * kb));
+            pd.O[u] = po;
+        }
     }
+    // S' = diag(exp gam_C) S + Kd^T Delta on this wave's rows
     {
         float g0[4], g1[4];
         lds_get4<float>(buf + B::GC + (32 * wv + 4 * lq) * 4, g0);
@@ -363,7 +329,9 @@ __device__ __forceinline__ void fwd_step(int c, const lds_char* buf, f32x4& S0, 
         S0 = a0;
         S1 = a1;
     }
-    put_block<OT>(xs, wv, S0, S1);  // every wave has read xs before barrier B
+    put_block<OT>(xw, wv, S0, S1);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) pd.D[u] = D[wv * TPW + u];
     pd.c = c;
 }
 
@@ -377,23 +345,18 @@ __device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, lds_char* 
     if (wv >= NW) {  // producer
         const Layout& L = a.L;
         const int pi = wv - NW;
-        auto G1 = [&](int n, lds_char* buf) {
+        auto G = [&](int n, lds_char* buf) {
             const long long cid = base + n;
             dma16<CH * DK * sizeof(OT)>(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM, pi);
-            if (OUT) dma16<CH * DK * sizeof(OT)>(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG, pi);
+            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_kd + cid * L.kd * sizeof(OT), buf + B::KD, pi);
+            if (OUT) {
+                dma16<CH * DK * sizeof(OT)>(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG, pi);
+                dma16<CH * CH * sizeof(OT)>(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M, pi);
+            }
             dma16<4 * 256 * sizeof(OT)>(a.ws + L.o_u + (cid * L.u + (size_t)j * 4 * 256) * sizeof(OT), buf + B::U,
                                         pi);
-        };
-        auto G2 = [&](int n, lds_char* buf) {
-            const long long cid = base + n;
-            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_kd + cid * L.kd * sizeof(OT), buf + B::KD, pi);
-            if (OUT) dma16<CH * CH * sizeof(OT)>(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M, pi);
             dma4<DK * 4>(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC, pi);
         };
-        constexpr int P1 = CH * DK * (int)sizeof(OT) / 1024;  // pieces of Wm and Qg
-        constexpr int PU = 4 * 256 * (int)sizeof(OT) / 1024;  // pieces of the U tiles
-        static_assert(P1 % NP == 0 && PU % NP == 0, "group 1 splits evenly over the producers");
-        constexpr int G1N = ((OUT ? 2 : 1) * P1 + PU) / NP;
         // prefetch regions: Wm, Kd, U (all slices), exp(gam_C) [, Qg, M]
         constexpr int LK = CH * DK * (int)sizeof(OT) / 128, LU = CH * DV * (int)sizeof(OT) / 128;
         constexpr int LM = CH * CH * (int)sizeof(OT) / 128, LG = DK * 4 / 128;
@@ -421,7 +384,7 @@ __device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, lds_char* 
             };
             prefetch_lines<LINES, NJ>(line, j, pi, pfslot);
         };
-        produce<DBUF, G1N, prefetch_count<LINES, NJ>()>(NT, b0, b1, G1, G2, PF);
+        produce<DBUF, prefetch_count<LINES, NJ>()>(NT, b0, b1, G, PF);
         return;
     }
     // compute waves: state rows 32 wv + 4 lq + i (S0) and 32 wv + 16 + 4 lq + i (S1),
@@ -435,25 +398,27 @@ __device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, lds_char* 
         S0[i] = a.h0 ? a.h0[r0 + (size_t)i * DV] : 0.f;
         S1[i] = a.h0 ? a.h0[r0 + (size_t)(16 + i) * DV] : 0.f;
     }
-    lds_char* xt = xs + NW * Xch<OT>::FRAG;
-    put_block<OT>(xs, wv, S0, S1);
+    lds_char* xs0 = xs;
+    lds_char* xs1 = xs + NW * Xch<OT>::FRAG;
+    put_block<OT>(xs0, wv, S0, S1);
     FwdPend<OT, NW> pd;
     pd.c = -1;
     if (DBUF) {
         for (int n = 0; n < NT; n += 2) {
             sync_lds();  // A_n
             fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
-            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n, b0, S0, S1, stage, xs, xt, pd);
+            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n, b0, S0, S1, stage, xs0, xs1, pd);
             if (n + 1 >= NT) break;
             sync_lds();  // A_{n+1}
             fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
-            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n + 1, b1, S0, S1, stage, xs, xt, pd);
+            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n + 1, b1, S0, S1, stage, xs1, xs0, pd);
         }
     } else {
         for (int n = 0; n < NT; ++n) {
             sync_lds();  // A_n
             fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
-            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n, b0, S0, S1, stage, xs, xt, pd);
+            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n, b0, S0, S1, stage, (n & 1) ? xs1 : xs0, (n & 1) ? xs0 : xs1,
+                                                 pd);
             sync_lds();  // C_n
         }
     }
@@ -493,13 +458,13 @@ __global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_fwd_chain(Args a) {
 template <class OT, int DK, int DV>
 struct BwdChainBuf {
     static constexpr int ES = sizeof(OT);
-    static constexpr int KD = 0;                  // group 1: Kd [64][DK] swizzled
-    static constexpr int M = KD + CH * DK * ES;   // group 1: M [64][64]
-    static constexpr int DO = M + CH * CH * ES;   // group 1: dO rows of this slice [64][16]
-    static constexpr int WM = DO + 64 * 16 * ES;  // group 2: Wm [64][DK]
-    static constexpr int QG = WM + CH * DK * ES;  // group 2: Qg [64][DK]
-    static constexpr int T = QG + CH * DK * ES;   // group 2: T [64][64]
-    static constexpr int GC = T + CH * CH * ES;   // group 2: exp(gam_C), DK floats
+    static constexpr int KD = 0;                  // Kd [64][DK] swizzled
+    static constexpr int M = KD + CH * DK * ES;   // M [64][64]
+    static constexpr int DO = M + CH * CH * ES;   // dO rows of this slice [64][16]
+    static constexpr int WM = DO + 64 * 16 * ES;  // Wm [64][DK]
+    static constexpr int QG = WM + CH * DK * ES;  // Qg [64][DK]
+    static constexpr int T = QG + CH * DK * ES;   // T [64][64]
+    static constexpr int GC = T + CH * CH * ES;   // exp(gam_C), DK floats
     static constexpr int BYTES = GC + DK * 4;
 };
 
@@ -524,11 +489,11 @@ __device__ __forceinline__ void bwd_flush(const Args& a, int s, int j, BwdPend<O
     for (int u = 0; u < TPW; ++u) store_tile<OT>(dy + (wv * TPW + u) * 256, pd.Y[u]);
 }
 
-// One chunk step of a compute wave; contains barrier B of the step. On entry the
-// gradient blocks of all waves are in xs; on exit this wave's new block is.
+// One chunk step of a compute wave. On entry the gradient blocks of all waves are in
+// xr; on exit this wave's new block is in xw (the other copy).
 template <class OT, int DK, int DV, int NW>
 __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0, f32x4& dS1, lds_char* stage,
-                                         lds_char* xs, lds_char* xt, BwdPend<OT, NW>& pd) {
+                                         const lds_char* xr, lds_char* xw, BwdPend<OT, NW>& pd) {
     using B = BwdChainBuf<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
     constexpr int TPW = BwdPend<OT, NW>::TPW;
@@ -536,30 +501,29 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0,
     const LSwz<OT, DK> vKD{buf + B::KD}, vQG{buf + B::QG}, vWM{buf + B::WM};
     const LSwz<OT, CH> vM{buf + B::M}, vT{buf + B::T};
     const LPad<OT> vDO{buf + B::DO, 16};
+    FT dSB[NW];
+#pragma unroll
+    for (int kb = 0; kb < NW; ++kb) dSB[kb] = get_block<OT>(xr, kb);
     stage_rows<OT>(stage, dS0, dS1, pd.st);  // gradient w.r.t. this chunk's end state
-    // phase 1 (group 1). B fragments of dO: K = token, N = this slice's 16 value channels
+    // B fragments of dO: K = token, N = this slice's 16 value channels
     FT dOB[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) dOB[kb] = lfrag_colk<OT, OT>(vDO, 0, 32 * kb);
-    FT dSB[NW];
+    // dDelta = M^T dO + Kd dS', all four token tiles
+    f32x4 dD[4];
 #pragma unroll
-    for (int kb = 0; kb < NW; ++kb) dSB[kb] = get_block<OT>(xs, kb);
-    // dDelta = M^T dO + Kd dS' on this wave's token tiles
+    for (int t = 0; t < 4; ++t) dD[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int t = wv * TPW + u;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < NW; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < NW; ++kb) mma(acc, lfrag_rowk<OT, OT>(vKD, 16 * t, 32 * kb), dSB[kb]);
+        for (int t = 0; t < 4; ++t) mma(dD[t], lfrag_rowk<OT, OT>(vKD, 16 * t, 32 * kb), dSB[kb]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vM, 16 * t, 32 * kb), dOB[kb]);
-        put_tile<OT>(xt, t, acc);
-    }
-    sync_lds();  // B
-    // phase 2 (group 2): dDelta as operands
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) mma(dD[t], lfrag_colk<OT, OT>(vM, 16 * t, 32 * kb), dOB[kb]);
     FT dDB[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) dDB[kb] = get_tiles<OT>(xt, kb);
+    for (int kb = 0; kb < 2; ++kb) dDB[kb] = frag_of<OT>(dD[2 * kb], dD[2 * kb + 1]);
     // dS = diag(exp gam_C) dS' + Qg^T dO - Wm^T dDelta on this wave's rows
     {
         float g0[4], g1[4];
@@ -578,6 +542,7 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0,
         dS0 = p0 - n0;
         dS1 = p1 - n1;
     }
+    put_block<OT>(xw, wv, dS0, dS1);
     // dY = T^T dDelta on this wave's token tiles (for the intra-chunk kernel)
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -587,7 +552,6 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0,
         for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vT, 16 * t, 32 * kb), dDB[kb]);
         pd.Y[u] = acc;
     }
-    put_block<OT>(xs, wv, dS0, dS1);  // every wave has read xs before barrier B
     pd.c = c;
 }
 
@@ -605,11 +569,15 @@ __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* 
         const int bidx = s / a.H, h = s % a.H;
         constexpr int EPL = 4 / sizeof(OT);           // dO elements per lane and instruction
         constexpr int RPI = 256 / (16 * sizeof(OT));  // dO rows per instruction
-        auto G1 = [&](int n, lds_char* buf) {
+        auto G = [&](int n, lds_char* buf) {
             const int c = last - n;
             const long long cid = base + c;
             dma16<CH * DK * sizeof(OT)>(a.ws + L.o_kd + cid * L.kd * sizeof(OT), buf + B::KD, pi);
             dma16<CH * CH * sizeof(OT)>(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M, pi);
+            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM, pi);
+            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG, pi);
+            dma16<CH * CH * sizeof(OT)>(a.ws + L.o_t + cid * L.t * sizeof(OT), buf + B::T, pi);
+            dma4<DK * 4>(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC, pi);
             // dO rows of this slice. Rows past the end of the sequence repeat its last row:
             // every product that reads dO (M^T dO, Qg^T dO) multiplies those rows by rows of
             // M and Qg that the intra-chunk kernel wrote as exact zeros.
@@ -623,17 +591,7 @@ __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* 
                 __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + B::DO + k * 256), 4, 0, 0);
             }
         };
-        auto G2 = [&](int n, lds_char* buf) {
-            const long long cid = base + (last - n);
-            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM, pi);
-            dma16<CH * DK * sizeof(OT)>(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG, pi);
-            dma16<CH * CH * sizeof(OT)>(a.ws + L.o_t + cid * L.t * sizeof(OT), buf + B::T, pi);
-            dma4<DK * 4>(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC, pi);
-        };
-        constexpr int PK = CH * DK * (int)sizeof(OT) / 1024, PM = CH * CH * (int)sizeof(OT) / 1024;
-        static_assert(PK % NP == 0 && PM % NP == 0 && (64 / RPI) % NP == 0,
-                      "group 1 splits evenly over the producers");
-        constexpr int G1N = (PK + PM + 64 / RPI) / NP;
+        static_assert((64 / RPI) % NP == 0, "the dO rows split evenly over the producers");
         // prefetch regions: Kd, Qg, Wm, M, T, exp(gam_C), dO rows (all slices)
         constexpr int LK = CH * DK * (int)sizeof(OT) / 128, LM = CH * CH * (int)sizeof(OT) / 128;
         constexpr int LG = DK * 4 / 128, LR = DV * (int)sizeof(OT) / 128;  // lines per dO row
@@ -667,7 +625,7 @@ __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* 
             };
             prefetch_lines<LINES, NJ>(line, j, pi, pfslot);
         };
-        produce<DBUF, G1N, prefetch_count<LINES, NJ>()>(NT, b0, b1, G1, G2, PF);
+        produce<DBUF, prefetch_count<LINES, NJ>()>(NT, b0, b1, G, PF);
         return;
     }
     const int l = lane_id(), li = l & 15, lq = l >> 4;
@@ -679,25 +637,26 @@ __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* 
         dS0[i] = a.dht ? a.dht[r0 + (size_t)i * DV] : 0.f;
         dS1[i] = a.dht ? a.dht[r0 + (size_t)(16 + i) * DV] : 0.f;
     }
-    lds_char* xt = xs + NW * Xch<OT>::FRAG;
-    put_block<OT>(xs, wv, dS0, dS1);
+    lds_char* xs0 = xs;
+    lds_char* xs1 = xs + NW * Xch<OT>::FRAG;
+    put_block<OT>(xs0, wv, dS0, dS1);
     BwdPend<OT, NW> pd;
     pd.c = -1;
     if (DBUF) {
         for (int n = 0; n < NT; n += 2) {
             sync_lds();  // A_n
             bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
-            bwd_step<OT, DK, DV, NW>(last - n, b0, dS0, dS1, stage, xs, xt, pd);
+            bwd_step<OT, DK, DV, NW>(last - n, b0, dS0, dS1, stage, xs0, xs1, pd);
             if (n + 1 >= NT) break;
             sync_lds();  // A_{n+1}
             bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
-            bwd_step<OT, DK, DV, NW>(last - n - 1, b1, dS0, dS1, stage, xs, xt, pd);
+            bwd_step<OT, DK, DV, NW>(last - n - 1, b1, dS0, dS1, stage, xs1, xs0, pd);
         }
     } else {
         for (int n = 0; n < NT; ++n) {
             sync_lds();  // A_n
             bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
-            bwd_step<OT, DK, DV, NW>(last - n, b0, dS0, dS1, stage, xs, xt, pd);
+            bwd_step<OT, DK, DV, NW>(last - n, b0, dS0, dS1, stage, (n & 1) ? xs1 : xs0, (n & 1) ? xs0 : xs1, pd);
             sync_lds();  // C_n
         }
     }
