@@ -194,7 +194,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         float gv[4][4], g0[4][4], ge[4][4];
         cvt_rows<OT>(rg[ac], nvalid, gv);
         gamma_scan(gv, gam[ac], g0, ge);
-        write_factors<DK>(sF, ch0, g0, ge);
+        RowExp rx;
+        row_exps<DK>(sF, ch0, g0, ge, rx);
     }
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
@@ -275,11 +276,15 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         for (int R = 0; R < 4; ++R)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                g0[R][i] = row_bcast(gam[ac][R][i], 0);
-                ge[R][i] = row_bcast(gam[ac][R][i], 15);
+                g0[R][i] = row_bcast<0>(gam[ac][R][i]);
+                ge[R][i] = row_bcast<15>(gam[ac][R][i]);
             }
+        const int ch0 = 16 * at + 4 * lq;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
+            float e0v[4], ecv[4];  // exp(gam_t0), exp(gam_C - gam_tend) of channels ch0 + i
+            lds_get4<float>(sF + ((F_ER0 + t) * DK + ch0) * 4, e0v);
+            lds_get4<float>(sF + ((F_ECE + t) * DK + ch0) * 4, ecv);
             f32x4 q4 = {0.f, 0.f, 0.f, 0.f}, b4 = q4, k4 = q4;
 #pragma unroll
             for (int kb = 0; kb < KV; ++kb) {
@@ -289,10 +294,9 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float e0 = __expf(g0[t][i]), ec = __expf(ge[3][i] - ge[t][i]);
-                Pq[ac][t][i] = e0 * q4[i];
-                Pb[ac][t][i] = -e0 * b4[i];
-                Pk[ac][t][i] = ec * k4[i];
+                Pq[ac][t][i] = e0v[i] * q4[i];
+                Pb[ac][t][i] = -e0v[i] * b4[i];
+                Pk[ac][t][i] = ecv[i] * k4[i];
             }
         }
         // sum over the chunk's tokens of dKd * Kd (Kd = k * exp(gam_C - gam)), per channel
@@ -335,14 +339,14 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         for (int R = 0; R < 4; ++R)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                g0[R][i] = row_bcast(gam[ac][R][i], 0);
-                ge[R][i] = row_bcast(gam[ac][R][i], 15);
+                g0[R][i] = row_bcast<0>(gam[ac][R][i]);
+                ge[R][i] = row_bcast<15>(gam[ac][R][i]);
             }
         float qv[4][4], kv[4][4], bv[4][4];
         cvt_rows<OT>(rq[ac], nvalid, qv);
         cvt_rows<OT>(rk[ac], nvalid, kv);
         cvt_rows<OT>(rb[ac], nvalid, bv);
-        scaled_factors_from<OT, DK>(qv, kv, bv, ch0, gam[ac], g0, ge, sXA, sXM, sY, nullptr, nullptr);
+        scaled_factors_from<OT, DK, false>(qv, kv, bv, ch0, gam[ac], g0, ge, sXA, sXM, sY, nullptr, nullptr, nullptr);
     }
     __syncthreads();
 
@@ -384,8 +388,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         for (int R = 0; R < 4; ++R)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                g0[R][i] = row_bcast(gam[ac][R][i], 0);
-                ge[R][i] = row_bcast(gam[ac][R][i], 15);
+                g0[R][i] = row_bcast<0>(gam[ac][R][i]);
+                ge[R][i] = row_bcast<15>(gam[ac][R][i]);
             }
         float qv[4][4], kv[4][4], bv[4][4];
         cvt_rows<OT>(rq[ac], nvalid, qv);
@@ -429,7 +433,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             for (int i = 0; i < 4; ++i) {
                 const float x = row_scan16(dgam[t][i]) + tot[i];
                 pre[t][i] = x;
-                tot[i] = row_bcast(x, 15);
+                tot[i] = row_bcast<15>(x);
             }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {

@@ -410,15 +410,16 @@ __device__ __forceinline__ float row_scan16(float x) {
     x += __int_as_float(v);
     return x;
 }
-// value held by lane (src_li, same lq) of the caller's 16-lane row
-__device__ __forceinline__ float row_bcast(float x, int src_li) {
-    const int l = lane_id();
-    return __shfl(x, (l & ~15) | src_li, 64);
+// value held by lane SRC of the caller's 16-lane row (DPP row_newbcast, a VALU move)
+template <int SRC>
+__device__ __forceinline__ float row_bcast(float x) {
+    static_assert(SRC >= 0 && SRC < 16, "a row has 16 lanes");
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + SRC, 0xF, 0xF, false));
 }
 // sum over the 16 lanes of a row (result in every lane of the row)
 __device__ __forceinline__ float row_sum16(float x) {
     float s = row_scan16(x);
-    return row_bcast(s, 15);
+    return row_bcast<15>(s);
 }
 
 }  // namespace gdr2

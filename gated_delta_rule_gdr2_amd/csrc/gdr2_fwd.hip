@@ -163,18 +163,14 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
                 float gv[4][4], gam[4][4], g0[4][4], ge[4][4];
                 cvt_rows16<OT>(rg[ai], hq, nvalid, gv);
                 gamma_scan(gv, gam, g0, ge);
-                write_factors<DK>(sF, ch0, g0, ge);
-                if (li == 0) {
-                    float gcv[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) gcv[i] = __expf(ge[3][i]);
-                    st4(gc_out + ch0, gcv);
-                }
+                RowExp rx;
+                row_exps<DK>(sF, ch0, g0, ge, rx);
+                if (li == 1) st4(gc_out + ch0, rx.x1);  // exp(gam_C)
                 float qv[4][4], kv[4][4], bv[4][4];
                 cvt_rows16<OT>(rq[ai], hq, nvalid, qv);
                 cvt_rows16<OT>(rk[ai], hq, nvalid, kv);
                 cvt_rows16<OT>(rb[ai], hq, nvalid, bv);
-                scaled_factors_from<OT, DK>(qv, kv, bv, ch0, gam, g0, ge, sXA, sXM, sY, qg_out, kd_out);
+                scaled_factors_from<OT, DK, true>(qv, kv, bv, ch0, gam, g0, ge, sXA, sXM, sY, qg_out, kd_out, &rx);
             }
         }
 #pragma unroll

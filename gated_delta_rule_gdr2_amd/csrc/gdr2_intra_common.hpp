@@ -31,18 +31,6 @@ constexpr int F_ROWS = 2 * NBLK + NPAIR;
 template <class OT>
 constexpr int pad_ot() { return sizeof(OT) == 2 ? 8 : 4; }
 
-// Load 4 consecutive elements of token row r (row stride rs) at column ch; rows at or
-// past nvalid (>= 1) read as zero. Branch-free: the address is clamped to a valid row
-// and the value selected afterwards, so independent loads can all be in flight at once.
-template <class IT>
-__device__ __forceinline__ void ld4_row(const IT* base, size_t rs, int r, int ch, int nvalid, float out[4]) {
-    const int rr = r < nvalid ? r : nvalid - 1;
-    ld4(base + (size_t)rr * rs + ch, out);
-    const bool ok = r < nvalid;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = ok ? out[i] : 0.f;
-}
-
 // Raw 4-element row pieces (Raw4, gdr2_device.hpp): loads are issued for a whole
 // phase before any of them is used, so a wave has all of its HBM requests in flight.
 
@@ -123,60 +111,105 @@ __device__ __forceinline__ void gamma_scan(const float (&gv)[4][4], float (&gam)
         for (int i = 0; i < 4; ++i) {
             const float x = row_scan16(gv[t][i]) + run[i];
             gam[t][i] = x;
-            run[i] = row_bcast(x, 15);
+            run[i] = row_bcast<15>(x);
         }
 #pragma unroll
     for (int R = 0; R < 4; ++R)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            g0[R][i] = row_bcast(gam[R][i], 0);
-            ge[R][i] = row_bcast(gam[R][i], 15);
+            g0[R][i] = row_bcast<0>(gam[R][i]);
+            ge[R][i] = row_bcast<15>(gam[R][i]);
         }
 }
-template <class OT>
-__device__ __forceinline__ void chunk_gamma(const OT* gb, size_t rs, int ch0, int nvalid, float (&gam)[4][4],
-                                            float (&g0)[4][4], float (&ge)[4][4]) {
-    const int li = lane_id() & 15;
-    float gv[4][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) ld4_row(gb, rs, 16 * t + li, ch0, nvalid, gv[t]);
-    gamma_scan(gv, gam, g0, ge);
+// Row-uniform exponentials of four channels ch0..ch0+3. They are the same in all 16
+// lanes of a row, so each lane computes a different one: lane li holds, for channel
+// ch0 + i,
+//   x0[i]: li < 10          s(R, I) = exp(gam_R0 - gam_Iend), (R, I) = pair_ri(li)
+//          li = 10 .. 13    exp(gam_R0), R = li - 10
+//          li = 14, 15      exp(gam_C - gam_Rend), R = li - 14
+//   x1[i]: li = 0           exp(gam_C - gam_2end)
+//          li = 1           exp(gam_C)
+//          li = 2           exp(gam_C - gam_3end) = 1
+// (gam_C = gam at the chunk's last row = gam_3end.) row_bcast moves them to the
+// lanes that use them.
+struct RowExp {
+    float x0[4], x1[4];
+};
+static_assert(NPAIR + NBLK + 2 == 16, "the row-uniform exponentials fill one 16-lane row");
+
+// broadcast of lane `src` of the row; src must fold to a constant after unrolling
+__device__ __forceinline__ float row_bcast_c(float x, int src) {
+    switch (src) {
+        case 0: return row_bcast<0>(x);
+        case 1: return row_bcast<1>(x);
+        case 2: return row_bcast<2>(x);
+        case 3: return row_bcast<3>(x);
+        case 4: return row_bcast<4>(x);
+        case 5: return row_bcast<5>(x);
+        case 6: return row_bcast<6>(x);
+        case 7: return row_bcast<7>(x);
+        case 8: return row_bcast<8>(x);
+        case 9: return row_bcast<9>(x);
+        case 10: return row_bcast<10>(x);
+        case 11: return row_bcast<11>(x);
+        case 12: return row_bcast<12>(x);
+        case 13: return row_bcast<13>(x);
+        case 14: return row_bcast<14>(x);
+        default: return row_bcast<15>(x);
+    }
+}
+// exp(gam_R0) and exp(gam_C - gam_Rend) of channel ch0 + i in every lane (R, i constants)
+__device__ __forceinline__ float rx_er0(const RowExp& x, int R, int i) { return row_bcast_c(x.x0[i], NPAIR + R); }
+__device__ __forceinline__ float rx_ece(const RowExp& x, int R, int i) {
+    if (R < 2) return row_bcast_c(x.x0[i], NPAIR + NBLK + R);
+    if (R == 2) return row_bcast<0>(x.x1[i]);
+    return 1.f;
 }
 
-// Factor arrays for the four channels ch0..ch0+3 (written by the li == 0 lanes).
+// Computes the row-uniform exponentials and writes the factor arrays of channels
+// ch0..ch0+3 (eR0, eCe and s rows of sF).
 template <int DK>
-__device__ __forceinline__ void write_factors(lds_char* sF, int ch0, const float (&g0)[4][4],
-                                              const float (&ge)[4][4]) {
-    if ((lane_id() & 15) != 0) return;
+__device__ __forceinline__ void row_exps(lds_char* sF, int ch0, const float (&g0)[4][4], const float (&ge)[4][4],
+                                         RowExp& x) {
+    const int li = lane_id() & 15;
+    // lane li's value is exp(A - B): ra = 0..3 -> A = gam_{ra,0}, 4 -> A = gam_C;
+    // ib = 0..3 -> B = gam_{ib,end}, 4 -> B = 0
+    // (all selects, no branches: pair_ri written out for li < NPAIR)
+    const int pr = li >= 6 ? 3 : li >= 3 ? 2 : li >= 1 ? 1 : 0, pi = li - pr * (pr + 1) / 2;
+    const int ra = li < NPAIR ? pr : li < NPAIR + NBLK ? li - NPAIR : 4;
+    const int ib = li < NPAIR ? pi : li < NPAIR + NBLK ? 4 : li - NPAIR - NBLK;
+    const bool a0 = ra == 0, a1 = ra == 1, a2 = ra == 2, a3 = ra == 3;
+    const bool b0 = ib == 0, b1 = ib == 1, b2 = ib == 2, b3 = ib == 3;
 #pragma unroll
-    for (int R = 0; R < 4; ++R) {
-        float e0[4], ec[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            e0[i] = __expf(g0[R][i]);
-            ec[i] = __expf(ge[3][i] - ge[R][i]);
-        }
-        lds_put4<float>(sF + ((F_ER0 + R) * DK + ch0) * 4, e0);
-        lds_put4<float>(sF + ((F_ECE + R) * DK + ch0) * 4, ec);
-#pragma unroll
-        for (int I = 0; I <= R; ++I) {
-            float sv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sv[i] = __expf(g0[R][i] - ge[I][i]);
-            lds_put4<float>(sF + ((F_S + pair_id(R, I)) * DK + ch0) * 4, sv);
-        }
+    for (int i = 0; i < 4; ++i) {
+        float A = ge[3][i], B = 0.f;
+        A = a3 ? g0[3][i] : A;
+        A = a2 ? g0[2][i] : A;
+        A = a1 ? g0[1][i] : A;
+        A = a0 ? g0[0][i] : A;
+        B = b3 ? ge[3][i] : B;
+        B = b2 ? ge[2][i] : B;
+        B = b1 ? ge[1][i] : B;
+        B = b0 ? ge[0][i] : B;
+        x.x0[i] = __expf(A - B);
+        const float B1 = li == 0 ? ge[2][i] : li == 2 ? ge[3][i] : 0.f;
+        x.x1[i] = __expf(ge[3][i] - B1);
     }
+    const int row = li < NPAIR ? F_S + li : li < NPAIR + NBLK ? F_ER0 + (li - NPAIR) : F_ECE + (li - NPAIR - NBLK);
+    lds_put4<float>(sF + (row * DK + ch0) * 4, x.x0);
+    if (li == 0 || li == 2) lds_put4<float>(sF + ((F_ECE + 2 + li / 2) * DK + ch0) * 4, x.x1);
 }
 
 // XA = b*k*E1, XM = q*E1, Y = k*E2 for channel tile rows of this lane, into swizzled LDS
-// tiles [CH][DK]; optionally also Qg = q*exp(gam) and Kd = k*exp(gam_C - gam) as swizzled
-// tiles in global memory.
-template <class OT, int DK>
+// tiles [CH][DK]; with OUTS also Qg = q*exp(gam) and Kd = k*exp(gam_C - gam) as swizzled
+// tiles in global memory (exp(gam) = E1 * exp(gam_R0), exp(gam_C - gam) = E2 *
+// exp(gam_C - gam_Rend), the row-uniform factors taken from rx).
+template <class OT, int DK, bool OUTS>
 __device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], const float (&kv)[4][4],
                                                     const float (&bv)[4][4], int ch0, const float (&gam)[4][4],
                                                     const float (&g0)[4][4], const float (&ge)[4][4],
                                                     lds_char* sXA, lds_char* sXM, lds_char* sY, OT* qg_out,
-                                                    OT* kd_out) {
+                                                    OT* kd_out, const RowExp* rx) {
     const int li = lane_id() & 15;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -189,31 +222,20 @@ __device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], con
             xa[i] = bv[t][i] * kv[t][i] * e1;
             xm[i] = qv[t][i] * e1;
             y[i] = kv[t][i] * e2;
-            qg[i] = xm[i] * __expf(g0[t][i]);
-            kd[i] = y[i] * __expf(ge[3][i] - ge[t][i]);
+            if constexpr (OUTS) {
+                qg[i] = xm[i] * rx_er0(*rx, t, i);
+                kd[i] = y[i] * rx_ece(*rx, t, i);
+            }
         }
         const int o = swz<OT, DK>(r, ch0) * (int)sizeof(OT);
         lds_put4<OT>(sXA + o, xa);
         lds_put4<OT>(sXM + o, xm);
         lds_put4<OT>(sY + o, y);
-        if (qg_out) st4(qg_out + swz<OT, DK>(r, ch0), qg);
-        if (kd_out) st4(kd_out + swz<OT, DK>(r, ch0), kd);
+        if constexpr (OUTS) {
+            st4(qg_out + swz<OT, DK>(r, ch0), qg);
+            st4(kd_out + swz<OT, DK>(r, ch0), kd);
+        }
     }
-}
-template <class OT, int DK>
-__device__ __forceinline__ void scaled_factors(const OT* qb, const OT* kb, const OT* bb, size_t rs, int ch0,
-                                               int nvalid, const float (&gam)[4][4], const float (&g0)[4][4],
-                                               const float (&ge)[4][4], lds_char* sXA, lds_char* sXM,
-                                               lds_char* sY, OT* qg_out, OT* kd_out) {
-    const int li = lane_id() & 15;
-    float qv[4][4], kv[4][4], bv[4][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        ld4_row(qb, rs, 16 * t + li, ch0, nvalid, qv[t]);
-        ld4_row(kb, rs, 16 * t + li, ch0, nvalid, kv[t]);
-        ld4_row(bb, rs, 16 * t + li, ch0, nvalid, bv[t]);
-    }
-    scaled_factors_from<OT, DK>(qv, kv, bv, ch0, gam, g0, ge, sXA, sXM, sY, qg_out, kd_out);
 }
 
 // X = w * v into a swizzled LDS tile [CH][DV] at columns ch0 .. ch0 + 3
@@ -229,25 +251,4 @@ __device__ __forceinline__ void x_tile_from(const float (&vv)[4][4], const float
         lds_put4<OT>(sX + swz<OT, DV>(16 * t + li, ch0) * (int)sizeof(OT), x);
     }
 }
-// X = w * v into a swizzled LDS tile [CH][DV] for value-channel tile jt
-template <class OT, int DV>
-__device__ __forceinline__ void chunk_x_tile(const OT* vb, const OT* wb, size_t rs, int jt, int nvalid,
-                                             lds_char* sX) {
-    const int l = lane_id(), li = l & 15, lq = l >> 4;
-    const int ch0 = 16 * jt + 4 * lq;
-    float vv[4][4], ww[4][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        ld4_row(vb, rs, 16 * t + li, ch0, nvalid, vv[t]);
-        ld4_row(wb, rs, 16 * t + li, ch0, nvalid, ww[t]);
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        float x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = vv[t][i] * ww[t][i];
-        lds_put4<OT>(sX + swz<OT, DV>(16 * t + li, ch0) * (int)sizeof(OT), x);
-    }
-}
-
 }  // namespace gdr2
