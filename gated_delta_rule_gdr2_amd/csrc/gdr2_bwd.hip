@@ -42,7 +42,11 @@ struct BwdLds {  // all matrices are swizzled tiles (see swz())
     static constexpr int DM = DA + CH * CH * ES;
     static constexpr int F = DM + CH * CH * ES;
     static constexpr int DMD = F + F_ROWS * DK * 4;  // diagonal of dM, fp32
-    static constexpr int BYTES = DMD + CH * 4;
+    static constexpr int G = DMD + CH * 4;           // g, q, k, b of the chunk [CH][DK]
+    static constexpr int Q = G + KMAT;
+    static constexpr int K = Q + KMAT;
+    static constexpr int B = K + KMAT;
+    static constexpr int BYTES = B + KMAT;
 };
 
 // tile dump [DV/16][4][64 lanes][4] -> swizzled LDS tile [CH][DV], in two steps so the
@@ -133,38 +137,40 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     const size_t rowk0 = ((size_t)bidx * a.T + t0) * a.H + h;
     const size_t rsk = (size_t)a.H * DK, rsv = (size_t)a.H * DV;
     const Layout& L = a.L;
-    const OT* qb = (const OT*)a.q + rowk0 * DK;
-    const OT* kb_ = (const OT*)a.k + rowk0 * DK;
-    const OT* bb = (const OT*)a.b + rowk0 * DK;
 
-    // ---- loads: every global input of the chunk this wave needs, issued up front.
-    // Wave wv owns key-channel tiles wv + NW ac and value-channel tiles wv + NW ji.
+    // ---- loads, all issued up front. The row tensors g, q, k, b and dO go to LDS by DMA
+    // in whole rows (dma_rows); v and w come to registers as 16-byte row pieces, lane
+    // t covering chunk t % NCV of row t / NCV of the chunk (pieces t, t + NTHR, ...);
+    // the saved states as MFMA fragments and the Delta / dY tile dumps as 4-element
+    // pieces. Wave wv owns key-channel tiles wv + NW ac.
     using RT = typename Raw4<OT>::type;
     using UD = Undump<OT, DV, NTHR>;
+    lds_char* sG = smem + LS::G;
+    lds_char* sQ = smem + LS::Q;
+    lds_char* sK = smem + LS::K;
+    lds_char* sB = smem + LS::B;
     const OT* Sg = (const OT*)(a.ws + L.o_s) + cid * L.s;
     const OT* dSg = (const OT*)(a.ws + L.o_ds) + cid * L.ds;
-    // value-side inputs (dO, v, w) are read 16 bytes per lane: piece p = wv + NW i covers
-    // row tile p % 4 and the GV = 4 WV channel group p / 4 (lane: WV channels)
-    constexpr int WV = 16 / (int)sizeof(OT), GV = 4 * WV, NPV = 4 * (DV / GV);
-    constexpr int NPW = (NPV + NW - 1) / NW;
+    dma_rows<OT, DK, NW>((const OT*)a.g + rowk0 * DK, rsk, nvalid, sG, wv);
+    dma_rows<OT, DK, NW>((const OT*)a.q + rowk0 * DK, rsk, nvalid, sQ, wv);
+    dma_rows<OT, DK, NW>((const OT*)a.k + rowk0 * DK, rsk, nvalid, sK, wv);
+    dma_rows<OT, DK, NW>((const OT*)a.b + rowk0 * DK, rsk, nvalid, sB, wv);
+    dma_rows<OT, DV, NW>((const OT*)a.dout + rowk0 * DV, rsv, nvalid, sDO, wv);
+    constexpr int WV = 16 / (int)sizeof(OT), NCV = DV / WV;  // elements per piece, pieces per row
+    constexpr int NPW = CH * NCV / NTHR;                     // v / w pieces per thread
+    static_assert(CH * NCV % NTHR == 0, "the value rows split evenly over the threads");
     using RW = typename Raw16<OT>::type;
-    RT rg[CPW][4], rq[CPW][4], rk[CPW][4], rb[CPW][4];
-    RW rdo[NPW], rv[NPW], rw[NPW];
+    RW rv[NPW], rw[NPW];
     RT rdl[UD::NU], rdy[UD::NU];
     // the saved-state fragments are fetched up front too, except for fp32 operands,
     // where they would not fit in registers next to the rest
     constexpr bool EARLY_S = sizeof(OT) == 2;
     FT Sf[CPW][KV], dSf[CPW][KV];
+    if (EARLY_S) {
 #pragma unroll
-    for (int ac = 0; ac < CPW; ++ac) {
-        const int at = wv + NW * ac;
-        if (at >= DK / 16) break;
-        const int ch0 = 16 * at + 4 * lq;
-        ld_rows((const OT*)a.g + rowk0 * DK, rsk, ch0, nvalid, rg[ac]);
-        ld_rows(qb, rsk, ch0, nvalid, rq[ac]);
-        ld_rows(kb_, rsk, ch0, nvalid, rk[ac]);
-        ld_rows(bb, rsk, ch0, nvalid, rb[ac]);
-        if (EARLY_S) {
+        for (int ac = 0; ac < CPW; ++ac) {
+            const int at = wv + NW * ac;
+            if (at >= DK / 16) break;
 #pragma unroll
             for (int kb = 0; kb < KV; ++kb) {
                 Sf[ac][kb] = frag_rowk8<OT>(Sg, DV, 16 * at, 32 * kb);
@@ -174,37 +180,42 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     }
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
-        const int pc = wv + NW * i;
-        if (pc >= NPV) break;
-        const int r = 16 * (pc & 3) + li, rr = r < nvalid ? r : nvalid - 1;
-        const size_t off = (rowk0 + (size_t)rr * a.H) * DV + GV * (pc >> 2) + WV * lq;
-        rdo[i] = *(const RW*)((const OT*)a.dout + off);
+        const int pc = tid + NTHR * i, r = pc / NCV, rr = r < nvalid ? r : nvalid - 1;
+        const size_t off = (rowk0 + (size_t)rr * a.H) * DV + WV * (pc % NCV);
         rv[i] = *(const RW*)((const OT*)a.v + off);
         rw[i] = *(const RW*)((const OT*)a.w + off);
     }
     undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_delta) + cid * L.delta, rdl);
     undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_dy) + cid * L.dy, rdy);
 
-    // ---- phase 1: cumulative decay and factors; dO, Delta, dY into LDS
+    // the staged rows have landed: zero the padding rows of a partial chunk
+    wait_vm<0>();
+    if (nvalid < CH) {
+        zero_tail_rows<OT, DK, NTHR>(sG, nvalid);
+        zero_tail_rows<OT, DK, NTHR>(sQ, nvalid);
+        zero_tail_rows<OT, DK, NTHR>(sK, nvalid);
+        zero_tail_rows<OT, DK, NTHR>(sB, nvalid);
+        zero_tail_rows<OT, DV, NTHR>(sDO, nvalid);
+    }
+    __syncthreads();
+    // this lane's 4-channel pieces (rows 16 t + li, channels ch0 .. ch0 + 3) of a staged tile
+    const LSwz<OT, DK> vG{sG}, vQ{sQ}, vK{sK}, vB{sB};
+    auto rows4 = [&](const LSwz<OT, DK>& v, int ch0, float (&out)[4][4]) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) lds_get4<OT>(v.p + v.off(16 * t + li, ch0), out[t]);
+    };
+
+    // ---- phase 1: cumulative decay and factors; Delta, dY into LDS
     float gam[CPW][4][4];
 #pragma unroll
     for (int ac = 0; ac < CPW; ++ac) {
         if (wv + NW * ac >= DK / 16) break;
         const int ch0 = 16 * (wv + NW * ac) + 4 * lq;
         float gv[4][4], g0[4][4], ge[4][4];
-        cvt_rows<OT>(rg[ac], nvalid, gv);
+        rows4(vG, ch0, gv);
         gamma_scan(gv, gam[ac], g0, ge);
         RowExp rx;
         row_exps<DK>(sF, ch0, g0, ge, rx);
-    }
-#pragma unroll
-    for (int i = 0; i < NPW; ++i) {
-        const int pc = wv + NW * i;
-        if (pc >= NPV) break;
-        const int r = 16 * (pc & 3) + li;
-        RW x = rdo[i];
-        if (r >= nvalid) x = RW{};
-        lds_store<RW>(sDO + swz<OT, DV>(r, GV * (pc >> 2) + WV * lq) * (int)sizeof(OT), x);
     }
     undump_store<OT, DV, NTHR>(rdl, sDL);
     undump_store<OT, DV, NTHR>(rdy, sDY);
@@ -301,7 +312,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         }
         // sum over the chunk's tokens of dKd * Kd (Kd = k * exp(gam_C - gam)), per channel
         float kx[4] = {0.f, 0.f, 0.f, 0.f}, kv[4][4];
-        cvt_rows<OT>(rk[ac], nvalid, kv);
+        rows4(vK, ch0, kv);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -309,12 +320,10 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) kdx[ac][i] = row_sum16(kx[i]);
     }
-    // dv = dY * w, dw = dY * v, 16 bytes per lane
+    // dv = dY * w, dw = dY * v, in the row-piece layout of v and w
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
-        const int pc = wv + NW * i;
-        if (pc >= NPV) break;
-        const int r = 16 * (pc & 3) + li, ch = GV * (pc >> 2) + WV * lq;
+        const int pc = tid + NTHR * i, r = pc / NCV, ch = WV * (pc % NCV);
         const RW dy = lds_load<RW>(sDY + swz<OT, DV>(r, ch) * (int)sizeof(OT));
         RW dvv, dww;
 #pragma unroll
@@ -343,9 +352,9 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
                 ge[R][i] = row_bcast<15>(gam[ac][R][i]);
             }
         float qv[4][4], kv[4][4], bv[4][4];
-        cvt_rows<OT>(rq[ac], nvalid, qv);
-        cvt_rows<OT>(rk[ac], nvalid, kv);
-        cvt_rows<OT>(rb[ac], nvalid, bv);
+        rows4(vQ, ch0, qv);
+        rows4(vK, ch0, kv);
+        rows4(vB, ch0, bv);
         scaled_factors_from<OT, DK, false>(qv, kv, bv, ch0, gam[ac], g0, ge, sXA, sXM, sY, nullptr, nullptr, nullptr);
     }
     __syncthreads();
@@ -392,9 +401,9 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
                 ge[R][i] = row_bcast<15>(gam[ac][R][i]);
             }
         float qv[4][4], kv[4][4], bv[4][4];
-        cvt_rows<OT>(rq[ac], nvalid, qv);
-        cvt_rows<OT>(rk[ac], nvalid, kv);
-        cvt_rows<OT>(rb[ac], nvalid, bv);
+        rows4(vQ, ch0, qv);
+        rows4(vK, ch0, kv);
+        rows4(vB, ch0, bv);
         float dgam[4][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {

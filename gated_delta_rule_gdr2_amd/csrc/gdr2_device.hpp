@@ -46,6 +46,13 @@ template <> struct Raw4<float> { typedef f32x4 type; };
 __device__ __forceinline__ int kmap(int lq, int e) { return 16 * (e >> 2) + 4 * lq + (e & 3); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // pair index -> (R, I), I <= R, in the order (0,0),(1,0),(1,1),(2,0),...
 __device__ __forceinline__ void pair_ri(int p, int& R, int& I) {
     R = (p >= 6) ? 3 : (p >= 3) ? 2 : (p >= 1) ? 1 : 0;
@@ -221,12 +228,15 @@ __device__ __forceinline__ void lds_store(lds_char* p, const T& v) {
 // banks): f(r) = 2*(r/2 mod 4) + (r/8 mod 2).
 // A tile is therefore copied into LDS verbatim by DMA and read back conflict-free.
 template <class OT, int RL>
+__device__ __forceinline__ int swz_f(int r) {  // chunk permutation of row r
+    constexpr int NCH = RL * (int)sizeof(OT) / 16;  // chunks per row
+    static_assert(NCH == 8 || NCH == 16, "swizzled tiles have 8 or 16 chunks per row");
+    return NCH == 16 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+template <class OT, int RL>
 __device__ __forceinline__ int swz(int r, int c) {
     constexpr int EPC = 16 / (int)sizeof(OT);  // elements per 16-byte chunk
-    constexpr int NCH = RL / EPC;              // chunks per row
-    static_assert(NCH == 8 || NCH == 16, "swizzled tiles have 8 or 16 chunks per row");
-    const int f = NCH == 16 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
-    return r * RL + (((c / EPC) ^ f) * EPC) + (c % EPC);
+    return r * RL + (((c / EPC) ^ swz_f<OT, RL>(r)) * EPC) + (c % EPC);
 }
 
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group the

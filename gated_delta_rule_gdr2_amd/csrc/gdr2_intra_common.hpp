@@ -251,4 +251,38 @@ __device__ __forceinline__ void x_tile_from(const float (&vv)[4][4], const float
         lds_put4<OT>(sX + swz<OT, DV>(16 * t + li, ch0) * (int)sizeof(OT), x);
     }
 }
+// Row tensors staged through LDS. A chunk's CH rows of a row-major tensor [.][RL]
+// (row stride rs elements) are copied into a swizzled LDS tile [CH][RL] by
+// asynchronous global->LDS DMA, 16 bytes per lane. One instruction fills 1 KB of the
+// tile, i.e. whole rows (4 of 256 bytes or 8 of 128 bytes), so every request is a whole
+// cache line; the lane that fills position p of row r fetches chunk p ^ f(r) of the row
+// (the swizzle only permutes chunks within a row). Rows at or past nvalid are fetched
+// from row nvalid - 1 and zeroed by zero_tail_rows once the copy has landed.
+// Instructions n = w, w + NW, ... belong to wave w.
+template <class OT, int RL, int NW>
+__device__ __forceinline__ void dma_rows(const OT* base, size_t rs, int nvalid, lds_char* tile, int wv) {
+    constexpr int EPC = 16 / (int)sizeof(OT);
+    constexpr int NCH = RL / EPC;  // 16-byte chunks per row
+    constexpr int RPI = 64 / NCH;  // rows per instruction
+    constexpr int NI = CH / RPI;   // instructions per tile
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < (NI + NW - 1) / NW; ++i) {
+        const int n = wv + NW * i;
+        if (NI % NW == 0 || n < NI) {
+            const int row = n * RPI + l / NCH, pos = l % NCH;
+            const int c = pos ^ swz_f<OT, RL>(row);
+            const int rr = row < nvalid ? row : nvalid - 1;
+            const char* src = (const char*)(base + (size_t)rr * rs + c * EPC);
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + n * 1024), 16, 0, 0);
+        }
+    }
+}
+// zero rows nvalid .. CH - 1 of a swizzled tile [CH][RL] (all threads of the workgroup)
+template <class OT, int RL, int NTHR>
+__device__ __forceinline__ void zero_tail_rows(lds_char* tile, int nvalid) {
+    constexpr int NCH = RL * (int)sizeof(OT) / 16;
+    for (int u = nvalid * NCH + (int)threadIdx.x; u < CH * NCH; u += NTHR) lds_store<f32x4>(tile + u * 16, f32x4{});
+}
+
 }  // namespace gdr2
