@@ -21,7 +21,7 @@
 //   k_bwd_chain : (gdr2_chain.hip) one workgroup per (sequence, 16-column value
 //                 slice), chunks in reverse; the state gradient's key rows split
 //                 over the compute waves, held in accumulator registers; writes
-//                 dS' (row-major) and dY (tiles) per chunk.
+//                 dS' (fragment-major) and dY (tiles) per chunk.
 //   k_bwd_intra : one workgroup per chunk, fully parallel; reads the saved S,
 //                 Delta, dS', dY and the inputs, writes dq, dk, dv, dg, db, dw.
 #include "gdr2_intra_common.hpp"
@@ -173,8 +173,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             if (at >= DK / 16) break;
 #pragma unroll
             for (int kb = 0; kb < KV; ++kb) {
-                Sf[ac][kb] = frag_rowk8<OT>(Sg, DV, 16 * at, 32 * kb);
-                dSf[ac][kb] = frag_rowk8<OT>(dSg, DV, 16 * at, 32 * kb);
+                Sf[ac][kb] = frag_fmaj<OT, DV>(Sg, at, kb);
+                dSf[ac][kb] = frag_fmaj<OT, DV>(dSg, at, kb);
             }
         }
     }
@@ -270,8 +270,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         if (!EARLY_S) {
 #pragma unroll
             for (int kb = 0; kb < KV; ++kb) {
-                Sf[ac][kb] = frag_rowk8<OT>(Sg, DV, 16 * at, 32 * kb);
-                dSf[ac][kb] = frag_rowk8<OT>(dSg, DV, 16 * at, 32 * kb);
+                Sf[ac][kb] = frag_fmaj<OT, DV>(Sg, at, kb);
+                dSf[ac][kb] = frag_fmaj<OT, DV>(dSg, at, kb);
             }
         }
         float pr = 0.f;
@@ -420,12 +420,11 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
                 dk[i] = gbk * bv[t][i] + e2 * Pk[ac][t][i] + dmd * qv[t][i];
                 dgam[t][i] = qv[t][i] * dq[i] + 2.f * bv[t][i] * db[i] - kv[t][i] * dk[i];
             }
-            if (r < nvalid) {
-                const size_t off = (size_t)r * rsk + ch0;
-                st4((OT*)a.dq + rowk0 * DK + off, dq);
-                st4((OT*)a.dk + rowk0 * DK + off, dk);
-                st4((OT*)a.db + rowk0 * DK + off, db);
-            }
+            // into the staged q, k, b tiles (this wave alone reads and writes these columns)
+            const int o = vQ.off(r, ch0);
+            lds_put4<OT>(sQ + o, dq);
+            lds_put4<OT>(sK + o, dk);
+            lds_put4<OT>(sB + o, db);
         }
         // scaling of the carried state at the chunk's last row: sum_r dKd*Kd + exp(gam_C) rowsum(dS'*S)
 #pragma unroll
@@ -446,15 +445,19 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int r = 16 * t + li;
-            if (r < nvalid) {
-                float dg[4];
+            float dg[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dg[i] = tot[i] - pre[t][i] + dgam[t][i];
-                st4((OT*)a.dg + rowk0 * DK + (size_t)r * rsk + ch0, dg);
-            }
+            for (int i = 0; i < 4; ++i) dg[i] = tot[i] - pre[t][i] + dgam[t][i];
+            lds_put4<OT>(sG + vG.off(16 * t + li, ch0), dg);
         }
     }
+    __syncthreads();
+
+    // ---- dq, dk, db, dg out of the staged tiles in whole rows
+    store_rows_tiles<OT, DK, NTHR>(sQ, (OT*)a.dq + rowk0 * DK, rsk, nvalid);
+    store_rows_tiles<OT, DK, NTHR>(sK, (OT*)a.dk + rowk0 * DK, rsk, nvalid);
+    store_rows_tiles<OT, DK, NTHR>(sB, (OT*)a.db + rowk0 * DK, rsk, nvalid);
+    store_rows_tiles<OT, DK, NTHR>(sG, (OT*)a.dg + rowk0 * DK, rsk, nvalid);
 }
 
 size_t bwd_intra_lds_bytes(int DK, int DV, int esz) {

@@ -90,8 +90,8 @@ __device__ __forceinline__ void chain_map(int gid, int NS, int NJ, int& s, int& 
     }
 }
 
-// Row-major [DK][DV] store of one wave's 32 state rows of a 16-column slice,
-// transposed through LDS so each lane stores whole 16-byte row pieces.
+// Store of one wave's 32 state rows of a 16-column slice, transposed through LDS so
+// each lane stores whole 16-byte row pieces.
 template <class OT>
 struct RowStore {
     static constexpr int LDSP = 16 + 16 / (int)sizeof(OT);             // staging pitch, rows 16-B aligned
@@ -120,6 +120,8 @@ __device__ __forceinline__ void stage_rows(lds_char* stage, const f32x4& s0, con
         pend[k] = lds_load<f32x4>(stage + (row * R::LDSP + col) * (int)sizeof(OT));
     }
 }
+// ... into a [DK][DV] state in fragment-major layout (fmaj_off), where each piece is
+// contiguous and a wave's pieces form whole 512-byte runs
 template <class OT, int DV>
 __device__ __forceinline__ void store_rows(OT* dst, int row0, int j, const f32x4 (&pend)[RowStore<OT>::PER_LANE]) {
     using R = RowStore<OT>;
@@ -127,7 +129,7 @@ __device__ __forceinline__ void store_rows(OT* dst, int row0, int j, const f32x4
 #pragma unroll
     for (int k = 0; k < R::PER_LANE; ++k) {
         const int p = l + 64 * k, row = p / R::PPR, col = (p % R::PPR) * R::EPP;
-        *(f32x4*)(dst + (size_t)(row0 + row) * DV + 16 * j + col) = pend[k];
+        *(f32x4*)(dst + fmaj_off<DV>(row0 + row, 16 * j + col)) = pend[k];
     }
 }
 
@@ -275,7 +277,7 @@ __device__ __forceinline__ void fwd_step(int c, const lds_char* buf, f32x4& S0, 
     FT SB[NW];
 #pragma unroll
     for (int kb = 0; kb < NW; ++kb) SB[kb] = get_block<OT>(xr, kb);
-    if (TRAIN) stage_rows<OT>(stage, S0, S1, pd.st);  // chunk start state -> pending row-major store
+    if (TRAIN) stage_rows<OT>(stage, S0, S1, pd.st);  // chunk start state -> pending store
     // Delta = U - Wm S, all four token tiles
     f32x4 D[4];
 #pragma unroll

@@ -133,6 +133,25 @@ __device__ __forceinline__ typename Frag<OT>::type frag_rowk(const OT* X, int ld
         return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 }
+// Fragment-major layout of a matrix with DV columns (rows a multiple of 16): its rowk8
+// fragments (below) one after another. Fragment (at, kb) -- rows 16 at .. + 15, columns
+// 32 kb .. + 31 -- is a block of 64 lanes x 8 elements, lane 16 lq + li holding row
+// 16 at + li, columns 32 kb + 8 lq .. + 7, so a wave reads a fragment as one contiguous
+// block (one 16-byte load per lane for bf16).
+template <int DV>
+__device__ __forceinline__ size_t fmaj_off(int r, int c) {
+    return ((size_t)((r >> 4) * (DV / 32) + (c >> 5)) * 64 + ((c >> 3) & 3) * 16 + (r & 15)) * 8 + (c & 7);
+}
+template <class OT, int DV>
+__device__ __forceinline__ typename Frag<OT>::type frag_fmaj(const OT* X, int at, int kb) {
+    const OT* p = X + ((size_t)(at * (DV / 32) + kb) * 64 + lane_id()) * 8;
+    if constexpr (sizeof(OT) == 2) {
+        return *(const bf16x8*)p;
+    } else {
+        f32x4 x0 = *(const f32x4*)p, x1 = *(const f32x4*)(p + 4);
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
 // "rowk8": the contiguous K-slot map k = k0 + 8*lq + e. Usable for a product only when
 // both operands are read from memory with it (never with an accumulator-derived
 // operand): lane (li, lq) reads X[row0 + li][k0 + 8*lq .. + 7], one 16-byte piece for

@@ -278,6 +278,22 @@ __device__ __forceinline__ void dma_rows(const OT* base, size_t rs, int nvalid, 
         }
     }
 }
+// Rows 0 .. nvalid - 1 of a swizzled LDS tile [CH][RL] out to a row-major tensor (row
+// stride rs elements), 16 bytes per lane with consecutive lanes on consecutive chunks
+// of a row, so every request is a whole cache line (all threads of the workgroup).
+template <class OT, int RL, int NTHR>
+__device__ __forceinline__ void store_rows_tiles(const lds_char* tile, OT* dst, size_t rs, int nvalid) {
+    constexpr int EPC = 16 / (int)sizeof(OT);
+    constexpr int NCH = RL / EPC;
+    static_assert(CH * NCH % NTHR == 0, "the tile splits evenly over the threads");
+#pragma unroll
+    for (int i = 0; i < CH * NCH / NTHR; ++i) {
+        const int u = (int)threadIdx.x + NTHR * i, row = u / NCH, pos = u % NCH;
+        const f32x4 x = lds_load<f32x4>(tile + u * 16);
+        if (row < nvalid) *(f32x4*)(dst + (size_t)row * rs + (pos ^ swz_f<OT, RL>(row)) * EPC) = x;
+    }
+}
+
 // zero rows nvalid .. CH - 1 of a swizzled tile [CH][RL] (all threads of the workgroup)
 template <class OT, int RL, int NTHR>
 __device__ __forceinline__ void zero_tail_rows(lds_char* tile, int nvalid) {

@@ -5,7 +5,8 @@
 // swizzled row-major tiles (see swz() in gdr2_device.hpp) in the operand type;
 // the state chains read them in either orientation from LDS. Accumulator-tile
 // dumps (U, Delta, dY) hold 16x16 tiles as 64 lanes x 4 elements, ordered
-// [value-column tile][token tile]. Each array starts on a 256-byte boundary.
+// [value-column tile][token tile]. The saved states S and dS' are fragment-major
+// (fmaj_off in gdr2_device.hpp). Each array starts on a 256-byte boundary.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
