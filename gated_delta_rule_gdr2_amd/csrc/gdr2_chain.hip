@@ -274,10 +274,37 @@ __device__ __forceinline__ void fwd_step(int c, const lds_char* buf, f32x4& S0, 
     const int l = lane_id(), lq = l >> 4, wv = wave_id();
     const LSwz<OT, DK> vWM{buf + B::WM}, vKD{buf + B::KD}, vQG{buf + B::QG};
     const LSwz<OT, CH> vM{buf + B::M};
-    FT SB[NW];
+    if (TRAIN) stage_rows<OT>(stage, S0, S1, pd.st);  // chunk start state -> pending store
+    // Every LDS operand read of the step is issued before the first product (the
+    // scheduling fence keeps them together), so the wave waits on LDS latency once.
+    FT SB[NW], WM[4][NW], QGf[TPW][NW], Mf[TPW][2], KDf[2][2];
+    float uu[4][4], g0[4], g1[4];
 #pragma unroll
     for (int kb = 0; kb < NW; ++kb) SB[kb] = get_block<OT>(xr, kb);
-    if (TRAIN) stage_rows<OT>(stage, S0, S1, pd.st);  // chunk start state -> pending store
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int kb = 0; kb < NW; ++kb) WM[t][kb] = lfrag_rowk<OT, OT>(vWM, 16 * t, 32 * kb);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) lds_get4<OT>(buf + B::U + (t * 256 + l * 4) * (int)sizeof(OT), uu[t]);
+    if (OUT) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int t = wv * TPW + u;
+#pragma unroll
+            for (int kb = 0; kb < NW; ++kb) QGf[u][kb] = lfrag_rowk<OT, OT>(vQG, 16 * t, 32 * kb);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) Mf[u][kb] = lfrag_rowk<OT, OT>(vM, 16 * t, 32 * kb);
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        KDf[0][kb] = lfrag_colk<OT, OT>(vKD, 32 * wv, 32 * kb);
+        KDf[1][kb] = lfrag_colk<OT, OT>(vKD, 32 * wv + 16, 32 * kb);
+    }
+    lds_get4<float>(buf + B::GC + (32 * wv + 4 * lq) * 4, g0);
+    lds_get4<float>(buf + B::GC + (32 * wv + 16 + 4 * lq) * 4, g1);
+    __builtin_amdgcn_sched_barrier(0);
     // Delta = U - Wm S, all four token tiles
     f32x4 D[4];
 #pragma unroll
@@ -285,14 +312,11 @@ __device__ __forceinline__ void fwd_step(int c, const lds_char* buf, f32x4& S0, 
 #pragma unroll
     for (int kb = 0; kb < NW; ++kb)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) mma(D[t], lfrag_rowk<OT, OT>(vWM, 16 * t, 32 * kb), SB[kb]);
+        for (int t = 0; t < 4; ++t) mma(D[t], WM[t][kb], SB[kb]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        float uu[4];
-        lds_get4<OT>(buf + B::U + (t * 256 + l * 4) * (int)sizeof(OT), uu);
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) D[t][i] = uu[i] - D[t][i];
-    }
+        for (int i = 0; i < 4; ++i) D[t][i] = uu[t][i] - D[t][i];
     FT DB[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) DB[kb] = frag_of<OT>(D[2 * kb], D[2 * kb + 1]);
@@ -300,26 +324,22 @@ __device__ __forceinline__ void fwd_step(int c, const lds_char* buf, f32x4& S0, 
     if (OUT) {
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
-            const int t = wv * TPW + u;
             f32x4 po = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < NW; ++kb) mma(po, SB[kb], lfrag_rowk<OT, OT>(vQG, 16 * t, 32 * kb));
+            for (int kb = 0; kb < NW; ++kb) mma(po, SB[kb], QGf[u][kb]);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) mma(po, DB[kb], lfrag_rowk<OT, OT>(vM, 16 * t, 32 * kb));
+            for (int kb = 0; kb < 2; ++kb) mma(po, DB[kb], Mf[u][kb]);
             pd.O[u] = po;
         }
     }
     // S' = diag(exp gam_C) S + Kd^T Delta on this wave's rows
     {
-        float g0[4], g1[4];
-        lds_get4<float>(buf + B::GC + (32 * wv + 4 * lq) * 4, g0);
-        lds_get4<float>(buf + B::GC + (32 * wv + 16 + 4 * lq) * 4, g1);
         f32x4 a0 = {g0[0] * S0[0], g0[1] * S0[1], g0[2] * S0[2], g0[3] * S0[3]};
         f32x4 a1 = {g1[0] * S1[0], g1[1] * S1[1], g1[2] * S1[2], g1[3] * S1[3]};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            mma(a0, lfrag_colk<OT, OT>(vKD, 32 * wv, 32 * kb), DB[kb]);
-            mma(a1, lfrag_colk<OT, OT>(vKD, 32 * wv + 16, 32 * kb), DB[kb]);
+            mma(a0, KDf[0][kb], DB[kb]);
+            mma(a1, KDf[1][kb], DB[kb]);
         }
         S0 = a0;
         S1 = a1;
@@ -496,14 +516,37 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0,
     const LSwz<OT, DK> vKD{buf + B::KD}, vQG{buf + B::QG}, vWM{buf + B::WM};
     const LSwz<OT, CH> vM{buf + B::M}, vT{buf + B::T};
     const LPad<OT> vDO{buf + B::DO, 16};
-    FT dSB[NW];
+    stage_rows<OT>(stage, dS0, dS1, pd.st);  // gradient w.r.t. this chunk's end state
+    // Every LDS operand read of the step is issued before the first product (the
+    // scheduling fence keeps them together), so the wave waits on LDS latency once.
+    FT dSB[NW], KDf[4][NW], Mf[4][2], dOB[2], WMf[2][2], QGf[2][2], Tf[TPW][2];
+    float g0[4], g1[4];
 #pragma unroll
     for (int kb = 0; kb < NW; ++kb) dSB[kb] = get_block<OT>(xr, kb);
-    stage_rows<OT>(stage, dS0, dS1, pd.st);  // gradient w.r.t. this chunk's end state
     // B fragments of dO: K = token, N = this slice's 16 value channels
-    FT dOB[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) dOB[kb] = lfrag_colk<OT, OT>(vDO, 0, 32 * kb);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int kb = 0; kb < NW; ++kb) KDf[t][kb] = lfrag_rowk<OT, OT>(vKD, 16 * t, 32 * kb);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) Mf[t][kb] = lfrag_colk<OT, OT>(vM, 16 * t, 32 * kb);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        WMf[0][kb] = lfrag_colk<OT, OT>(vWM, 32 * wv, 32 * kb);
+        WMf[1][kb] = lfrag_colk<OT, OT>(vWM, 32 * wv + 16, 32 * kb);
+        QGf[0][kb] = lfrag_colk<OT, OT>(vQG, 32 * wv, 32 * kb);
+        QGf[1][kb] = lfrag_colk<OT, OT>(vQG, 32 * wv + 16, 32 * kb);
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) Tf[u][kb] = lfrag_colk<OT, OT>(vT, 16 * (wv * TPW + u), 32 * kb);
+    lds_get4<float>(buf + B::GC + (32 * wv + 4 * lq) * 4, g0);
+    lds_get4<float>(buf + B::GC + (32 * wv + 16 + 4 * lq) * 4, g1);
+    __builtin_amdgcn_sched_barrier(0);
     // dDelta = M^T dO + Kd dS', all four token tiles
     f32x4 dD[4];
 #pragma unroll
@@ -511,28 +554,25 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0,
 #pragma unroll
     for (int kb = 0; kb < NW; ++kb)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) mma(dD[t], lfrag_rowk<OT, OT>(vKD, 16 * t, 32 * kb), dSB[kb]);
+        for (int t = 0; t < 4; ++t) mma(dD[t], KDf[t][kb], dSB[kb]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) mma(dD[t], lfrag_colk<OT, OT>(vM, 16 * t, 32 * kb), dOB[kb]);
+        for (int t = 0; t < 4; ++t) mma(dD[t], Mf[t][kb], dOB[kb]);
     FT dDB[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) dDB[kb] = frag_of<OT>(dD[2 * kb], dD[2 * kb + 1]);
     // dS = diag(exp gam_C) dS' + Qg^T dO - Wm^T dDelta on this wave's rows
     {
-        float g0[4], g1[4];
-        lds_get4<float>(buf + B::GC + (32 * wv + 4 * lq) * 4, g0);
-        lds_get4<float>(buf + B::GC + (32 * wv + 16 + 4 * lq) * 4, g1);
         f32x4 p0 = {g0[0] * dS0[0], g0[1] * dS0[1], g0[2] * dS0[2], g0[3] * dS0[3]};
         f32x4 p1 = {g1[0] * dS1[0], g1[1] * dS1[1], g1[2] * dS1[2], g1[3] * dS1[3]};
         f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = n0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            mma(n0, lfrag_colk<OT, OT>(vWM, 32 * wv, 32 * kb), dDB[kb]);
-            mma(n1, lfrag_colk<OT, OT>(vWM, 32 * wv + 16, 32 * kb), dDB[kb]);
-            mma(p0, lfrag_colk<OT, OT>(vQG, 32 * wv, 32 * kb), dOB[kb]);
-            mma(p1, lfrag_colk<OT, OT>(vQG, 32 * wv + 16, 32 * kb), dOB[kb]);
+            mma(n0, WMf[0][kb], dDB[kb]);
+            mma(n1, WMf[1][kb], dDB[kb]);
+            mma(p0, QGf[0][kb], dOB[kb]);
+            mma(p1, QGf[1][kb], dOB[kb]);
         }
         dS0 = p0 - n0;
         dS1 = p1 - n1;
@@ -541,10 +581,9 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0,
     // dY = T^T dDelta on this wave's token tiles (for the intra-chunk kernel)
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-        const int t = wv * TPW + u;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vT, 16 * t, 32 * kb), dDB[kb]);
+        for (int kb = 0; kb < 2; ++kb) mma(acc, Tf[u][kb], dDB[kb]);
         pd.Y[u] = acc;
     }
     pd.c = c;
