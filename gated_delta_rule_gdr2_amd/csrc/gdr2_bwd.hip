@@ -188,7 +188,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_delta) + cid * L.delta, rdl);
     undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_dy) + cid * L.dy, rdy);
 
-    // the staged rows have landed: zero the padding rows of a partial chunk
+    // zero the padding rows of a partial chunk (positions no DMA writes); then wait for
+    // this wave's copies, and the barrier below for everyone's
     wait_vm<0>();
     if (nvalid < CH) {
         zero_tail_rows<OT, DK, NTHR>(sG, nvalid);

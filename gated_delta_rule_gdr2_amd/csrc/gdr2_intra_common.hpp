@@ -256,9 +256,9 @@ __device__ __forceinline__ void x_tile_from(const float (&vv)[4][4], const float
 // asynchronous global->LDS DMA, 16 bytes per lane. One instruction fills 1 KB of the
 // tile, i.e. whole rows (4 of 256 bytes or 8 of 128 bytes), so every request is a whole
 // cache line; the lane that fills position p of row r fetches chunk p ^ f(r) of the row
-// (the swizzle only permutes chunks within a row). Rows at or past nvalid are fetched
-// from row nvalid - 1 and zeroed by zero_tail_rows once the copy has landed.
-// Instructions n = w, w + NW, ... belong to wave w.
+// (the swizzle only permutes chunks within a row). Lanes of rows at or past nvalid
+// issue no copy (their positions are written by zero_tail_rows alone, so the two never
+// race). Instructions n = w, w + NW, ... belong to wave w.
 template <class OT, int RL, int NW>
 __device__ __forceinline__ void dma_rows(const OT* base, size_t rs, int nvalid, lds_char* tile, int wv) {
     constexpr int EPC = 16 / (int)sizeof(OT);
@@ -272,9 +272,10 @@ __device__ __forceinline__ void dma_rows(const OT* base, size_t rs, int nvalid, 
         if (NI % NW == 0 || n < NI) {
             const int row = n * RPI + l / NCH, pos = l % NCH;
             const int c = pos ^ swz_f<OT, RL>(row);
-            const int rr = row < nvalid ? row : nvalid - 1;
-            const char* src = (const char*)(base + (size_t)rr * rs + c * EPC);
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + n * 1024), 16, 0, 0);
+            if (row < nvalid) {
+                const char* src = (const char*)(base + (size_t)row * rs + c * EPC);
+                __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + n * 1024), 16, 0, 0);
+            }
         }
     }
 }
@@ -285,12 +286,13 @@ template <class OT, int RL, int NTHR>
 __device__ __forceinline__ void store_rows_tiles(const lds_char* tile, OT* dst, size_t rs, int nvalid) {
     constexpr int EPC = 16 / (int)sizeof(OT);
     constexpr int NCH = RL / EPC;
-    static_assert(CH * NCH % NTHR == 0, "the tile splits evenly over the threads");
 #pragma unroll
-    for (int i = 0; i < CH * NCH / NTHR; ++i) {
+    for (int i = 0; i < (CH * NCH + NTHR - 1) / NTHR; ++i) {
         const int u = (int)threadIdx.x + NTHR * i, row = u / NCH, pos = u % NCH;
-        const f32x4 x = lds_load<f32x4>(tile + u * 16);
-        if (row < nvalid) *(f32x4*)(dst + (size_t)row * rs + (pos ^ swz_f<OT, RL>(row)) * EPC) = x;
+        if ((CH * NCH % NTHR == 0 || u < CH * NCH) && row < nvalid) {
+            const f32x4 x = lds_load<f32x4>(tile + u * 16);
+            *(f32x4*)(dst + (size_t)row * rs + (pos ^ swz_f<OT, RL>(row)) * EPC) = x;
+        }
     }
 }
 
