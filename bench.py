@@ -118,6 +118,7 @@ class HipEvents:
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         evs = (ctypes.c_void_p * n)()
@@ -128,6 +129,11 @@ class HipEvents:
                 raise RuntimeError("hipEventCreate failed: %d" % st)
             evs[i] = e.value
         return evs
+
+    def record(self, e, stream):
+        st = self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % st)
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -316,6 +322,20 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    # The same steps once more, each after a 512 MiB write that evicts the 256 MB Infinity
+    # Cache, timed by events around the step alone (the write is outside): HBM-honest step time.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ev_f = hip.create(2 * K)
+    for i in range(K):
+        flush.fill_(i & 255)
+        hip.record(ev_f[2 * i], stream)
+        step(None)
+        hip.record(ev_f[2 * i + 1], stream)
+    torch.cuda.synchronize()
+    flushed_ms = sorted(hip.elapsed_ms(ev_f[2 * i], ev_f[2 * i + 1]) for i in range(K))[K // 2]
+    hip.destroy(ev_f)
+    del flush
+
     kern = {"fwd_intra": (0, 1), "fwd_chain": (1, 2), "bwd_chain": (3, 4), "bwd_intra": (4, 5)}
     avg_ms = {k: sum(hip.elapsed_ms(evs[6 * i + a], evs[6 * i + b]) for i in range(K)) / K
               for k, (a, b) in kern.items()}
@@ -348,6 +368,7 @@ def main():
         "step_roofline": {"bound": "hbm", "algorithmic_bytes": step_bytes, "t_roofline_ms": t_roof_ms,
                           "frac": t_roof_ms / ms_step},
         "kernels_avg_ms": avg_ms,
+        "ms_per_step_cache_evicted": flushed_ms,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, host)
