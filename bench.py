@@ -248,6 +248,37 @@ def summarize_profile(d, workload, copy_mib, command):
     print("wrote", traffic_summary_path(workload), "and the kernel table")
 
 
+def decode_step_measurement(torch, g2, reps=50):
+    """Recurrent step (gdr2_step, decoding): one token per call for B = 512 sequences of H = 16
+    heads at d_k = d_v = 128, bf16, state fp32 and updated in place. Algorithmic bytes per call:
+    the state read and written (2 x 64 KB per head) plus the token's q, k, g, b, v, w and o."""
+    B, H, D = 512, 16, 128  # a 512 MB state, twice the Infinity Cache: every call streams HBM
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    def rnd(*shape):
+        return torch.randn(*shape, device="cuda", generator=gen)
+    q, k = (torch.nn.functional.normalize(rnd(B, 1, H, D), dim=-1).bfloat16() for _ in range(2))
+    v = rnd(B, 1, H, D).bfloat16()
+    g = (-torch.nn.functional.softplus(rnd(B, 1, H, D)) * 0.1).bfloat16()
+    b, w = (torch.sigmoid(rnd(B, 1, H, D)).bfloat16() for _ in range(2))
+    state = rnd(B, H, D, D) * 0.02
+    o = torch.empty(B, 1, H, D, dtype=torch.bfloat16, device="cuda")
+    for _ in range(10):
+        g2.gdr2_step(q, k, v, g, b, w, state, o=o)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g2.gdr2_step(q, k, v, g, b, w, state, o=o)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = B * H * (2 * D * D * 4 + 7 * D * 2)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "decode_bf16_b512h16d128_t1", "us_per_call": us, "tokens_per_s": B / (us * 1e-6),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,6 +400,7 @@ def main():
                           "frac": t_roof_ms / ms_step},
         "kernels_avg_ms": avg_ms,
         "ms_per_step_cache_evicted": flushed_ms,
+        "decode_step": decode_step_measurement(torch, g2),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, host)

@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["gdr2_fwd", "gdr2_bwd", "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes",
+__all__ = ["gdr2_fwd", "gdr2_bwd", "gdr2_step", "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes",
            "gdr2_strerror", "gdr2_version", "GDR2Function", "library_path", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +28,7 @@ _lib = None
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 _DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
-EXPORTED = ["gdr2_fwd", "gdr2_bwd", "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes",
+EXPORTED = ["gdr2_fwd", "gdr2_bwd", "gdr2_step", "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes",
             "gdr2_strerror", "gdr2_version"]
 
 
@@ -54,6 +54,8 @@ def load_library():
     lib.gdr2_fwd.restype = i
     lib.gdr2_bwd.argtypes = [vp] * 16 + [i] * 8 + [vp, sz, vp, vp]
     lib.gdr2_bwd.restype = i
+    lib.gdr2_step.argtypes = [vp] * 8 + [i] * 6 + [vp]
+    lib.gdr2_step.restype = i
     lib.gdr2_strerror.argtypes = [i]
     lib.gdr2_strerror.restype = ctypes.c_char_p
     lib.gdr2_version.argtypes = []
@@ -147,6 +149,26 @@ def gdr2_fwd(q, k, v, g, b, w, h0=None, *, chunk=64, save_for_bwd=False, ws=None
                       stage_events)
     _raise(st, "gdr2_fwd")
     return o, ht, ws
+
+
+def gdr2_step(q, k, v, g, b, w, state, *, o=None, stream=None):
+    """Recurrent step (decoding): the T tokens of q, k, g, b [B,T,H,dk] and v, w [B,T,H,dv]
+    one at a time from ``state`` ([B,H,dk,dv] fp32), which is updated in place. Returns o."""
+    lib = load_library()
+    B, T, H, dk, dv, dt = _dims(q, v)
+    for t, n, shp in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)), (g, "g", (B, T, H, dk)),
+                      (b, "b", (B, T, H, dk)), (v, "v", (B, T, H, dv)), (w, "w", (B, T, H, dv))):
+        _check(t, n, q.dtype, shp)
+    if state is None:
+        raise ValueError("state is required")
+    _check(state, "state", torch.float32, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty(B, T, H, dv, dtype=q.dtype, device=q.device)
+    _check(o, "o", q.dtype, (B, T, H, dv))
+    st = lib.gdr2_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(state), _ptr(o),
+                       B, T, H, dk, dv, dt, _stream(stream))
+    _raise(st, "gdr2_step")
+    return o
 
 
 def gdr2_bwd(q, k, v, g, b, w, h0, dout, dht=None, *, chunk=64, ws=None, fwd_saved=False,

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdr2.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["gdr2_api.cpp", "gdr2_fwd.hip", "gdr2_bwd.hip", "gdr2_chain.hip"]
+SOURCES = ["gdr2_api.cpp", "gdr2_fwd.hip", "gdr2_bwd.hip", "gdr2_chain.hip", "gdr2_step.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

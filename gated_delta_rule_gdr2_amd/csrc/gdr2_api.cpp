@@ -114,6 +114,22 @@ int gdr2_bwd(const void* q, const void* k, const void* v, const void* g, const v
     return e == hipSuccess ? GDR2_OK : GDR2_ERR_HIP;
 }
 
+int gdr2_step(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+              float* state, void* o, int B, int T, int H, int dk, int dv, int dtype, void* stream) {
+    if (!q || !k || !v || !g || !b || !w || !state || !o) return GDR2_ERR_NULL;
+    int st = check_shape(B, T, H, dk, dv, 64, dtype);
+    if (st != GDR2_OK) return st;
+    const void* ptrs[] = {q, k, v, g, b, w, state, o};
+    for (const void* p : ptrs)
+        if (!aligned(p)) return GDR2_ERR_ALIGN;
+    gdr2::Args a = {};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.b = b; a.w = w;
+    a.o = o; a.state = state;
+    fill_common(a, B, T, H, dk, dv, dtype, nullptr);
+    hipError_t e = gdr2::launch_step(a, dtype == GDR2_DTYPE_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? GDR2_OK : GDR2_ERR_HIP;
+}
+
 const char* gdr2_strerror(int status) {
     switch (status) {
         case GDR2_OK: return "ok";

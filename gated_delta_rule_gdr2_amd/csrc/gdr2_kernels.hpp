@@ -17,6 +17,7 @@ struct Args {
     float* ht;          // [B, H, DK, DV] or null
     void *dq, *dk, *dv, *dg, *db, *dw;
     float* dh0;         // [B, H, DK, DV] or null
+    float* state;       // recurrent step: [B, H, DK, DV], read and overwritten
     char* ws;           // workspace base
     Layout L;
     int B, T, H, NT;
@@ -36,6 +37,7 @@ template <class OT, int DK, int DV>
 hipError_t launch_bwd_chain_t(const Args& a, hipStream_t stream);
 hipError_t launch_fwd(const Args& a, bool bf16, bool train, hipStream_t stream);
 hipError_t launch_bwd(const Args& a, bool bf16, hipStream_t stream);
+hipError_t launch_step(const Args& a, bool bf16, hipStream_t stream);
 size_t fwd_intra_lds_bytes(int DK, int DV, int esz);
 size_t bwd_intra_lds_bytes(int DK, int DV, int esz);
 

@@ -86,7 +86,19 @@ int gdr2_bwd(const void* q, const void* k, const void* v, const void* g, const v
              int dtype, int fwd_saved, void* workspace, size_t workspace_bytes, void* stream,
              void* const* stage_events);
 
-/* stage_events (both calls): NULL, or an array of hipEvent_t that the call
+/* Recurrent step, for decoding: processes the T tokens of q, k, v, g, b, w one at a
+ * time, starting from the state in `state` (fp32 [B][H][dk][dv], required), which is
+ * read and then overwritten with the state after the last token; writes o (layouts as
+ * above). Same recurrence as gdr2_fwd -- for state = h0 it returns the same o and final
+ * state up to fp32 rounding order -- computed token by token with each head's state
+ * held on chip: constant memory per head however long the sequence (chatpaper.ai
+ * abstract of "Gated DeltaNet-2": constant-memory decoding). Supported dk/dv/dtype as
+ * gdr2_fwd; no workspace; no backward. Errors as gdr2_fwd (GDR2_ERR_NULL when state
+ * is NULL). */
+int gdr2_step(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+              float* state, void* o, int B, int T, int H, int dk, int dv, int dtype, void* stream);
+
+/* stage_events (gdr2_fwd and gdr2_bwd): NULL, or an array of hipEvent_t that the call
  * records on `stream` around its kernels, for per-kernel timing: element 0
  * before the first kernel and element i after the i-th kernel. gdr2_fwd runs
  * 2 kernels (intra-chunk, state chain), so it needs 3 events; gdr2_bwd runs

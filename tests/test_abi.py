@@ -138,3 +138,22 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(g2, "_lib", None)
     with pytest.raises(RuntimeError, match="not found"):
         g2.load_library()
+
+
+def step(lib, ptrs=None, B=1, T=1, H=1, dk=64, dv=64, dtype=g2.DTYPE_BF16):
+    p = [FAKE] * 8 if ptrs is None else ptrs
+    return lib.gdr2_step(*[ctypes.c_void_p(x) for x in p], B, T, H, dk, dv, dtype, None)
+
+
+def test_step_rejects_bad_arguments(lib):
+    # q k v g b w state o: all required
+    for i in range(8):
+        p = [FAKE] * 8
+        p[i] = 0
+        assert step(lib, p) == ERR_NULL, i
+        p[i] = FAKE + 4
+        assert step(lib, p) == ERR_ALIGN, i
+    assert step(lib, B=0) == ERR_SHAPE
+    assert step(lib, T=0) == ERR_SHAPE
+    assert step(lib, dk=96) == ERR_UNSUP
+    assert step(lib, dk=128, dv=128, dtype=g2.DTYPE_F32) == ERR_UNSUP
