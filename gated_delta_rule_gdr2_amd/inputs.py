@@ -34,7 +34,8 @@ class Workload:
     backward: bool        # fwd only, or fwd+bwd
     seed: int
     g_scale: float = 0.1  # g = -softplus(N(0,1)) * g_scale per key channel
-    b_mu: float = 0.0     # b = sigmoid(N(b_mu, 1)) per channel
+    b_mu: float = 0.0     # b = b_scale * sigmoid(N(b_mu, 1)) per channel
+    b_scale: float = 1.0  # 2.0: the [0, 2] erase range (negative eigenvalues of the transition)
     w_mu: float = 0.0     # w = sigmoid(N(w_mu, 1)) per channel
     h0_std: float = 0.0   # h0 ~ N(0, h0_std) in fp32 (0 -> no initial state)
     tied: bool = False    # b = w = beta * 1, beta = sigmoid(N(0,1)) per token
@@ -100,7 +101,7 @@ def make_inputs(wl: Workload, device="cpu", **overrides) -> dict:
         b = np.broadcast_to(beta, (B, T, H, DK)).copy()
         w = np.broadcast_to(beta, (B, T, H, DV)).copy()
     else:
-        b = _sigmoid(rng.standard_normal((B, T, H, DK)) + wl.b_mu)
+        b = wl.b_scale * _sigmoid(rng.standard_normal((B, T, H, DK)) + wl.b_mu)
         w = _sigmoid(rng.standard_normal((B, T, H, DV)) + wl.w_mu)
     h0 = rng.standard_normal((B, H, DK, DV)) * wl.h0_std if wl.h0_std > 0 else None
     do = rng.standard_normal((B, T, H, DV)) if wl.backward else None

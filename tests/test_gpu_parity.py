@@ -9,6 +9,8 @@ every supported (dk, dv); the five benchmark workloads run at full size in the
 same launch configuration the benchmark times, and are compared on sampled
 (batch, head) sequences, which the oracle computes independently.
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -117,6 +119,9 @@ SMALL = [
     # rows that the backward kernel stages and zeroes in LDS
     dict(DK=128, DV=128, T=191, dtype="bf16", B=2, H=8),
     dict(DK=64, DV=128, T=100, dtype="bf16", B=4, H=4),
+    # the [0, 2] erase range: b = 2 sigmoid(.), negative eigenvalues of the transition
+    dict(DK=128, DV=128, T=200, dtype="bf16", b_scale=2.0, h0_std=0.1),
+    dict(DK=64, DV=64, T=130, dtype="f32", b_scale=2.0),
 ]
 
 
@@ -159,6 +164,16 @@ def test_workload_full_size(name):
     sel = None if wl.B * wl.H * wl.T <= 4096 else _sample(wl)
     ref = run_oracle(inp, wl.backward, sel=sel)
     compare(gpu, ref, wl.dtype, wl.backward, sel=sel, has_h0=inp["h0"] is not None)
+
+
+def test_erase_range_two_full_size():
+    """The headline training shape with the [0, 2] erase range (b = 2 sigmoid(N(0, 1)))."""
+    wl = replace(WORKLOADS["fwdbwd_bf16_b2h16t4096d128"], b_scale=2.0, seed=33)
+    inp = make_inputs(wl)
+    gpu = run_gpu(inp, True)
+    sel = _sample(wl)
+    ref = run_oracle(inp, True, sel=sel)
+    compare(gpu, ref, wl.dtype, True, sel=sel, has_h0=False)
 
 
 def test_state_size_matches_the_pages():

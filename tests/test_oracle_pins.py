@@ -177,6 +177,26 @@ def test_overwrite_property():
     assert relerr(o, w * v) < 1e-12
 
 
+def test_erase_strength_two_is_a_householder_reflection():
+    """The [0, 2] erase range (LIT-802 takeaway 5 / Table 5): with b = 2*1, a unit key, no
+    decay and no write, the transition I - 2 k k^T is a reflection: it keeps the state's
+    Frobenius norm, negates the state's component along k, and twice the same key restores
+    the state exactly."""
+    rng = np.random.default_rng(12)
+    B, T, H, DK, DV = 1, 2, 1, 5, 3
+    q, k, v, g, b, w, h0 = rand_inputs(rng, B, T, H, DK, DV)
+    k[:, 1] = k[:, 0]
+    b = np.full_like(b, 2.0)
+    g = np.zeros_like(g)
+    w = np.zeros_like(w)
+    _, h1 = oracle.fwd(q[:, :1], k[:, :1], v[:, :1], g[:, :1], b[:, :1], w[:, :1], h0)
+    _, h2 = oracle.fwd(q, k, v, g, b, w, h0)
+    kk = k[0, 0, 0]
+    assert abs(np.linalg.norm(h1) - np.linalg.norm(h0)) < 1e-13 * np.linalg.norm(h0)
+    assert relerr(kk @ h1[0, 0], -(kk @ h0[0, 0])) < 1e-13
+    assert relerr(h2, h0) < 1e-13
+
+
 def test_b_zero_is_decayed_linear_attention():
     """b = 0 removes the erase: o_t = sum_{i<=t} [sum_c q_tc k_ic exp(G_tc - G_ic)] (w_i*v_i)
     + (q_t*exp(G_t))^T h0 with G the running sum of g; with g = 0 it is tril(Q K^T)(W*V) + Q h0."""
