@@ -383,3 +383,45 @@ def test_golden_regression_fixture():
     assert relerr(o, d["o"]) < 1e-14 and relerr(ht, d["ht"]) < 1e-14
     for key in ["dq", "dk", "dv", "dg", "db", "dw", "dh0"]:
         assert relerr(gr[key], d[key]) < 1e-14, key
+
+
+# ----------------------------------------------------------------------------- gate logits
+
+def test_gate_logit_activations():
+    """sigmoid(0) = 1/2, softplus(0) = ln 2, and the activations' limits."""
+    g, b, w = oracle.gates_from_logits(np.array([0.0, -40.0, 40.0]), np.array([0.0, -40.0, 40.0]),
+                                       np.array([0.0, 3.0, -3.0]), 0.5)
+    assert np.allclose(g, [-0.5 * np.log(2.0), -0.5 * np.exp(-40.0), -20.0], rtol=1e-12, atol=0)
+    assert np.allclose(b, [0.5, np.exp(-40.0), 1.0], rtol=1e-12, atol=0)
+    assert np.allclose(w, [0.5, 1.0 / (1.0 + np.exp(-3.0)), 1.0 / (1.0 + np.exp(3.0))], rtol=1e-12, atol=0)
+
+
+def test_backward_through_gate_logits_matches_finite_differences():
+    rng = np.random.default_rng(21)
+    B, T, H, DK, DV = 1, 9, 1, 3, 4
+    q, k, v, _, _, _, h0 = rand_inputs(rng, B, T, H, DK, DV, normalize=False)
+    zg, zb, zw = rng.standard_normal((B, T, H, DK)), rng.standard_normal((B, T, H, DK)), \
+        rng.standard_normal((B, T, H, DV))
+    do = rng.standard_normal(v.shape)
+    dht = rng.standard_normal(h0.shape)
+    s = 0.7
+    gr = oracle.bwd_logits(q, k, v, zg, zb, zw, h0, do, dht, g_scale=s)
+
+    def lossz(zg, zb, zw):
+        o, ht = oracle.fwd_logits(q, k, v, zg, zb, zw, h0, g_scale=s)
+        return float(np.sum(o * do) + np.sum(ht * dht))
+
+    args = dict(zg=zg, zb=zb, zw=zw)
+    eps = 1e-6
+    for name, key in [("zg", "dg"), ("zb", "db"), ("zw", "dw")]:
+        x = args[name]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            ix = it.multi_index
+            xp = x.copy(); xp[ix] += eps
+            xm = x.copy(); xm[ix] -= eps
+            fd[ix] = (lossz(**dict(args, **{name: xp})) - lossz(**dict(args, **{name: xm}))) / (2 * eps)
+        err = np.max(np.abs(gr[key] - fd)) / np.max(np.abs(fd))
+        assert err < 1e-7, (name, err)
+
