@@ -117,35 +117,37 @@ def bwd(q, k, v, g, b, w, h0, do, dht=None):
 
 # ----------------------------------------------------------------------------- gate logits
 # The gates as the pages define them: the erase gate b and the write gate w are each a
-# sigmoid of their own projection (LIT-802, "Key takeaways", first bullet). The pages do
-# not fix how the log-decay is parametrised; the reading used here is g = -s * softplus(z_g)
-# with a positive scale s per call (so alpha = exp g lies in (0, 1)). In numpy, fp64.
+# sigmoid of their own projection (Gated DeltaNet-2 record LIT-802, "Key takeaways", first
+# bullet); the widened erase range [0, 2] of its Table 5 ablation is b = 2 sigmoid(z_b),
+# taken here as b = b_scale * sigmoid(z_b). The pages do not fix how the log-decay is
+# parametrised; the reading used here is g = -g_scale * softplus(z_g), g_scale > 0, so
+# that alpha = exp g lies in (0, 1). numpy, fp64.
 
 def _sigmoid(z):
     e = np.exp(-np.abs(z))                       # never overflows; exact in both tails
     return np.where(z >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
 
 
-def gates_from_logits(zg, zb, zw, g_scale):
-    """(g, b, w) from the logits: g = -g_scale * softplus(zg), b = sigmoid(zb), w = sigmoid(zw)."""
+def gates_from_logits(zg, zb, zw, g_scale=1.0, b_scale=1.0):
+    """(g, b, w) = (-g_scale softplus(zg), b_scale sigmoid(zb), sigmoid(zw))."""
     zg, zb, zw = (_f64(x) for x in (zg, zb, zw))
-    return -g_scale * np.logaddexp(0.0, zg), _sigmoid(zb), _sigmoid(zw)
+    return -g_scale * np.logaddexp(0.0, zg), b_scale * _sigmoid(zb), _sigmoid(zw)
 
 
-def fwd_logits(q, k, v, zg, zb, zw, h0=None, g_scale=1.0):
+def fwd_logits(q, k, v, zg, zb, zw, h0=None, g_scale=1.0, b_scale=1.0):
     """Forward recurrence with the gates given as logits (see gates_from_logits)."""
-    g, b, w = gates_from_logits(zg, zb, zw, g_scale)
+    g, b, w = gates_from_logits(zg, zb, zw, g_scale, b_scale)
     return fwd(q, k, v, g, b, w, h0)
 
 
-def bwd_logits(q, k, v, zg, zb, zw, h0, do, dht=None, g_scale=1.0):
+def bwd_logits(q, k, v, zg, zb, zw, h0, do, dht=None, g_scale=1.0, b_scale=1.0):
     """Backward with the gates given as logits: the dict holds dL/dzg, dL/dzb, dL/dzw under
-    the keys dg, db, dw (chain rule through the activations: sigmoid' = s (1 - s),
-    d(-c softplus(z))/dz = -c sigmoid(z)), the other gradients as bwd()."""
-    g, b, w = gates_from_logits(zg, zb, zw, g_scale)
+    the keys dg, db, dw, the other gradients as bwd(). Chain rule through the activations:
+    d sigmoid/dz = sigmoid (1 - sigmoid), d softplus/dz = sigmoid."""
+    g, b, w = gates_from_logits(zg, zb, zw, g_scale, b_scale)
     gr = bwd(q, k, v, g, b, w, h0, do, dht)
+    sb = _sigmoid(_f64(zb))
     gr["dg"] = gr["dg"] * (-g_scale * _sigmoid(_f64(zg)))
-    gr["db"] = gr["db"] * b * (1.0 - b)
-    gr["dw"] = gr["dw"] * w * (1.0 - w)
+    gr["db"] = gr["db"] * (b_scale * sb * (1.0 - sb))
+    gr["dw"] = gr["dw"] * (w * (1.0 - w))
     return gr
-

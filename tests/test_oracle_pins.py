@@ -390,9 +390,9 @@ def test_golden_regression_fixture():
 def test_gate_logit_activations():
     """sigmoid(0) = 1/2, softplus(0) = ln 2, and the activations' limits."""
     g, b, w = oracle.gates_from_logits(np.array([0.0, -40.0, 40.0]), np.array([0.0, -40.0, 40.0]),
-                                       np.array([0.0, 3.0, -3.0]), 0.5)
+                                       np.array([0.0, 3.0, -3.0]), 0.5, 2.0)
     assert np.allclose(g, [-0.5 * np.log(2.0), -0.5 * np.exp(-40.0), -20.0], rtol=1e-12, atol=0)
-    assert np.allclose(b, [0.5, np.exp(-40.0), 1.0], rtol=1e-12, atol=0)
+    assert np.allclose(b, [1.0, 2.0 * np.exp(-40.0), 2.0], rtol=1e-12, atol=0)
     assert np.allclose(w, [0.5, 1.0 / (1.0 + np.exp(-3.0)), 1.0 / (1.0 + np.exp(3.0))], rtol=1e-12, atol=0)
 
 
@@ -405,10 +405,10 @@ def test_backward_through_gate_logits_matches_finite_differences():
     do = rng.standard_normal(v.shape)
     dht = rng.standard_normal(h0.shape)
     s = 0.7
-    gr = oracle.bwd_logits(q, k, v, zg, zb, zw, h0, do, dht, g_scale=s)
+    gr = oracle.bwd_logits(q, k, v, zg, zb, zw, h0, do, dht, g_scale=s, b_scale=2.0)
 
     def lossz(zg, zb, zw):
-        o, ht = oracle.fwd_logits(q, k, v, zg, zb, zw, h0, g_scale=s)
+        o, ht = oracle.fwd_logits(q, k, v, zg, zb, zw, h0, g_scale=s, b_scale=2.0)
         return float(np.sum(o * do) + np.sum(ht * dht))
 
     args = dict(zg=zg, zb=zb, zw=zw)
