@@ -279,6 +279,54 @@ def decode_step_measurement(torch, g2, reps=50):
                          "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nbytes}}
 
 
+def gate_logits_measurement(torch, g2, wl, K, stream):
+    """Fused gate activations: forward+backward steps with the gates passed as logits
+    (activated inside the kernels), against the same steps with the activations and their
+    chain rule done as separate elementwise passes in torch around the plain entry points.
+    Median of K event-timed steps each."""
+    from gated_delta_rule_gdr2_amd.inputs import make_inputs
+    x = {k: (None if v is None else v.cuda()) for k, v in make_inputs(wl, gates="logits").items()}
+    names = ("q", "k", "v", "zg", "zb", "zw")
+    sc = dict(g_scale=wl.g_scale, b_scale=wl.b_scale)
+    ws = g2.workspace(wl.B, wl.T, wl.H, wl.DK, wl.DV, x["q"].dtype, True, "cuda")
+    grads = {n: torch.empty_like(x[m]) for n, m in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg", "zg"),
+                                                     ("db", "zb"), ("dw", "zw"))}
+
+    def fused():
+        g2.gdr2_fwd_logits(*(x[n] for n in names), x["h0"], save_for_bwd=True, ws=ws, stream=stream, **sc)
+        g2.gdr2_bwd_logits(*(x[n] for n in names), x["h0"], x["do"], ws=ws, fwd_saved=True, grads=grads,
+                           need_dh0=False, stream=stream, **sc)
+
+    def separate():
+        zg, zb, zw = (x[n].float() for n in ("zg", "zb", "zw"))
+        g = (-wl.g_scale * torch.nn.functional.softplus(zg)).to(x["q"].dtype)
+        sb, w = torch.sigmoid(zb), torch.sigmoid(zw)
+        b = (wl.b_scale * sb).to(x["q"].dtype)
+        wq = w.to(x["q"].dtype)
+        g2.gdr2_fwd(x["q"], x["k"], x["v"], g, b, wq, x["h0"], save_for_bwd=True, ws=ws, stream=stream)
+        gr = g2.gdr2_bwd(x["q"], x["k"], x["v"], g, b, wq, x["h0"], x["do"], ws=ws, fwd_saved=True,
+                         need_dh0=False, stream=stream)
+        (gr["dg"].float() * (-wl.g_scale * torch.sigmoid(zg))).to(x["q"].dtype)
+        (gr["db"].float() * (wl.b_scale * sb * (1 - sb))).to(x["q"].dtype)
+        (gr["dw"].float() * (w * (1 - w))).to(x["q"].dtype)
+
+    hip = HipEvents()
+    res = {}
+    for name, fn in (("fused", fused), ("separate_torch_passes", separate)):
+        fn()
+        torch.cuda.synchronize()
+        ev = hip.create(2 * K)
+        for i in range(K):
+            hip.record(ev[2 * i], stream)
+            fn()
+            hip.record(ev[2 * i + 1], stream)
+        torch.cuda.synchronize()
+        res[name] = sorted(hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(K))[K // 2]
+        hip.destroy(ev)
+    return {"workload": wl.name + "_logits", "ms_per_step": res["fused"],
+            "ms_per_step_separate_torch_passes": res["separate_torch_passes"]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,6 +449,7 @@ def main():
         "kernels_avg_ms": avg_ms,
         "ms_per_step_cache_evicted": flushed_ms,
         "decode_step": decode_step_measurement(torch, g2),
+        "gate_logits": gate_logits_measurement(torch, g2, wl, K, stream),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, host)

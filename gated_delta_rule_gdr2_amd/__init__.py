@@ -19,8 +19,9 @@ import os
 
 import torch
 
-__all__ = ["gdr2_fwd", "gdr2_bwd", "gdr2_step", "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes",
-           "gdr2_strerror", "gdr2_version", "GDR2Function", "library_path", "load_library"]
+__all__ = ["gdr2_fwd", "gdr2_bwd", "gdr2_step", "gdr2_fwd_logits", "gdr2_bwd_logits", "gdr2_step_logits",
+           "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes", "gdr2_strerror", "gdr2_version",
+           "GDR2Function", "library_path", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr2.so")
@@ -28,8 +29,8 @@ _lib = None
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 _DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
-EXPORTED = ["gdr2_fwd", "gdr2_bwd", "gdr2_step", "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes",
-            "gdr2_strerror", "gdr2_version"]
+EXPORTED = ["gdr2_fwd", "gdr2_bwd", "gdr2_step", "gdr2_fwd_logits", "gdr2_bwd_logits", "gdr2_step_logits",
+            "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes", "gdr2_strerror", "gdr2_version"]
 
 
 def library_path() -> str:
@@ -56,6 +57,13 @@ def load_library():
     lib.gdr2_bwd.restype = i
     lib.gdr2_step.argtypes = [vp] * 8 + [i] * 6 + [vp]
     lib.gdr2_step.restype = i
+    f = ctypes.c_float
+    lib.gdr2_fwd_logits.argtypes = [vp] * 6 + [f, f] + [vp] * 3 + [i] * 8 + [vp, sz, vp, vp]
+    lib.gdr2_fwd_logits.restype = i
+    lib.gdr2_bwd_logits.argtypes = [vp] * 6 + [f, f] + [vp] * 10 + [i] * 8 + [vp, sz, vp, vp]
+    lib.gdr2_bwd_logits.restype = i
+    lib.gdr2_step_logits.argtypes = [vp] * 6 + [f, f] + [vp] * 2 + [i] * 6 + [vp]
+    lib.gdr2_step_logits.restype = i
     lib.gdr2_strerror.argtypes = [i]
     lib.gdr2_strerror.restype = ctypes.c_char_p
     lib.gdr2_version.argtypes = []
@@ -132,6 +140,19 @@ def gdr2_fwd(q, k, v, g, b, w, h0=None, *, chunk=64, save_for_bwd=False, ws=None
     h0: [B,H,dk,dv] fp32 or None. Returns (o, ht or None, ws). Pass ``ws`` back to
     gdr2_bwd(..., fwd_saved=True) when save_for_bwd is set. ``stage_events``: optional
     ctypes array of hipEvent_t handles recorded around the kernels (see include/gdr2.h)."""
+    return _fwd(None, q, k, v, g, b, w, h0, chunk, save_for_bwd, ws, o, output_final_state, stream,
+                stage_events)
+
+
+def gdr2_fwd_logits(q, k, v, zg, zb, zw, h0=None, *, g_scale=1.0, b_scale=1.0, chunk=64, save_for_bwd=False,
+                    ws=None, o=None, output_final_state=True, stream=None, stage_events=None):
+    """Forward pass with the gates given as logits, activated inside the kernels:
+    g = -g_scale softplus(zg), b = b_scale sigmoid(zb), w = sigmoid(zw). Otherwise as gdr2_fwd."""
+    return _fwd((g_scale, b_scale), q, k, v, zg, zb, zw, h0, chunk, save_for_bwd, ws, o, output_final_state,
+                stream, stage_events)
+
+
+def _fwd(scales, q, k, v, g, b, w, h0, chunk, save_for_bwd, ws, o, output_final_state, stream, stage_events):
     lib = load_library()
     B, T, H, dk, dv, dt = _dims(q, v)
     for t, n, shp in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)), (g, "g", (B, T, H, dk)),
@@ -144,16 +165,28 @@ def gdr2_fwd(q, k, v, g, b, w, h0=None, *, chunk=64, save_for_bwd=False, ws=None
     ht = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device) if output_final_state else None
     if ws is None:
         ws = workspace(B, T, H, dk, dv, dt, save_for_bwd, q.device)
-    st = lib.gdr2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(h0), _ptr(o), _ptr(ht),
-                      B, T, H, dk, dv, chunk, dt, int(bool(save_for_bwd)), _ptr(ws), ws.numel(), _stream(stream),
-                      stage_events)
-    _raise(st, "gdr2_fwd")
+    tail = (_ptr(h0), _ptr(o), _ptr(ht), B, T, H, dk, dv, chunk, dt, int(bool(save_for_bwd)), _ptr(ws),
+            ws.numel(), _stream(stream), stage_events)
+    if scales is None:
+        st = lib.gdr2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), *tail)
+    else:
+        st = lib.gdr2_fwd_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), *scales, *tail)
+    _raise(st, "gdr2_fwd" if scales is None else "gdr2_fwd_logits")
     return o, ht, ws
 
 
 def gdr2_step(q, k, v, g, b, w, state, *, o=None, stream=None):
     """Recurrent step (decoding): the T tokens of q, k, g, b [B,T,H,dk] and v, w [B,T,H,dv]
     one at a time from ``state`` ([B,H,dk,dv] fp32), which is updated in place. Returns o."""
+    return _step(None, q, k, v, g, b, w, state, o, stream)
+
+
+def gdr2_step_logits(q, k, v, zg, zb, zw, state, *, g_scale=1.0, b_scale=1.0, o=None, stream=None):
+    """Recurrent step with the gates given as logits (activations as gdr2_fwd_logits)."""
+    return _step((g_scale, b_scale), q, k, v, zg, zb, zw, state, o, stream)
+
+
+def _step(scales, q, k, v, g, b, w, state, o, stream):
     lib = load_library()
     B, T, H, dk, dv, dt = _dims(q, v)
     for t, n, shp in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)), (g, "g", (B, T, H, dk)),
@@ -165,9 +198,12 @@ def gdr2_step(q, k, v, g, b, w, state, *, o=None, stream=None):
     if o is None:
         o = torch.empty(B, T, H, dv, dtype=q.dtype, device=q.device)
     _check(o, "o", q.dtype, (B, T, H, dv))
-    st = lib.gdr2_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(state), _ptr(o),
-                       B, T, H, dk, dv, dt, _stream(stream))
-    _raise(st, "gdr2_step")
+    tail = (_ptr(state), _ptr(o), B, T, H, dk, dv, dt, _stream(stream))
+    if scales is None:
+        st = lib.gdr2_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), *tail)
+    else:
+        st = lib.gdr2_step_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), *scales, *tail)
+    _raise(st, "gdr2_step" if scales is None else "gdr2_step_logits")
     return o
 
 
@@ -176,6 +212,20 @@ def gdr2_bwd(q, k, v, g, b, w, h0, dout, dht=None, *, chunk=64, ws=None, fwd_sav
     """Backward pass. Returns a dict with dq, dk, dv, dg, db, dw (input dtype) and dh0 (fp32 or None).
     With fwd_saved=True, ``ws`` must be the workspace of a gdr2_fwd(..., save_for_bwd=True) call on
     the same inputs."""
+    return _bwd(None, q, k, v, g, b, w, h0, dout, dht, chunk, ws, fwd_saved, need_dh0, grads, stream,
+                stage_events)
+
+
+def gdr2_bwd_logits(q, k, v, zg, zb, zw, h0, dout, dht=None, *, g_scale=1.0, b_scale=1.0, chunk=64, ws=None,
+                    fwd_saved=False, need_dh0=True, grads=None, stream=None, stage_events=None):
+    """Backward with the gates given as logits: dg, db, dw of the returned dict are the gradients
+    with respect to zg, zb, zw. With fwd_saved=True, ``ws`` must come from gdr2_fwd_logits on the
+    same inputs and scales."""
+    return _bwd((g_scale, b_scale), q, k, v, zg, zb, zw, h0, dout, dht, chunk, ws, fwd_saved, need_dh0, grads,
+                stream, stage_events)
+
+
+def _bwd(scales, q, k, v, g, b, w, h0, dout, dht, chunk, ws, fwd_saved, need_dh0, grads, stream, stage_events):
     lib = load_library()
     B, T, H, dk, dv, dt = _dims(q, v)
     for t, n, shp in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)), (g, "g", (B, T, H, dk)),
@@ -192,11 +242,14 @@ def gdr2_bwd(q, k, v, g, b, w, h0, dout, dht=None, *, chunk=64, ws=None, fwd_sav
         if fwd_saved:
             raise ValueError("fwd_saved=True needs the forward's workspace")
         ws = workspace(B, T, H, dk, dv, dt, True, q.device)
-    st = lib.gdr2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(h0), _ptr(dout), _ptr(dht),
-                      _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dg"]),
-                      _ptr(grads["db"]), _ptr(grads["dw"]), _ptr(grads["dh0"]), B, T, H, dk, dv, chunk, dt,
-                      int(bool(fwd_saved)), _ptr(ws), ws.numel(), _stream(stream), stage_events)
-    _raise(st, "gdr2_bwd")
+    tail = (_ptr(h0), _ptr(dout), _ptr(dht), _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]),
+            _ptr(grads["dg"]), _ptr(grads["db"]), _ptr(grads["dw"]), _ptr(grads["dh0"]), B, T, H, dk, dv, chunk,
+            dt, int(bool(fwd_saved)), _ptr(ws), ws.numel(), _stream(stream), stage_events)
+    if scales is None:
+        st = lib.gdr2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), *tail)
+    else:
+        st = lib.gdr2_bwd_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), *scales, *tail)
+    _raise(st, "gdr2_bwd" if scales is None else "gdr2_bwd_logits")
     return grads
 
 

@@ -35,6 +35,11 @@ gdr2::Layout layout_for(int B, int T, int H, int dk, int dv, int dtype) {
     return gdr2::make_layout((long long)B * H * NT, dk, dv, esize(dtype));
 }
 
+// gate scales of the logit entry points: finite, g_scale > 0, 0 < b_scale <= 2
+bool scales_ok(float g_scale, float b_scale) {
+    return g_scale > 0.f && g_scale <= 3.0e38f && b_scale > 0.f && b_scale <= 2.f;
+}
+
 void fill_common(gdr2::Args& a, int B, int T, int H, int dk, int dv, int dtype, void* ws) {
     a.B = B;
     a.T = T;
@@ -60,11 +65,16 @@ size_t gdr2_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, 
     return layout_for(B, T, H, dk, dv, dtype).train_bytes;
 }
 
-int gdr2_fwd(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+}  // extern "C"
+
+namespace {
+
+int fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
              const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk, int dtype,
              int save_for_bwd, void* workspace, size_t workspace_bytes, void* stream,
-             void* const* stage_events) {
+             void* const* stage_events, int act, float g_scale, float b_scale) {
     if (!q || !k || !v || !g || !b || !w || !o) return GDR2_ERR_NULL;
+    if (act && !scales_ok(g_scale, b_scale)) return GDR2_ERR_VALUE;
     int st = check_shape(B, T, H, dk, dv, chunk, dtype);
     if (st != GDR2_OK) return st;
     const void* ptrs[] = {q, k, v, g, b, w, h0, o, ht, workspace};
@@ -76,19 +86,21 @@ int gdr2_fwd(const void* q, const void* k, const void* v, const void* g, const v
     gdr2::Args a = {};
     a.q = q; a.k = k; a.v = v; a.g = g; a.b = b; a.w = w;
     a.h0 = h0; a.o = o; a.ht = ht;
+    a.act = act; a.g_scale = g_scale; a.b_scale = b_scale;
     fill_common(a, B, T, H, dk, dv, dtype, workspace);
     a.events = (hipEvent_t const*)stage_events;
     hipError_t e = gdr2::launch_fwd(a, dtype == GDR2_DTYPE_BF16, save_for_bwd != 0, (hipStream_t)stream);
     return e == hipSuccess ? GDR2_OK : GDR2_ERR_HIP;
 }
 
-int gdr2_bwd(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+int bwd_impl(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
              const float* h0, const void* dout, const float* dht, void* dq, void* dk_, void* dv_, void* dg,
              void* db, void* dw, float* dh0, int B, int T, int H, int dk, int dv, int chunk, int dtype,
              int fwd_saved, void* workspace, size_t workspace_bytes, void* stream,
-             void* const* stage_events) {
+             void* const* stage_events, int act, float g_scale, float b_scale) {
     if (!q || !k || !v || !g || !b || !w || !dout || !dq || !dk_ || !dv_ || !dg || !db || !dw)
         return GDR2_ERR_NULL;
+    if (act && !scales_ok(g_scale, b_scale)) return GDR2_ERR_VALUE;
     int st = check_shape(B, T, H, dk, dv, chunk, dtype);
     if (st != GDR2_OK) return st;
     const void* ptrs[] = {q, k, v, g, b, w, h0, dout, dht, dq, dk_, dv_, dg, db, dw, dh0, workspace};
@@ -102,6 +114,7 @@ int gdr2_bwd(const void* q, const void* k, const void* v, const void* g, const v
     a.h0 = h0; a.dout = dout; a.dht = dht;
     a.dq = dq; a.dk = dk_; a.dv = dv_; a.dg = dg; a.db = db; a.dw = dw; a.dh0 = dh0;
     a.o = nullptr; a.ht = nullptr;
+    a.act = act; a.g_scale = g_scale; a.b_scale = b_scale;
     fill_common(a, B, T, H, dk, dv, dtype, workspace);
     const bool bf = dtype == GDR2_DTYPE_BF16;
     hipError_t e = hipSuccess;
@@ -114,9 +127,11 @@ int gdr2_bwd(const void* q, const void* k, const void* v, const void* g, const v
     return e == hipSuccess ? GDR2_OK : GDR2_ERR_HIP;
 }
 
-int gdr2_step(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
-              float* state, void* o, int B, int T, int H, int dk, int dv, int dtype, void* stream) {
+int step_impl(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+              float* state, void* o, int B, int T, int H, int dk, int dv, int dtype, void* stream, int act,
+              float g_scale, float b_scale) {
     if (!q || !k || !v || !g || !b || !w || !state || !o) return GDR2_ERR_NULL;
+    if (act && !scales_ok(g_scale, b_scale)) return GDR2_ERR_VALUE;
     int st = check_shape(B, T, H, dk, dv, 64, dtype);
     if (st != GDR2_OK) return st;
     const void* ptrs[] = {q, k, v, g, b, w, state, o};
@@ -125,9 +140,60 @@ int gdr2_step(const void* q, const void* k, const void* v, const void* g, const 
     gdr2::Args a = {};
     a.q = q; a.k = k; a.v = v; a.g = g; a.b = b; a.w = w;
     a.o = o; a.state = state;
+    a.act = act; a.g_scale = g_scale; a.b_scale = b_scale;
     fill_common(a, B, T, H, dk, dv, dtype, nullptr);
     hipError_t e = gdr2::launch_step(a, dtype == GDR2_DTYPE_BF16, (hipStream_t)stream);
     return e == hipSuccess ? GDR2_OK : GDR2_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr2_fwd(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+             const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+             int save_for_bwd, void* workspace, size_t workspace_bytes, void* stream,
+             void* const* stage_events) {
+    return fwd_impl(q, k, v, g, b, w, h0, o, ht, B, T, H, dk, dv, chunk, dtype, save_for_bwd, workspace,
+                    workspace_bytes, stream, stage_events, 0, 1.f, 1.f);
+}
+
+int gdr2_fwd_logits(const void* q, const void* k, const void* v, const void* zg, const void* zb, const void* zw,
+                    float g_scale, float b_scale, const float* h0, void* o, float* ht, int B, int T, int H,
+                    int dk, int dv, int chunk, int dtype, int save_for_bwd, void* workspace,
+                    size_t workspace_bytes, void* stream, void* const* stage_events) {
+    return fwd_impl(q, k, v, zg, zb, zw, h0, o, ht, B, T, H, dk, dv, chunk, dtype, save_for_bwd, workspace,
+                    workspace_bytes, stream, stage_events, 1, g_scale, b_scale);
+}
+
+int gdr2_bwd(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+             const float* h0, const void* dout, const float* dht, void* dq, void* dk_, void* dv_, void* dg,
+             void* db, void* dw, float* dh0, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+             int fwd_saved, void* workspace, size_t workspace_bytes, void* stream,
+             void* const* stage_events) {
+    return bwd_impl(q, k, v, g, b, w, h0, dout, dht, dq, dk_, dv_, dg, db, dw, dh0, B, T, H, dk, dv, chunk,
+                    dtype, fwd_saved, workspace, workspace_bytes, stream, stage_events, 0, 1.f, 1.f);
+}
+
+int gdr2_bwd_logits(const void* q, const void* k, const void* v, const void* zg, const void* zb,
+                    const void* zw, float g_scale, float b_scale, const float* h0, const void* dout,
+                    const float* dht, void* dq, void* dk_, void* dv_, void* dzg, void* dzb, void* dzw,
+                    float* dh0, int B, int T, int H, int dk, int dv, int chunk, int dtype, int fwd_saved,
+                    void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events) {
+    return bwd_impl(q, k, v, zg, zb, zw, h0, dout, dht, dq, dk_, dv_, dzg, dzb, dzw, dh0, B, T, H, dk, dv,
+                    chunk, dtype, fwd_saved, workspace, workspace_bytes, stream, stage_events, 1, g_scale,
+                    b_scale);
+}
+
+int gdr2_step(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+              float* state, void* o, int B, int T, int H, int dk, int dv, int dtype, void* stream) {
+    return step_impl(q, k, v, g, b, w, state, o, B, T, H, dk, dv, dtype, stream, 0, 1.f, 1.f);
+}
+
+int gdr2_step_logits(const void* q, const void* k, const void* v, const void* zg, const void* zb,
+                     const void* zw, float g_scale, float b_scale, float* state, void* o, int B, int T,
+                     int H, int dk, int dv, int dtype, void* stream) {
+    return step_impl(q, k, v, zg, zb, zw, state, o, B, T, H, dk, dv, dtype, stream, 1, g_scale, b_scale);
 }
 
 const char* gdr2_strerror(int status) {
@@ -139,6 +205,7 @@ const char* gdr2_strerror(int status) {
         case GDR2_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case GDR2_ERR_WORKSPACE: return "workspace is NULL or too small";
         case GDR2_ERR_HIP: return "HIP launch failed";
+        case GDR2_ERR_VALUE: return "gate scale out of range (need g_scale > 0 finite, 0 < b_scale <= 2)";
         default: return "unknown status";
     }
 }

@@ -24,6 +24,9 @@
 //                 dS' (fragment-major) and dY (tiles) per chunk.
 //   k_bwd_intra : one workgroup per chunk, fully parallel; reads the saved S,
 //                 Delta, dS', dY and the inputs, writes dq, dk, dv, dg, db, dw.
+//                 With gates passed as logits (ACT) it activates them where they
+//                 are read and multiplies dg, db, dw by the activations' derivatives
+//                 before they are stored (gradients with respect to the logits).
 #include "gdr2_intra_common.hpp"
 #include "gdr2_kernels.hpp"
 
@@ -108,7 +111,7 @@ __device__ __forceinline__ void undump_tiles(const OT* src, lds_char* dst) {
 
 constexpr int BWD_NW = 8;  // waves per workgroup of the backward intra-chunk kernel
 
-template <class OT, int DK, int DV>
+template <class OT, int DK, int DV, bool ACT>
 __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     using LS = BwdLds<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
@@ -214,6 +217,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         const int ch0 = 16 * (wv + NW * ac) + 4 * lq;
         float gv[4][4], g0[4][4], ge[4][4];
         rows4(vG, ch0, gv);
+        if (ACT) activate_rows<OT, GATE_G>(gv, nvalid, a.g_scale, a.b_scale);
         gamma_scan(gv, gam[ac], g0, ge);
         RowExp rx;
         row_exps<DK>(sF, ch0, g0, ge, rx);
@@ -329,8 +333,10 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         RW dvv, dww;
 #pragma unroll
         for (int e = 0; e < WV; ++e) {
-            dvv[e] = to_ot<OT>(to_f(dy[e]) * to_f(rw[i][e]));
-            dww[e] = to_ot<OT>(to_f(dy[e]) * to_f(rv[i][e]));
+            const float w = ACT ? gate_sigmoid<OT>(to_f(rw[i][e])) : to_f(rw[i][e]);
+            const float dwdz = ACT ? w * (1.f - w) : 1.f;  // gradient through the write gate's sigmoid
+            dvv[e] = to_ot<OT>(to_f(dy[e]) * w);
+            dww[e] = to_ot<OT>(to_f(dy[e]) * to_f(rv[i][e]) * dwdz);
         }
         if (r < nvalid) {
             *(RW*)((OT*)a.dv + rowk0 * DV + (size_t)r * rsv + ch) = dvv;
@@ -356,6 +362,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         rows4(vQ, ch0, qv);
         rows4(vK, ch0, kv);
         rows4(vB, ch0, bv);
+        if (ACT) activate_rows<OT, GATE_B>(bv, nvalid, a.g_scale, a.b_scale);
         scaled_factors_from<OT, DK, false>(qv, kv, bv, ch0, gam[ac], g0, ge, sXA, sXM, sY, nullptr, nullptr, nullptr);
     }
     __syncthreads();
@@ -405,6 +412,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         rows4(vQ, ch0, qv);
         rows4(vK, ch0, kv);
         rows4(vB, ch0, bv);
+        if (ACT) activate_rows<OT, GATE_B>(bv, nvalid, a.g_scale, a.b_scale);
         float dgam[4][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -420,6 +428,11 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
                 db[i] = gbk * kv[t][i];
                 dk[i] = gbk * bv[t][i] + e2 * Pk[ac][t][i] + dmd * qv[t][i];
                 dgam[t][i] = qv[t][i] * dq[i] + 2.f * bv[t][i] * db[i] - kv[t][i] * dk[i];
+            }
+            if (ACT) {  // db through the erase gate's scaled sigmoid: b_scale s (1 - s), s = b / b_scale
+                const float rb = 1.f / a.b_scale;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) db[i] *= bv[t][i] * (1.f - bv[t][i] * rb);
             }
             // into the staged q, k, b tiles (this wave alone reads and writes these columns)
             const int o = vQ.off(r, ch0);
@@ -444,11 +457,22 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
                 pre[t][i] = x;
                 tot[i] = row_bcast<15>(x);
             }
+        float gf[4][4];  // ACT: d g / d z = -g_scale sigmoid(z), from the logits still in sG
+        if (ACT) {
+            rows4(vG, ch0, gf);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gf[t][i] = -a.g_scale * gate_sigmoid<OT>(gf[t][i]);
+        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             float dg[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dg[i] = tot[i] - pre[t][i] + dgam[t][i];
+            for (int i = 0; i < 4; ++i) {
+                dg[i] = tot[i] - pre[t][i] + dgam[t][i];
+                if (ACT) dg[i] *= gf[t][i];
+            }
             lds_put4<OT>(sG + vG.off(16 * t + li, ch0), dg);
         }
     }
@@ -473,7 +497,7 @@ size_t bwd_intra_lds_bytes(int DK, int DV, int esz) {
 template <class OT, int DK, int DV>
 static hipError_t launch_bwd_t(const Args& a, hipStream_t stream) {
     const size_t lds = BwdLds<OT, DK, DV>::BYTES;
-    auto intra = k_bwd_intra<OT, DK, DV>;
+    auto intra = a.act ? k_bwd_intra<OT, DK, DV, true> : k_bwd_intra<OT, DK, DV, false>;
     hipError_t e = hipFuncSetAttribute((const void*)intra, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     if ((e = mark(a, 0, stream)) != hipSuccess) return e;

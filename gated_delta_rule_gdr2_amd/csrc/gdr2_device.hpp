@@ -95,6 +95,30 @@ __device__ __forceinline__ typename Frag<OT>::type frag_of(const f32x4& d0, cons
 
 // ----------------------------------------------------------------------------- 4-element vectors
 // load / store 4 consecutive elements (8 B for bf16, 16 B for fp32); p must be aligned
+// Gate activations, for gates passed as logits. The erase gate b and the write gate w
+// are sigmoids of their own projections (Gated DeltaNet-2 record LIT-802, "Key
+// takeaways", first bullet), b scaled by b_scale > 0 (2: the [0, 2] erase range of the
+// Table 5 ablation); the log-decay is g = -g_scale * softplus(z), which keeps
+// exp g in (0, 1). The fp32 operand path takes the accurate library exp / log1p, the bf16
+// path the hardware approximations (their error is far below bf16 rounding).
+template <class OT>
+__device__ __forceinline__ float gate_sigmoid(float z) {
+    if constexpr (sizeof(OT) == 4) return 1.f / (1.f + expf(-z));
+    else return __builtin_amdgcn_rcpf(1.f + __expf(-z));
+}
+template <class OT>
+__device__ __forceinline__ float gate_softplus(float z) {
+    if constexpr (sizeof(OT) == 4) return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
+    else return fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z)));
+}
+enum GateKind { GATE_G, GATE_B, GATE_W };
+template <class OT, int KIND>
+__device__ __forceinline__ float gate_act(float z, float g_scale, float b_scale) {
+    if constexpr (KIND == GATE_G) return -g_scale * gate_softplus<OT>(z);
+    else if constexpr (KIND == GATE_B) return b_scale * gate_sigmoid<OT>(z);
+    else return gate_sigmoid<OT>(z);
+}
+
 __device__ __forceinline__ void ld4(const bf16* p, float out[4]) {
     bf16x4 v = *(const bf16x4*)p;
 #pragma unroll

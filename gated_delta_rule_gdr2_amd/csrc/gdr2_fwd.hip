@@ -20,7 +20,8 @@
 // state chains (gdr2_chain.hip): Wm, Kd, Qg, M and (training) T as swizzled
 // tiles, U as accumulator tiles, exp(gam_C). Phases reuse LDS (A over the
 // query factors, T over the key factors once each is dead) so that two
-// workgroups fit on one compute unit.
+// workgroups fit on one compute unit. With gates passed as logits (ACT) the gates are
+// activated in phase 1, as they are converted to fp32; nothing else changes.
 #include "gdr2_intra_common.hpp"
 #include "gdr2_kernels.hpp"
 
@@ -96,7 +97,7 @@ __device__ __forceinline__ void upper_ri(int u, int& R, int& I) {
     I = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
 }
 
-template <class OT, int DK, int DV, bool TRAIN>
+template <class OT, int DK, int DV, bool TRAIN, bool ACT>
 __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
     using LS = FwdLds<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
@@ -162,6 +163,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
                 const int ch0 = GC * (wv + 4 * ai) + W * lq + 4 * hq;
                 float gv[4][4], gam[4][4], g0[4][4], ge[4][4];
                 cvt_rows16<OT>(rg[ai], hq, nvalid, gv);
+                if (ACT) activate_rows<OT, GATE_G>(gv, nvalid, a.g_scale, a.b_scale);
                 gamma_scan(gv, gam, g0, ge);
                 RowExp rx;
                 row_exps<DK>(sF, ch0, g0, ge, rx);
@@ -170,6 +172,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
                 cvt_rows16<OT>(rq[ai], hq, nvalid, qv);
                 cvt_rows16<OT>(rk[ai], hq, nvalid, kv);
                 cvt_rows16<OT>(rb[ai], hq, nvalid, bv);
+                if (ACT) activate_rows<OT, GATE_B>(bv, nvalid, a.g_scale, a.b_scale);
                 scaled_factors_from<OT, DK, true>(qv, kv, bv, ch0, gam, g0, ge, sXA, sXM, sY, qg_out, kd_out, &rx);
             }
         }
@@ -181,6 +184,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
                 float vv[4][4], ww[4][4];
                 cvt_rows16<OT>(rv[ji], hq, nvalid, vv);
                 cvt_rows16<OT>(rw[ji], hq, nvalid, ww);
+                if (ACT) activate_rows<OT, GATE_W>(ww, nvalid, a.g_scale, a.b_scale);
                 x_tile_from<OT, DV>(vv, ww, GC * (wv + 4 * ji) + W * lq + 4 * hq, sX);
             }
         }
@@ -290,7 +294,8 @@ size_t fwd_intra_lds_bytes(int DK, int DV, int esz) {
 template <class OT, int DK, int DV>
 static hipError_t launch_fwd_t(const Args& a, bool train, hipStream_t stream) {
     const size_t lds = FwdLds<OT, DK, DV>::BYTES;
-    auto intra = train ? k_fwd_intra<OT, DK, DV, true> : k_fwd_intra<OT, DK, DV, false>;
+    auto intra = a.act ? (train ? k_fwd_intra<OT, DK, DV, true, true> : k_fwd_intra<OT, DK, DV, false, true>)
+                       : (train ? k_fwd_intra<OT, DK, DV, true, false> : k_fwd_intra<OT, DK, DV, false, false>);
     hipError_t e = hipFuncSetAttribute((const void*)intra, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     if ((e = mark(a, 0, stream)) != hipSuccess) return e;

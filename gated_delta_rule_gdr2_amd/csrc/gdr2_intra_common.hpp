@@ -86,6 +86,20 @@ __device__ __forceinline__ void cvt_rows16(const typename Raw16<OT>::type (&raw)
     }
 }
 
+// gates passed as logits: activate a lane's rows 16 t + li (4 channels each) in place;
+// rows at or past nvalid stay zero (a zero log-decay keeps the chunk's cumulative decay
+// at its last real token)
+template <class OT, int KIND>
+__device__ __forceinline__ void activate_rows(float (&x)[4][4], int nvalid, float g_scale, float b_scale) {
+    const int li = lane_id() & 15;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const bool ok = 16 * t + li < nvalid;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[t][i] = ok ? gate_act<OT, KIND>(x[t][i], g_scale, b_scale) : 0.f;
+    }
+}
+
 template <class OT>
 __device__ __forceinline__ void lds_put4(lds_char* p, const float v[4]) {
     if constexpr (sizeof(OT) == 2) {

@@ -18,6 +18,11 @@ struct Args {
     void *dq, *dk, *dv, *dg, *db, *dw;
     float* dh0;         // [B, H, DK, DV] or null
     float* state;       // recurrent step: [B, H, DK, DV], read and overwritten
+    // gates: act = 0 -> g, b, w are the gates themselves; act = 1 -> they are logits,
+    // g = -g_scale softplus(g), b = b_scale sigmoid(b), w = sigmoid(w), and the backward
+    // writes the gradients with respect to the logits into dg, db, dw
+    int act;
+    float g_scale, b_scale;
     char* ws;           // workspace base
     Layout L;
     int B, T, H, NT;

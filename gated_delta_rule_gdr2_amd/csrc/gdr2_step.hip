@@ -13,6 +13,7 @@
 // vectors (k, b*k, q, exp g) and the slice's v, w are staged in LDS (the next token's
 // are loaded while this one is computed); the two sums over the key axis (u and o) are
 // in-lane over the lane's rows and then over the 8 row groups with lane shuffles.
+// Gates passed as logits (ACT) are activated as they are staged.
 #include "gdr2_device.hpp"
 #include "gdr2_kernels.hpp"
 
@@ -28,7 +29,7 @@ __device__ __forceinline__ f32x4 xor_sum_rows(f32x4 x) {  // sum over lanes l ^ 
     return x;
 }
 
-template <class OT, int DK, int DV>
+template <class OT, int DK, int DV, bool ACT>
 __global__ __launch_bounds__(128) void k_step(Args a) {
     constexpr int NI = DK / 8;  // state rows per lane
     __shared__ float sk[2][4][DK];             // per token: k, b*k, q, exp(g)
@@ -63,14 +64,16 @@ __global__ __launch_bounds__(128) void k_step(Args a) {
     for (int t = 0; t < a.T; ++t) {
         const int p = t & 1;
         if (tid < DK) {
+            const float b = ACT ? gate_act<OT, GATE_B>(x[1], a.g_scale, a.b_scale) : x[1];
+            const float g = ACT ? gate_act<OT, GATE_G>(x[3], a.g_scale, a.b_scale) : x[3];
             sk[p][0][tid] = x[0];
-            sk[p][1][tid] = x[1] * x[0];
+            sk[p][1][tid] = b * x[0];
             sk[p][2][tid] = x[2];
-            sk[p][3][tid] = __expf(x[3]);
+            sk[p][3][tid] = __expf(g);
         }
         if (tid < STEP_COLS) {
             sv[p][0][tid] = x[4];
-            sv[p][1][tid] = x[5];
+            sv[p][1][tid] = ACT ? gate_act<OT, GATE_W>(x[5], a.g_scale, a.b_scale) : x[5];
         }
         __syncthreads();  // token t staged; token t - 1's buffer (the other one) is free
         if (t + 1 < a.T) load(t + 1, x);
@@ -108,8 +111,11 @@ __global__ __launch_bounds__(128) void k_step(Args a) {
 
 template <class OT, int DK, int DV>
 static hipError_t launch_step_t(const Args& a, hipStream_t stream) {
-    hipLaunchKernelGGL((k_step<OT, DK, DV>), dim3((unsigned)(a.B * a.H * (DV / STEP_COLS))), dim3(128), 0, stream,
-                       a);
+    const dim3 grid((unsigned)(a.B * a.H * (DV / STEP_COLS)));
+    if (a.act)
+        hipLaunchKernelGGL((k_step<OT, DK, DV, true>), grid, dim3(128), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_step<OT, DK, DV, false>), grid, dim3(128), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -82,12 +82,17 @@ def _softplus(x):
     return np.logaddexp(0.0, x)
 
 
-def make_inputs(wl: Workload, device="cpu", **overrides) -> dict:
+def make_inputs(wl: Workload, device="cpu", gates="act", **overrides) -> dict:
     """Draw the workload's tensors. Returns torch tensors on ``device``:
     q, k, g, b [B,T,H,DK]; v, w [B,T,H,DV] in the working dtype; h0 [B,H,DK,DV]
-    fp32 or None; do [B,T,H,DV] in the working dtype (None for fwd-only)."""
+    fp32 or None; do [B,T,H,DV] in the working dtype (None for fwd-only).
+    gates="logits": instead of g, b, w the dict holds the normal draws they are made
+    from, zg, zb, zw (zb and zw with their means b_mu, w_mu added), for the entry
+    points that take the gates as logits with scales g_scale, b_scale."""
     if overrides:
         wl = replace(wl, **overrides)
+    if gates not in ("act", "logits") or (gates == "logits" and wl.tied):
+        raise ValueError("gates must be 'act' or 'logits' (logits: untied gates only)")
     rng = np.random.default_rng(wl.seed)
     B, T, H, DK, DV = wl.B, wl.T, wl.H, wl.DK, wl.DV
     q = rng.standard_normal((B, T, H, DK))
@@ -95,14 +100,17 @@ def make_inputs(wl: Workload, device="cpu", **overrides) -> dict:
     k = rng.standard_normal((B, T, H, DK))
     k /= np.linalg.norm(k, axis=-1, keepdims=True)
     v = rng.standard_normal((B, T, H, DV))
-    g = -_softplus(rng.standard_normal((B, T, H, DK))) * wl.g_scale
+    zg = rng.standard_normal((B, T, H, DK))
+    g = -_softplus(zg) * wl.g_scale
     if wl.tied:
         beta = _sigmoid(rng.standard_normal((B, T, H, 1)))
         b = np.broadcast_to(beta, (B, T, H, DK)).copy()
         w = np.broadcast_to(beta, (B, T, H, DV)).copy()
     else:
-        b = wl.b_scale * _sigmoid(rng.standard_normal((B, T, H, DK)) + wl.b_mu)
-        w = _sigmoid(rng.standard_normal((B, T, H, DV)) + wl.w_mu)
+        zb = rng.standard_normal((B, T, H, DK)) + wl.b_mu
+        b = wl.b_scale * _sigmoid(zb)
+        zw = rng.standard_normal((B, T, H, DV)) + wl.w_mu
+        w = _sigmoid(zw)
     h0 = rng.standard_normal((B, H, DK, DV)) * wl.h0_std if wl.h0_std > 0 else None
     do = rng.standard_normal((B, T, H, DV)) if wl.backward else None
 
@@ -113,6 +121,9 @@ def make_inputs(wl: Workload, device="cpu", **overrides) -> dict:
             return None
         return torch.from_numpy(np.ascontiguousarray(x)).to(dtype).to(device)
 
+    if gates == "logits":
+        return dict(q=cast(q), k=cast(k), v=cast(v), zg=cast(zg), zb=cast(zb), zw=cast(zw),
+                    h0=cast(h0, torch.float32), do=cast(do))
     return dict(q=cast(q), k=cast(k), v=cast(v), g=cast(g), b=cast(b), w=cast(w),
                 h0=cast(h0, torch.float32), do=cast(do))
 

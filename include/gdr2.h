@@ -11,11 +11,12 @@
  *
  * b_t is the channel-wise erase gate on the key axis, w_t the channel-wise
  * write gate on the value axis, g_t the channel-wise log-decay on the key axis
- * (alpha_t = exp g_t). The gates arrive already activated and nothing is
- * normalised or scaled inside the operator. The forward pass runs the
- * chunkwise algorithm with the cumulative decay folded into asymmetric erase
- * factors and one shared WY/UT inverse (LIT-802 takeaway 2, App. A); the
- * backward pass is the gate-aware one (App. B).
+ * (alpha_t = exp g_t). gdr2_fwd / gdr2_bwd / gdr2_step take the gates already
+ * activated; the *_logits variants take their logits and activate them inside
+ * the kernels (see below). Nothing is normalised inside the operator. The
+ * forward pass runs the chunkwise algorithm with the cumulative decay folded
+ * into asymmetric erase factors and one shared WY/UT inverse (LIT-802
+ * takeaway 2, App. A); the backward pass is the gate-aware one (App. B).
  *
  * Layouts (all contiguous, row-major, in the element type `dtype`):
  *   q, k, g, b and dq, dk, dg, db : [B][T][H][dk]
@@ -53,7 +54,8 @@ enum gdr2_status {
     GDR2_ERR_UNSUPPORTED = -3, /* dk/dv/chunk/dtype combination not built */
     GDR2_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
     GDR2_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
-    GDR2_ERR_HIP = -6          /* a HIP launch failed */
+    GDR2_ERR_HIP = -6,         /* a HIP launch failed */
+    GDR2_ERR_VALUE = -7        /* a gate scale is out of range (*_logits entry points) */
 };
 
 /* Bytes of workspace gdr2_fwd needs. save_for_bwd = 1 sizes it for a later
@@ -98,7 +100,37 @@ int gdr2_bwd(const void* q, const void* k, const void* v, const void* g, const v
 int gdr2_step(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
               float* state, void* o, int B, int T, int H, int dk, int dv, int dtype, void* stream);
 
-/* stage_events (gdr2_fwd and gdr2_bwd): NULL, or an array of hipEvent_t that the call
+/* Gates as logits. The erase and write gates are sigmoids of their own projections
+ * ("Gated DeltaNet-2", anthology record LIT-802, "Key takeaways", first bullet); these
+ * entry points take the projections' outputs (logits) zg, zb, zw (layouts of g, b, w)
+ * and apply, inside the kernels,
+ *     b = b_scale * sigmoid(zb),   w = sigmoid(zw),   g = -g_scale * softplus(zg),
+ * so that no separate elementwise pass over the gates is needed. b_scale = 1 is the
+ * plain erase gate, b_scale = 2 the widened [0, 2] erase range of the paper's Table 5
+ * ablation; 0 < b_scale <= 2. The log-decay parametrisation (any g_scale > 0, finite)
+ * keeps the decay exp g in (0, 1); the pages leave it open and this is the reading
+ * taken. The backward variant writes dL/dzg, dL/dzb, dL/dzw into dzg, dzb, dzw (the
+ * other outputs as gdr2_bwd). Everything else -- layouts, dtypes, workspace (the same
+ * size functions), ownership, events, errors -- is as for gdr2_fwd / gdr2_bwd /
+ * gdr2_step; a scale out of range returns GDR2_ERR_VALUE and enqueues nothing.
+ * A gdr2_bwd_logits(..., fwd_saved = 1) must follow gdr2_fwd_logits with the same
+ * logits and scales. */
+int gdr2_fwd_logits(const void* q, const void* k, const void* v, const void* zg, const void* zb,
+                    const void* zw, float g_scale, float b_scale, const float* h0, void* o, float* ht,
+                    int B, int T, int H, int dk, int dv, int chunk, int dtype, int save_for_bwd,
+                    void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events);
+
+int gdr2_bwd_logits(const void* q, const void* k, const void* v, const void* zg, const void* zb,
+                    const void* zw, float g_scale, float b_scale, const float* h0, const void* dout,
+                    const float* dht, void* dq, void* dk_, void* dv_, void* dzg, void* dzb, void* dzw,
+                    float* dh0, int B, int T, int H, int dk, int dv, int chunk, int dtype, int fwd_saved,
+                    void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events);
+
+int gdr2_step_logits(const void* q, const void* k, const void* v, const void* zg, const void* zb,
+                     const void* zw, float g_scale, float b_scale, float* state, void* o, int B, int T,
+                     int H, int dk, int dv, int dtype, void* stream);
+
+/* stage_events (gdr2_fwd and gdr2_bwd, and their _logits variants): NULL, or an array of hipEvent_t that the call
  * records on `stream` around its kernels, for per-kernel timing: element 0
  * before the first kernel and element i after the i-th kernel. gdr2_fwd runs
  * 2 kernels (intra-chunk, state chain), so it needs 3 events; gdr2_bwd runs

@@ -12,7 +12,7 @@ import gated_delta_rule_gdr2_amd as g2
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdr2.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_HIP, ERR_VALUE = 0, -1, -2, -3, -4, -5, -6, -7
 
 
 @pytest.fixture(scope="module")
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_strerror(lib):
     assert g2.gdr2_version() >= 100
-    for st in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_HIP):
+    for st in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_HIP, ERR_VALUE):
         assert g2.gdr2_strerror(st) and g2.gdr2_strerror(st) != "unknown status"
     assert g2.gdr2_strerror(-99) == "unknown status"
 
@@ -157,3 +157,51 @@ def test_step_rejects_bad_arguments(lib):
     assert step(lib, T=0) == ERR_SHAPE
     assert step(lib, dk=96) == ERR_UNSUP
     assert step(lib, dk=128, dv=128, dtype=g2.DTYPE_F32) == ERR_UNSUP
+
+
+# ----------------------------------------------------------------------------- gate-logit entry points
+
+def fwd_logits(lib, ptrs=None, gs=1.0, bs=1.0, B=1, T=64, H=1, dk=64, dv=64, ws=FAKE, ws_bytes=1 << 40):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    v = [ctypes.c_void_p(x) for x in p]
+    return lib.gdr2_fwd_logits(*v[:6], gs, bs, *v[6:], B, T, H, dk, dv, 64, g2.DTYPE_BF16, 1,
+                               ctypes.c_void_p(ws), ws_bytes, None, None)
+
+
+def bwd_logits(lib, ptrs=None, gs=1.0, bs=1.0, B=1, T=64, H=1, dk=64, dv=64, ws=FAKE, ws_bytes=1 << 40):
+    p = [FAKE] * 16 if ptrs is None else ptrs
+    v = [ctypes.c_void_p(x) for x in p]
+    return lib.gdr2_bwd_logits(*v[:6], gs, bs, *v[6:], B, T, H, dk, dv, 64, g2.DTYPE_BF16, 1,
+                               ctypes.c_void_p(ws), ws_bytes, None, None)
+
+
+def step_logits(lib, ptrs=None, gs=1.0, bs=1.0, B=1, T=1, H=1, dk=64, dv=64):
+    p = [FAKE] * 8 if ptrs is None else ptrs
+    v = [ctypes.c_void_p(x) for x in p]
+    return lib.gdr2_step_logits(*v[:6], gs, bs, *v[6:], B, T, H, dk, dv, g2.DTYPE_BF16, None)
+
+
+@pytest.mark.parametrize("gs,bs", [(0.0, 1.0), (-1.0, 1.0), (float("nan"), 1.0), (float("inf"), 1.0),
+                                   (1.0, 0.0), (1.0, 2.5), (1.0, float("nan")), (1.0, -1.0)])
+def test_logit_entry_points_reject_bad_scales(lib, gs, bs):
+    assert fwd_logits(lib, gs=gs, bs=bs) == ERR_VALUE
+    assert bwd_logits(lib, gs=gs, bs=bs) == ERR_VALUE
+    assert step_logits(lib, gs=gs, bs=bs) == ERR_VALUE
+
+
+def test_logit_entry_points_validate_like_the_plain_ones(lib):
+    p = [FAKE] * 9
+    p[3] = 0  # zg
+    assert fwd_logits(lib, p) == ERR_NULL
+    p[3] = FAKE + 2
+    assert fwd_logits(lib, p) == ERR_ALIGN
+    assert fwd_logits(lib, dk=96) == ERR_UNSUP
+    assert fwd_logits(lib, ws_bytes=1) == ERR_WS
+    p = [FAKE] * 16
+    p[14] = 0  # dzw
+    assert bwd_logits(lib, p) == ERR_NULL
+    assert bwd_logits(lib, B=0) == ERR_SHAPE
+    p = [FAKE] * 8
+    p[6] = 0  # state
+    assert step_logits(lib, p) == ERR_NULL
+    assert step_logits(lib, dv=32) == ERR_UNSUP
