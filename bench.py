@@ -279,6 +279,83 @@ def decode_step_measurement(torch, g2, reps=50):
                          "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nbytes}}
 
 
+def seg_step_ms(torch, g2, wl, segments, K, stream, x=None):
+    """Median over K event-timed fwd+bwd steps of gdr2_fwd_seg / gdr2_bwd_seg, with the
+    median of each stage (intra-chunk and chain kernels as the library's events split them)."""
+    from gated_delta_rule_gdr2_amd.inputs import make_inputs
+    if x is None:
+        x = {k: (None if v is None else v.cuda()) for k, v in make_inputs(wl).items()}
+    names = ("q", "k", "v", "g", "b", "w")
+    ws = g2.workspace(wl.B, wl.T, wl.H, wl.DK, wl.DV, x["q"].dtype, True, "cuda", segments)
+    grads = {n: torch.empty_like(x[n[1:]]) for n in ("dq", "dk", "dv", "dg", "db", "dw")}
+    hip = HipEvents()
+    evs = hip.create(6 * K)
+    arrs = [((ctypes.c_void_p * 3)(*evs[6 * i:6 * i + 3]), (ctypes.c_void_p * 3)(*evs[6 * i + 3:6 * i + 6]))
+            for i in range(K)]
+
+    def step(i):
+        fe = None if i is None else ctypes.cast(arrs[i][0], ctypes.c_void_p)
+        be = None if i is None else ctypes.cast(arrs[i][1], ctypes.c_void_p)
+        g2.gdr2_fwd_seg(*(x[n] for n in names), x["h0"], segments=segments, save_for_bwd=True, ws=ws,
+                        stream=stream, stage_events=fe)
+        g2.gdr2_bwd_seg(*(x[n] for n in names), x["h0"], x["do"], segments=segments, ws=ws, fwd_saved=True,
+                        grads=grads, need_dh0=x["h0"] is not None, stream=stream, stage_events=be)
+
+    for _ in range(2):
+        step(None)
+    torch.cuda.synchronize()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+
+    def med(a, b):
+        return sorted(hip.elapsed_ms(evs[6 * i + a], evs[6 * i + b]) for i in range(K))[K // 2]
+
+    out = {"segments": segments, "ms_per_step": med(0, 2) + med(3, 5), "fwd_intra": med(0, 1),
+           "fwd_chain": med(1, 2), "bwd_chain": med(3, 4), "bwd_intra": med(4, 5)}
+    hip.destroy(evs)
+    return out
+
+
+def scan_workloads():
+    from dataclasses import replace
+    from gated_delta_rule_gdr2_amd.inputs import WORKLOADS
+    long_wl = WORKLOADS["fwdbwd_bf16_b1h16t16384d128_h0"]
+    return [long_wl, replace(long_wl, H=4, name="fwdbwd_bf16_b1h4t16384d128_h0"),
+            replace(long_wl, H=1, name="fwdbwd_bf16_b1h1t16384d128_h0"), WORKLOADS["fwdbwd_bf16_b2h16t4096d128"]]
+
+
+def scan_sweep(torch, g2, K=10):
+    """Chunk-parallel scan: fwd+bwd step time against the segment count on the long-sequence
+    workload, the same with 4 and 1 heads, and the training shape. One JSON line each."""
+    from gated_delta_rule_gdr2_amd.inputs import make_inputs
+    stream = torch.cuda.current_stream()
+    for wl in scan_workloads():
+        x = {k: (None if v is None else v.cuda()) for k, v in make_inputs(wl).items()}
+        auto = next(s for s in range(1, 33) if g2.gdr2_seg_workspace_bytes(
+            wl.B, wl.T, wl.H, wl.DK, wl.DV, 64, s, g2.DTYPE_BF16, True) ==
+            g2.gdr2_bwd_workspace_bytes(wl.B, wl.T, wl.H, wl.DK, wl.DV, 64, g2.DTYPE_BF16))
+        for segments in (1, 2, 4, 8, 16, 32):
+            r = seg_step_ms(torch, g2, wl, segments, K, stream, x)
+            r.update({"workload": wl.name, "automatic_segments": auto})
+            print(json.dumps(r), flush=True)
+        del x
+
+
+def chain_scan_measurement(torch, g2, K, stream):
+    """The long-sequence workload with 4 heads instead of 16 (32 chain workgroups): fwd+bwd
+    step with the chains walked whole, and with the segment count the plain entry points
+    pick."""
+    wl = scan_workloads()[1]
+    from gated_delta_rule_gdr2_amd.inputs import make_inputs
+    x = {k: (None if v is None else v.cuda()) for k, v in make_inputs(wl).items()}
+    one = seg_step_ms(torch, g2, wl, 1, K, stream, x)
+    best = seg_step_ms(torch, g2, wl, 8, K, stream, x)
+    return {"workload": wl.name, "ms_per_step_one_segment": one["ms_per_step"],
+            "ms_per_step_8_segments": best["ms_per_step"], "chains_ms_one_segment": one["fwd_chain"] +
+            one["bwd_chain"], "chains_ms_8_segments": best["fwd_chain"] + best["bwd_chain"]}
+
+
 def gate_logits_measurement(torch, g2, wl, K, stream):
     """Fused gate activations: forward+backward steps with the gates passed as logits
     (activated inside the kernels), against the same steps with the activations and their
@@ -340,6 +417,8 @@ def main():
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
                     help="summarise a rocprofv3 run (no GPU needed) into profiles/")
     ap.add_argument("--profile-command", default="", help="the command line recorded with --summarize-profile")
+    ap.add_argument("--scan-sweep", action="store_true",
+                    help="print fwd+bwd step times against the chain segment count (chunk-parallel scan) and exit")
     args = ap.parse_args()
     if args.summarize_profile:
         from gated_delta_rule_gdr2_amd.inputs import HEADLINE
@@ -356,6 +435,10 @@ def main():
     import torch
     import gated_delta_rule_gdr2_amd as g2
     from gated_delta_rule_gdr2_amd.inputs import HEADLINE, WORKLOADS, make_inputs
+
+    if args.scan_sweep:
+        scan_sweep(torch, g2)
+        return
 
     wl = WORKLOADS[args.workload or HEADLINE]
     if not wl.backward:
@@ -450,6 +533,7 @@ def main():
         "ms_per_step_cache_evicted": flushed_ms,
         "decode_step": decode_step_measurement(torch, g2),
         "gate_logits": gate_logits_measurement(torch, g2, wl, K, stream),
+        "chain_scan": chain_scan_measurement(torch, g2, K, stream),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, host)

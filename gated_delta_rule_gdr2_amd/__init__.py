@@ -20,8 +20,9 @@ import os
 import torch
 
 __all__ = ["gdr2_fwd", "gdr2_bwd", "gdr2_step", "gdr2_fwd_logits", "gdr2_bwd_logits", "gdr2_step_logits",
-           "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes", "gdr2_strerror", "gdr2_version",
-           "GDR2Function", "library_path", "load_library"]
+           "gdr2_fwd_seg", "gdr2_bwd_seg", "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes",
+           "gdr2_seg_workspace_bytes", "gdr2_strerror", "gdr2_version", "GDR2Function", "library_path",
+           "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr2.so")
@@ -30,7 +31,8 @@ _lib = None
 DTYPE_F32, DTYPE_BF16 = 0, 1
 _DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 EXPORTED = ["gdr2_fwd", "gdr2_bwd", "gdr2_step", "gdr2_fwd_logits", "gdr2_bwd_logits", "gdr2_step_logits",
-            "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes", "gdr2_strerror", "gdr2_version"]
+            "gdr2_fwd_seg", "gdr2_bwd_seg", "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes",
+            "gdr2_seg_workspace_bytes", "gdr2_strerror", "gdr2_version"]
 
 
 def library_path() -> str:
@@ -64,6 +66,12 @@ def load_library():
     lib.gdr2_bwd_logits.restype = i
     lib.gdr2_step_logits.argtypes = [vp] * 6 + [f, f] + [vp] * 2 + [i] * 6 + [vp]
     lib.gdr2_step_logits.restype = i
+    lib.gdr2_seg_workspace_bytes.argtypes = [i] * 9
+    lib.gdr2_seg_workspace_bytes.restype = sz
+    lib.gdr2_fwd_seg.argtypes = [vp] * 9 + [i] * 9 + [vp, sz, vp, vp]
+    lib.gdr2_fwd_seg.restype = i
+    lib.gdr2_bwd_seg.argtypes = [vp] * 16 + [i] * 9 + [vp, sz, vp, vp]
+    lib.gdr2_bwd_seg.restype = i
     lib.gdr2_strerror.argtypes = [i]
     lib.gdr2_strerror.restype = ctypes.c_char_p
     lib.gdr2_version.argtypes = []
@@ -86,6 +94,11 @@ def gdr2_fwd_workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=DTYPE_BF16, save_f
 
 def gdr2_bwd_workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=DTYPE_BF16) -> int:
     return int(load_library().gdr2_bwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype))
+
+
+def gdr2_seg_workspace_bytes(B, T, H, dk, dv, chunk=64, segments=1, dtype=DTYPE_BF16, save_for_bwd=False) -> int:
+    return int(load_library().gdr2_seg_workspace_bytes(B, T, H, dk, dv, chunk, segments, dtype,
+                                                       int(bool(save_for_bwd))))
 
 
 def _ptr(t):
@@ -124,11 +137,15 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def workspace(B, T, H, dk, dv, dtype, train, device="cuda"):
-    """Allocate a workspace tensor (uint8) big enough for gdr2_fwd(save_for_bwd=train) / gdr2_bwd."""
+def workspace(B, T, H, dk, dv, dtype, train, device="cuda", segments=None):
+    """Allocate a workspace tensor (uint8) big enough for gdr2_fwd(save_for_bwd=train) / gdr2_bwd
+    (segments=None), or for their _seg variants with that many segments."""
     dt = _DT[dtype] if isinstance(dtype, torch.dtype) else dtype
-    n = gdr2_bwd_workspace_bytes(B, T, H, dk, dv, 64, dt) if train else \
-        gdr2_fwd_workspace_bytes(B, T, H, dk, dv, 64, dt, False)
+    if segments is None:
+        n = gdr2_bwd_workspace_bytes(B, T, H, dk, dv, 64, dt) if train else \
+            gdr2_fwd_workspace_bytes(B, T, H, dk, dv, 64, dt, False)
+    else:
+        n = gdr2_seg_workspace_bytes(B, T, H, dk, dv, 64, segments, dt, train)
     if n == 0:
         raise ValueError("unsupported shape/dtype for gdr2: B=%d T=%d H=%d dk=%d dv=%d" % (B, T, H, dk, dv))
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -144,6 +161,14 @@ def gdr2_fwd(q, k, v, g, b, w, h0=None, *, chunk=64, save_for_bwd=False, ws=None
                 stage_events)
 
 
+def gdr2_fwd_seg(q, k, v, g, b, w, h0=None, *, segments, chunk=64, save_for_bwd=False, ws=None, o=None,
+                 output_final_state=True, stream=None, stage_events=None):
+    """gdr2_fwd with the state chains cut into ``segments`` pieces walked in parallel
+    (chunk-parallel scan; see include/gdr2.h). The workspace must be sized for the same segments."""
+    return _fwd(None, q, k, v, g, b, w, h0, chunk, save_for_bwd, ws, o, output_final_state, stream,
+                stage_events, segments)
+
+
 def gdr2_fwd_logits(q, k, v, zg, zb, zw, h0=None, *, g_scale=1.0, b_scale=1.0, chunk=64, save_for_bwd=False,
                     ws=None, o=None, output_final_state=True, stream=None, stage_events=None):
     """Forward pass with the gates given as logits, activated inside the kernels:
@@ -152,7 +177,8 @@ def gdr2_fwd_logits(q, k, v, zg, zb, zw, h0=None, *, g_scale=1.0, b_scale=1.0, c
                 stream, stage_events)
 
 
-def _fwd(scales, q, k, v, g, b, w, h0, chunk, save_for_bwd, ws, o, output_final_state, stream, stage_events):
+def _fwd(scales, q, k, v, g, b, w, h0, chunk, save_for_bwd, ws, o, output_final_state, stream, stage_events,
+         segments=None):
     lib = load_library()
     B, T, H, dk, dv, dt = _dims(q, v)
     for t, n, shp in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)), (g, "g", (B, T, H, dk)),
@@ -164,9 +190,14 @@ def _fwd(scales, q, k, v, g, b, w, h0, chunk, save_for_bwd, ws, o, output_final_
     _check(o, "o", q.dtype, (B, T, H, dv))
     ht = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device) if output_final_state else None
     if ws is None:
-        ws = workspace(B, T, H, dk, dv, dt, save_for_bwd, q.device)
+        ws = workspace(B, T, H, dk, dv, dt, save_for_bwd, q.device, segments)
     tail = (_ptr(h0), _ptr(o), _ptr(ht), B, T, H, dk, dv, chunk, dt, int(bool(save_for_bwd)), _ptr(ws),
             ws.numel(), _stream(stream), stage_events)
+    if segments is not None:
+        st = lib.gdr2_fwd_seg(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), *tail[:9], segments,
+                              *tail[9:])
+        _raise(st, "gdr2_fwd_seg")
+        return o, ht, ws
     if scales is None:
         st = lib.gdr2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), *tail)
     else:
@@ -216,6 +247,14 @@ def gdr2_bwd(q, k, v, g, b, w, h0, dout, dht=None, *, chunk=64, ws=None, fwd_sav
                 stage_events)
 
 
+def gdr2_bwd_seg(q, k, v, g, b, w, h0, dout, dht=None, *, segments, chunk=64, ws=None, fwd_saved=False,
+                 need_dh0=True, grads=None, stream=None, stage_events=None):
+    """gdr2_bwd with the reverse state chains cut into ``segments`` pieces (chunk-parallel scan).
+    With fwd_saved=True, ``ws`` must come from gdr2_fwd_seg(save_for_bwd=True) with the same segments."""
+    return _bwd(None, q, k, v, g, b, w, h0, dout, dht, chunk, ws, fwd_saved, need_dh0, grads, stream,
+                stage_events, segments)
+
+
 def gdr2_bwd_logits(q, k, v, zg, zb, zw, h0, dout, dht=None, *, g_scale=1.0, b_scale=1.0, chunk=64, ws=None,
                     fwd_saved=False, need_dh0=True, grads=None, stream=None, stage_events=None):
     """Backward with the gates given as logits: dg, db, dw of the returned dict are the gradients
@@ -225,7 +264,8 @@ def gdr2_bwd_logits(q, k, v, zg, zb, zw, h0, dout, dht=None, *, g_scale=1.0, b_s
                 stream, stage_events)
 
 
-def _bwd(scales, q, k, v, g, b, w, h0, dout, dht, chunk, ws, fwd_saved, need_dh0, grads, stream, stage_events):
+def _bwd(scales, q, k, v, g, b, w, h0, dout, dht, chunk, ws, fwd_saved, need_dh0, grads, stream, stage_events,
+         segments=None):
     lib = load_library()
     B, T, H, dk, dv, dt = _dims(q, v)
     for t, n, shp in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)), (g, "g", (B, T, H, dk)),
@@ -241,10 +281,15 @@ def _bwd(scales, q, k, v, g, b, w, h0, dout, dht, chunk, ws, fwd_saved, need_dh0
     if ws is None:
         if fwd_saved:
             raise ValueError("fwd_saved=True needs the forward's workspace")
-        ws = workspace(B, T, H, dk, dv, dt, True, q.device)
+        ws = workspace(B, T, H, dk, dv, dt, True, q.device, segments)
     tail = (_ptr(h0), _ptr(dout), _ptr(dht), _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]),
             _ptr(grads["dg"]), _ptr(grads["db"]), _ptr(grads["dw"]), _ptr(grads["dh0"]), B, T, H, dk, dv, chunk,
             dt, int(bool(fwd_saved)), _ptr(ws), ws.numel(), _stream(stream), stage_events)
+    if segments is not None:
+        st = lib.gdr2_bwd_seg(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), *tail[:16], segments,
+                              *tail[16:])
+        _raise(st, "gdr2_bwd_seg")
+        return grads
     if scales is None:
         st = lib.gdr2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), *tail)
     else:

@@ -30,9 +30,35 @@ int check_shape(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
     return GDR2_OK;
 }
 
-gdr2::Layout layout_for(int B, int T, int H, int dk, int dv, int dtype) {
+// Segments of the state chains: `segments` requested (>= 1) -> chunks per segment and
+// the number of (non-empty) segments actually used.
+void seg_plan(int T, int segments, int& nseg, int& seg_len) {
+    const int NT = (T + 63) / 64;
+    const int req = segments < NT ? segments : NT;
+    seg_len = (NT + req - 1) / req;
+    nseg = (NT + seg_len - 1) / seg_len;
+}
+
+// The segment count gdr2_fwd / gdr2_bwd use. The chains run one workgroup per (sequence,
+// 16 value columns) and their throughput is set by the operand traffic of all walks
+// together, which the scan roughly triples, so it pays only when the walks are too few
+// to fill the 256 compute units: up to 128 chain workgroups, 256 / (workgroups)
+// segments, at most 8, each of at least 8 chunks.
+int auto_segments(int B, int T, int H, int dv) {
+    const long long wgs = (long long)B * H * (dv / 16);
+    const int NT = (T + 63) / 64;
+    if (wgs < 1 || wgs > 128) return 1;
+    int n = (int)(256 / wgs);
+    if (n > 8) n = 8;
+    if (n > NT / 8) n = NT / 8;
+    return n < 1 ? 1 : n;
+}
+
+gdr2::Layout layout_for(int B, int T, int H, int dk, int dv, int dtype, int segments, bool train) {
     const long long NT = (T + 63) / 64;
-    return gdr2::make_layout((long long)B * H * NT, dk, dv, esize(dtype));
+    int nseg, seg_len;
+    seg_plan(T, segments, nseg, seg_len);
+    return gdr2::make_layout((long long)B * H * NT, dk, dv, esize(dtype), (long long)B * H, nseg, train);
 }
 
 // gate scales of the logit entry points: finite, g_scale > 0, 0 < b_scale <= 2
@@ -40,13 +66,15 @@ bool scales_ok(float g_scale, float b_scale) {
     return g_scale > 0.f && g_scale <= 3.0e38f && b_scale > 0.f && b_scale <= 2.f;
 }
 
-void fill_common(gdr2::Args& a, int B, int T, int H, int dk, int dv, int dtype, void* ws) {
+void fill_common(gdr2::Args& a, int B, int T, int H, int dk, int dv, int dtype, void* ws, int segments = 1,
+                 bool train = true) {
     a.B = B;
     a.T = T;
     a.H = H;
     a.NT = (T + 63) / 64;
     a.NC = (long long)B * H * a.NT;
-    a.L = layout_for(B, T, H, dk, dv, dtype);
+    seg_plan(T, segments, a.nseg, a.seg_len);
+    a.L = layout_for(B, T, H, dk, dv, dtype, segments, train);
     a.ws = (char*)ws;
 }
 
@@ -54,15 +82,21 @@ void fill_common(gdr2::Args& a, int B, int T, int H, int dk, int dv, int dtype, 
 
 extern "C" {
 
+size_t gdr2_seg_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int segments, int dtype,
+                                int save_for_bwd) {
+    if (check_shape(B, T, H, dk, dv, chunk, dtype) != GDR2_OK || segments < 1) return 0;
+    gdr2::Layout L = layout_for(B, T, H, dk, dv, dtype, segments, save_for_bwd != 0);
+    return save_for_bwd ? L.train_bytes : L.fwd_infer_bytes;
+}
+
 size_t gdr2_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype, int save_for_bwd) {
     if (check_shape(B, T, H, dk, dv, chunk, dtype) != GDR2_OK) return 0;
-    gdr2::Layout L = layout_for(B, T, H, dk, dv, dtype);
-    return save_for_bwd ? L.train_bytes : L.fwd_infer_bytes;
+    return gdr2_seg_workspace_bytes(B, T, H, dk, dv, chunk, auto_segments(B, T, H, dv), dtype, save_for_bwd);
 }
 
 size_t gdr2_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
     if (check_shape(B, T, H, dk, dv, chunk, dtype) != GDR2_OK) return 0;
-    return layout_for(B, T, H, dk, dv, dtype).train_bytes;
+    return gdr2_seg_workspace_bytes(B, T, H, dk, dv, chunk, auto_segments(B, T, H, dv), dtype, 1);
 }
 
 }  // extern "C"
@@ -72,22 +106,24 @@ namespace {
 int fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
              const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk, int dtype,
              int save_for_bwd, void* workspace, size_t workspace_bytes, void* stream,
-             void* const* stage_events, int act, float g_scale, float b_scale) {
+             void* const* stage_events, int act, float g_scale, float b_scale, int segments) {
     if (!q || !k || !v || !g || !b || !w || !o) return GDR2_ERR_NULL;
     if (act && !scales_ok(g_scale, b_scale)) return GDR2_ERR_VALUE;
+    if (segments < 0) return GDR2_ERR_VALUE;  // 0: the automatic count
     int st = check_shape(B, T, H, dk, dv, chunk, dtype);
     if (st != GDR2_OK) return st;
+    if (segments == 0) segments = auto_segments(B, T, H, dv);
     const void* ptrs[] = {q, k, v, g, b, w, h0, o, ht, workspace};
     for (const void* p : ptrs)
         if (p && !aligned(p)) return GDR2_ERR_ALIGN;
-    const size_t need = gdr2_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype, save_for_bwd);
+    const size_t need = gdr2_seg_workspace_bytes(B, T, H, dk, dv, chunk, segments, dtype, save_for_bwd);
     if (!workspace || workspace_bytes < need) return GDR2_ERR_WORKSPACE;
 
     gdr2::Args a = {};
     a.q = q; a.k = k; a.v = v; a.g = g; a.b = b; a.w = w;
     a.h0 = h0; a.o = o; a.ht = ht;
     a.act = act; a.g_scale = g_scale; a.b_scale = b_scale;
-    fill_common(a, B, T, H, dk, dv, dtype, workspace);
+    fill_common(a, B, T, H, dk, dv, dtype, workspace, segments, save_for_bwd != 0);
     a.events = (hipEvent_t const*)stage_events;
     hipError_t e = gdr2::launch_fwd(a, dtype == GDR2_DTYPE_BF16, save_for_bwd != 0, (hipStream_t)stream);
     return e == hipSuccess ? GDR2_OK : GDR2_ERR_HIP;
@@ -97,16 +133,18 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* g, const v
              const float* h0, const void* dout, const float* dht, void* dq, void* dk_, void* dv_, void* dg,
              void* db, void* dw, float* dh0, int B, int T, int H, int dk, int dv, int chunk, int dtype,
              int fwd_saved, void* workspace, size_t workspace_bytes, void* stream,
-             void* const* stage_events, int act, float g_scale, float b_scale) {
+             void* const* stage_events, int act, float g_scale, float b_scale, int segments) {
     if (!q || !k || !v || !g || !b || !w || !dout || !dq || !dk_ || !dv_ || !dg || !db || !dw)
         return GDR2_ERR_NULL;
     if (act && !scales_ok(g_scale, b_scale)) return GDR2_ERR_VALUE;
+    if (segments < 0) return GDR2_ERR_VALUE;  // 0: the automatic count
     int st = check_shape(B, T, H, dk, dv, chunk, dtype);
     if (st != GDR2_OK) return st;
+    if (segments == 0) segments = auto_segments(B, T, H, dv);
     const void* ptrs[] = {q, k, v, g, b, w, h0, dout, dht, dq, dk_, dv_, dg, db, dw, dh0, workspace};
     for (const void* p : ptrs)
         if (p && !aligned(p)) return GDR2_ERR_ALIGN;
-    const size_t need = gdr2_bwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype);
+    const size_t need = gdr2_seg_workspace_bytes(B, T, H, dk, dv, chunk, segments, dtype, 1);
     if (!workspace || workspace_bytes < need) return GDR2_ERR_WORKSPACE;
 
     gdr2::Args a = {};
@@ -115,7 +153,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* g, const v
     a.dq = dq; a.dk = dk_; a.dv = dv_; a.dg = dg; a.db = db; a.dw = dw; a.dh0 = dh0;
     a.o = nullptr; a.ht = nullptr;
     a.act = act; a.g_scale = g_scale; a.b_scale = b_scale;
-    fill_common(a, B, T, H, dk, dv, dtype, workspace);
+    fill_common(a, B, T, H, dk, dv, dtype, workspace, segments);
     const bool bf = dtype == GDR2_DTYPE_BF16;
     hipError_t e = hipSuccess;
     a.events = (hipEvent_t const*)stage_events;
@@ -155,7 +193,15 @@ int gdr2_fwd(const void* q, const void* k, const void* v, const void* g, const v
              int save_for_bwd, void* workspace, size_t workspace_bytes, void* stream,
              void* const* stage_events) {
     return fwd_impl(q, k, v, g, b, w, h0, o, ht, B, T, H, dk, dv, chunk, dtype, save_for_bwd, workspace,
-                    workspace_bytes, stream, stage_events, 0, 1.f, 1.f);
+                    workspace_bytes, stream, stage_events, 0, 1.f, 1.f, 0);
+}
+
+int gdr2_fwd_seg(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+                 const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk, int segments,
+                 int dtype, int save_for_bwd, void* workspace, size_t workspace_bytes, void* stream,
+                 void* const* stage_events) {
+    return fwd_impl(q, k, v, g, b, w, h0, o, ht, B, T, H, dk, dv, chunk, dtype, save_for_bwd, workspace,
+                    workspace_bytes, stream, stage_events, 0, 1.f, 1.f, segments < 1 ? -1 : segments);
 }
 
 int gdr2_fwd_logits(const void* q, const void* k, const void* v, const void* zg, const void* zb, const void* zw,
@@ -163,7 +209,7 @@ int gdr2_fwd_logits(const void* q, const void* k, const void* v, const void* zg,
                     int dk, int dv, int chunk, int dtype, int save_for_bwd, void* workspace,
                     size_t workspace_bytes, void* stream, void* const* stage_events) {
     return fwd_impl(q, k, v, zg, zb, zw, h0, o, ht, B, T, H, dk, dv, chunk, dtype, save_for_bwd, workspace,
-                    workspace_bytes, stream, stage_events, 1, g_scale, b_scale);
+                    workspace_bytes, stream, stage_events, 1, g_scale, b_scale, 0);
 }
 
 int gdr2_bwd(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
@@ -172,7 +218,17 @@ int gdr2_bwd(const void* q, const void* k, const void* v, const void* g, const v
              int fwd_saved, void* workspace, size_t workspace_bytes, void* stream,
              void* const* stage_events) {
     return bwd_impl(q, k, v, g, b, w, h0, dout, dht, dq, dk_, dv_, dg, db, dw, dh0, B, T, H, dk, dv, chunk,
-                    dtype, fwd_saved, workspace, workspace_bytes, stream, stage_events, 0, 1.f, 1.f);
+                    dtype, fwd_saved, workspace, workspace_bytes, stream, stage_events, 0, 1.f, 1.f, 0);
+}
+
+int gdr2_bwd_seg(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+                 const float* h0, const void* dout, const float* dht, void* dq, void* dk_, void* dv_, void* dg,
+                 void* db, void* dw, float* dh0, int B, int T, int H, int dk, int dv, int chunk, int segments,
+                 int dtype, int fwd_saved, void* workspace, size_t workspace_bytes, void* stream,
+                 void* const* stage_events) {
+    return bwd_impl(q, k, v, g, b, w, h0, dout, dht, dq, dk_, dv_, dg, db, dw, dh0, B, T, H, dk, dv, chunk,
+                    dtype, fwd_saved, workspace, workspace_bytes, stream, stage_events, 0, 1.f, 1.f,
+                    segments < 1 ? -1 : segments);
 }
 
 int gdr2_bwd_logits(const void* q, const void* k, const void* v, const void* zg, const void* zb,
@@ -182,7 +238,7 @@ int gdr2_bwd_logits(const void* q, const void* k, const void* v, const void* zg,
                     void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events) {
     return bwd_impl(q, k, v, zg, zb, zw, h0, dout, dht, dq, dk_, dv_, dzg, dzb, dzw, dh0, B, T, H, dk, dv,
                     chunk, dtype, fwd_saved, workspace, workspace_bytes, stream, stage_events, 1, g_scale,
-                    b_scale);
+                    b_scale, 0);
 }
 
 int gdr2_step(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
@@ -205,7 +261,8 @@ const char* gdr2_strerror(int status) {
         case GDR2_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case GDR2_ERR_WORKSPACE: return "workspace is NULL or too small";
         case GDR2_ERR_HIP: return "HIP launch failed";
-        case GDR2_ERR_VALUE: return "gate scale out of range (need g_scale > 0 finite, 0 < b_scale <= 2)";
+        case GDR2_ERR_VALUE:
+            return "a scalar argument is out of range (g_scale > 0 finite, 0 < b_scale <= 2, segments >= 1)";
         default: return "unknown status";
     }
 }

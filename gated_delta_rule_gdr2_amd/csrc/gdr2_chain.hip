@@ -32,6 +32,17 @@
 // producers also pull the operands of the chunk PFD steps ahead into L2, with 4-byte
 // DMAs (one cache line per lane) into a scratch word of LDS; the NJ workgroups of a
 // sequence, which share one XCD's L2, split those lines between them.
+//
+// Chunk-parallel scan. The chunk transition is affine in the state, S' = P_c S + H_c
+// with P_c = diag(exp gam_C) - Kd^T Wm and H_c = Kd^T U, so a sequence's chunks can be
+// cut into NSEG segments that are walked at the same time: (1) a summary walk of every
+// segment but the last, from a zero start (segment 0: from h0), gives its end state H,
+// and a walk whose state starts as the identity and whose value input is zero gives its
+// transition P (the product of its P_c); (2) a scan over the segments gives each
+// segment's true start state, X_{k+1} = P_k X_k + H_k; (3) every segment is walked
+// again from its true start, with all outputs. The backward mirrors it in reverse with
+// P_k^T: summaries of the start-state gradient from a zero end gradient (the last
+// segment: from dht), a reverse scan, and the full walks.
 #include "gdr2_device.hpp"
 #include "gdr2_kernels.hpp"
 
@@ -89,6 +100,20 @@ __device__ __forceinline__ void chain_map(int gid, int NS, int NJ, int& s, int& 
         j = gid % NJ;
     }
 }
+
+// One walk of a chain over the chunks c0 .. c0 + n - 1 of a sequence (the backward walks
+// them in reverse). Its state slice is the columns col .. col + 15 of the start and end
+// matrices (row strides ld_start, ld_end).
+struct WalkSpec {
+    int c0, n;
+    const float* start;  // start matrix, or null: start from zero
+    int ld_start;
+    bool ident;          // start from the identity instead (a transition walk)
+    float* end;          // where the end state goes, or null
+    int ld_end;
+    int col;
+    bool noU;            // no value input, U = 0 (a transition walk)
+};
 
 // Store of one wave's 32 state rows of a 16-column slice, transposed through LDS so
 // each lane stores whole 16-byte row pieces.
@@ -267,7 +292,7 @@ __device__ __forceinline__ void fwd_flush(const Args& a, int s, int j, FwdPend<O
 // on exit this wave's new block is in xw (the other copy).
 template <class OT, int DK, int DV, bool TRAIN, bool OUT, int NW>
 __device__ __forceinline__ void fwd_step(int c, const lds_char* buf, f32x4& S0, f32x4& S1, lds_char* stage,
-                                         const lds_char* xr, lds_char* xw, FwdPend<OT, NW>& pd) {
+                                         const lds_char* xr, lds_char* xw, FwdPend<OT, NW>& pd, bool noU) {
     using B = FwdChainBuf<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
     constexpr int TPW = FwdPend<OT, NW>::TPW;
@@ -286,7 +311,14 @@ __device__ __forceinline__ void fwd_step(int c, const lds_char* buf, f32x4& S0, 
 #pragma unroll
         for (int kb = 0; kb < NW; ++kb) WM[t][kb] = lfrag_rowk<OT, OT>(vWM, 16 * t, 32 * kb);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) lds_get4<OT>(buf + B::U + (t * 256 + l * 4) * (int)sizeof(OT), uu[t]);
+    for (int t = 0; t < 4; ++t) {
+        if (noU) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) uu[t][i] = 0.f;
+        } else {
+            lds_get4<OT>(buf + B::U + (t * 256 + l * 4) * (int)sizeof(OT), uu[t]);
+        }
+    }
     if (OUT) {
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
@@ -351,12 +383,12 @@ __device__ __forceinline__ void fwd_step(int c, const lds_char* buf, f32x4& S0, 
 }
 
 template <class OT, int DK, int DV, bool TRAIN, bool OUT, int NW, bool DBUF>
-__device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, lds_char* b0, lds_char* b1, lds_char* xs,
-                                         lds_char* stage_base, lds_char* pfslot) {
+__device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, const WalkSpec& w, lds_char* b0, lds_char* b1,
+                                         lds_char* xs, lds_char* stage_base, lds_char* pfslot) {
     using B = FwdChainBuf<OT, DK, DV>;
     const int wv = wave_id();
-    const int NT = a.NT;
-    const long long base = (long long)s * NT;
+    const int NT = w.n;
+    const long long base = (long long)s * a.NT + w.c0;
     if (wv >= NW) {  // producer
         const Layout& L = a.L;
         const int pi = wv - NW;
@@ -368,8 +400,9 @@ __device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, lds_char* 
                 dma16<CH * DK * sizeof(OT)>(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG, pi);
                 dma16<CH * CH * sizeof(OT)>(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M, pi);
             }
-            dma16<4 * 256 * sizeof(OT)>(a.ws + L.o_u + (cid * L.u + (size_t)j * 4 * 256) * sizeof(OT), buf + B::U,
-                                        pi);
+            if (!w.noU)
+                dma16<4 * 256 * sizeof(OT)>(a.ws + L.o_u + (cid * L.u + (size_t)j * 4 * 256) * sizeof(OT),
+                                            buf + B::U, pi);
             dma4<DK * 4>(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC, pi);
         };
         // prefetch regions: Wm, Kd, U (all slices), exp(gam_C) [, Qg, M]
@@ -397,52 +430,58 @@ __device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, lds_char* 
                 if (v < LK) return qg + v * 128;
                 return m + (v - LK) * 128;
             };
-            prefetch_lines<LINES, NJ>(line, j, pi, pfslot);
+            prefetch_lines<LINES, NJ>(line, j % NJ, pi, pfslot);
         };
         produce<DBUF, prefetch_count<LINES, NJ>()>(NT, b0, b1, G, PF);
         return;
     }
     // compute waves: state rows 32 wv + 4 lq + i (S0) and 32 wv + 16 + 4 lq + i (S1),
-    // column 16 j + li
+    // column w.col + li
     const int l = lane_id(), li = l & 15, lq = l >> 4;
     lds_char* stage = stage_base + wv * RowStore<OT>::BYTES;
-    const size_t r0 = ((size_t)s * DK + 32 * wv + 4 * lq) * DV + 16 * j + li;
+    const int row0 = 32 * wv + 4 * lq, col = w.col + li;
     f32x4 S0, S1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        S0[i] = a.h0 ? a.h0[r0 + (size_t)i * DV] : 0.f;
-        S1[i] = a.h0 ? a.h0[r0 + (size_t)(16 + i) * DV] : 0.f;
+        if (w.ident) {
+            S0[i] = row0 + i == col ? 1.f : 0.f;
+            S1[i] = row0 + 16 + i == col ? 1.f : 0.f;
+        } else {
+            S0[i] = w.start ? w.start[(size_t)(row0 + i) * w.ld_start + col] : 0.f;
+            S1[i] = w.start ? w.start[(size_t)(row0 + 16 + i) * w.ld_start + col] : 0.f;
+        }
     }
     lds_char* xs0 = xs;
     lds_char* xs1 = xs + NW * Xch<OT>::FRAG;
     put_block<OT>(xs0, wv, S0, S1);
     FwdPend<OT, NW> pd;
     pd.c = -1;
+    const int c0 = w.c0;
     if (DBUF) {
         for (int n = 0; n < NT; n += 2) {
             sync_lds();  // A_n
             fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
-            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n, b0, S0, S1, stage, xs0, xs1, pd);
+            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(c0 + n, b0, S0, S1, stage, xs0, xs1, pd, w.noU);
             if (n + 1 >= NT) break;
             sync_lds();  // A_{n+1}
             fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
-            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n + 1, b1, S0, S1, stage, xs1, xs0, pd);
+            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(c0 + n + 1, b1, S0, S1, stage, xs1, xs0, pd, w.noU);
         }
     } else {
         for (int n = 0; n < NT; ++n) {
             sync_lds();  // A_n
             fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
-            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(n, b0, S0, S1, stage, (n & 1) ? xs1 : xs0, (n & 1) ? xs0 : xs1,
-                                                 pd);
+            fwd_step<OT, DK, DV, TRAIN, OUT, NW>(c0 + n, b0, S0, S1, stage, (n & 1) ? xs1 : xs0,
+                                                 (n & 1) ? xs0 : xs1, pd, w.noU);
             sync_lds();  // C_n
         }
     }
     fwd_flush<OT, DK, DV, TRAIN, OUT, NW>(a, s, j, pd);
-    if (a.ht) {
+    if (w.end) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            a.ht[r0 + (size_t)i * DV] = S0[i];
-            a.ht[r0 + (size_t)(16 + i) * DV] = S1[i];
+            w.end[(size_t)(row0 + i) * w.ld_end + col] = S0[i];
+            w.end[(size_t)(row0 + 16 + i) * w.ld_end + col] = S1[i];
         }
     }
 }
@@ -459,14 +498,66 @@ __global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_fwd_chain(Args a) {
     __shared__ __align__(16) char xch[XBYTES];
     __shared__ __align__(16) char stage[SBYTES];
     __shared__ __align__(16) char pfslot[256];  // target of the L2 prefetch DMAs, never read
-    int s, j;
-    chain_map(blockIdx.x, a.B * a.H, NJ, s, j);
+    // one walk per (sequence, segment, slice), with all outputs
+    const int NSEG = a.nseg;
+    int u, j;
+    chain_map(blockIdx.x, a.B * a.H * NSEG, NJ, u, j);
+    const int s = u / NSEG, seg = u % NSEG;
+    const Layout& L = a.L;
+    const size_t sq = (size_t)DK * DV;
+    WalkSpec w;
+    w.c0 = seg * a.seg_len;
+    w.n = min(a.seg_len, a.NT - w.c0);
+    w.start = seg == 0 ? (a.h0 ? a.h0 + s * sq : nullptr)
+                       : (const float*)(a.ws + L.o_segx) + ((size_t)s * NSEG + seg) * L.segx;
+    w.ld_start = DV;
+    w.ident = false;
+    w.end = (seg == NSEG - 1 && a.ht) ? a.ht + s * sq : nullptr;
+    w.ld_end = DV;
+    w.col = 16 * j;
+    w.noU = false;
     if (a.o)
-        fwd_walk<OT, DK, DV, TRAIN, true, NW, DBUF>(a, s, j, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch,
+        fwd_walk<OT, DK, DV, TRAIN, true, NW, DBUF>(a, s, j, w, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch,
                                                     (lds_char*)stage, (lds_char*)pfslot);
     else
-        fwd_walk<OT, DK, DV, TRAIN, false, NW, DBUF>(a, s, j, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch,
+        fwd_walk<OT, DK, DV, TRAIN, false, NW, DBUF>(a, s, j, w, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch,
                                                      (lds_char*)stage, (lds_char*)pfslot);
+}
+
+// Summary walks of the chunk-parallel scan, one per (sequence, segment k < NSEG - 1,
+// slice): value slices j < DV / 16 walk from a zero start (segment 0: from h0) and write
+// the segment's end state H_k; transition slices j >= DV / 16 walk the identity's
+// columns with no value input and write P_k (not needed, and not run, for segment 0).
+template <class OT, int DK, int DV>
+__global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_fwd_chain_sum(Args a) {
+    using B = FwdChainBuf<OT, DK, DV>;
+    constexpr int NW = DK / 32, NJ = DV / 16, NJP = DK / 16;
+    constexpr int XBYTES = Xch<OT>::bytes(NW);
+    constexpr bool DBUF = 2 * B::BYTES + XBYTES + 256 <= LDS_LIMIT;
+    __shared__ __align__(16) char buf0[B::BYTES];
+    __shared__ __align__(16) char buf1[DBUF ? B::BYTES : 16];
+    __shared__ __align__(16) char xch[XBYTES];
+    __shared__ __align__(16) char pfslot[256];  // target of the L2 prefetch DMAs, never read
+    const int NSEG = a.nseg;
+    int u, j;
+    chain_map(blockIdx.x, a.B * a.H * (NSEG - 1), NJ + NJP, u, j);
+    const int s = u / (NSEG - 1), seg = u % (NSEG - 1);
+    const bool trans = j >= NJ;
+    if (trans && seg == 0) return;  // the whole workgroup: segment 0 needs no transition
+    const Layout& L = a.L;
+    const size_t sub = (size_t)s * NSEG + seg;
+    WalkSpec w;
+    w.c0 = seg * a.seg_len;
+    w.n = a.seg_len;  // every segment but the last is full
+    w.ident = trans;
+    w.start = (!trans && seg == 0 && a.h0) ? a.h0 + (size_t)s * DK * DV : nullptr;
+    w.ld_start = DV;
+    w.end = trans ? (float*)(a.ws + L.o_segp) + sub * L.segp : (float*)(a.ws + L.o_segh) + sub * L.segh;
+    w.ld_end = trans ? DK : DV;
+    w.col = 16 * (trans ? j - NJ : j);
+    w.noU = trans;
+    fwd_walk<OT, DK, DV, false, false, NW, DBUF>(a, s, j, w, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch,
+                                                 nullptr, (lds_char*)pfslot);
 }
 
 // ============================================================================ backward chain
@@ -506,7 +597,8 @@ __device__ __forceinline__ void bwd_flush(const Args& a, int s, int j, BwdPend<O
 
 // One chunk step of a compute wave. On entry the gradient blocks of all waves are in
 // xr; on exit this wave's new block is in xw (the other copy).
-template <class OT, int DK, int DV, int NW>
+// SUM: a summary walk -- only the state gradient, no per-chunk outputs.
+template <class OT, int DK, int DV, int NW, bool SUM>
 __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0, f32x4& dS1, lds_char* stage,
                                          const lds_char* xr, lds_char* xw, BwdPend<OT, NW>& pd) {
     using B = BwdChainBuf<OT, DK, DV>;
@@ -516,7 +608,7 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0,
     const LSwz<OT, DK> vKD{buf + B::KD}, vQG{buf + B::QG}, vWM{buf + B::WM};
     const LSwz<OT, CH> vM{buf + B::M}, vT{buf + B::T};
     const LPad<OT> vDO{buf + B::DO, 16};
-    stage_rows<OT>(stage, dS0, dS1, pd.st);  // gradient w.r.t. this chunk's end state
+    if (!SUM) stage_rows<OT>(stage, dS0, dS1, pd.st);  // gradient w.r.t. this chunk's end state
     // Every LDS operand read of the step is issued before the first product (the
     // scheduling fence keeps them together), so the wave waits on LDS latency once.
     FT dSB[NW], KDf[4][NW], Mf[4][2], dOB[2], WMf[2][2], QGf[2][2], Tf[TPW][2];
@@ -540,10 +632,12 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0,
         QGf[0][kb] = lfrag_colk<OT, OT>(vQG, 32 * wv, 32 * kb);
         QGf[1][kb] = lfrag_colk<OT, OT>(vQG, 32 * wv + 16, 32 * kb);
     }
+    if (!SUM) {
 #pragma unroll
-    for (int u = 0; u < TPW; ++u)
+        for (int u = 0; u < TPW; ++u)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) Tf[u][kb] = lfrag_colk<OT, OT>(vT, 16 * (wv * TPW + u), 32 * kb);
+            for (int kb = 0; kb < 2; ++kb) Tf[u][kb] = lfrag_colk<OT, OT>(vT, 16 * (wv * TPW + u), 32 * kb);
+    }
     lds_get4<float>(buf + B::GC + (32 * wv + 4 * lq) * 4, g0);
     lds_get4<float>(buf + B::GC + (32 * wv + 16 + 4 * lq) * 4, g1);
     __builtin_amdgcn_sched_barrier(0);
@@ -578,6 +672,7 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0,
         dS1 = p1 - n1;
     }
     put_block<OT>(xw, wv, dS0, dS1);
+    if (SUM) return;
     // dY = T^T dDelta on this wave's token tiles (for the intra-chunk kernel)
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -589,13 +684,13 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4& dS0,
     pd.c = c;
 }
 
-template <class OT, int DK, int DV, int NW, bool DBUF>
-__device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* b0, lds_char* b1, lds_char* xs,
-                                         lds_char* stage_base, lds_char* pfslot) {
+template <class OT, int DK, int DV, int NW, bool DBUF, bool SUM>
+__device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, const WalkSpec& w, lds_char* b0, lds_char* b1,
+                                         lds_char* xs, lds_char* stage_base, lds_char* pfslot) {
     using B = BwdChainBuf<OT, DK, DV>;
     const int wv = wave_id();
-    const int NT = a.NT, last = NT - 1;
-    const long long base = (long long)s * NT;
+    const int NT = w.n, last = w.c0 + w.n - 1;  // walk index n is chunk last - n
+    const long long base = (long long)s * a.NT;
     if (wv >= NW) {  // producer; walk index n is chunk last - n
         const Layout& L = a.L;
         const int pi = wv - NW;
@@ -610,7 +705,7 @@ __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* 
             dma16<CH * CH * sizeof(OT)>(a.ws + L.o_m + cid * L.m * sizeof(OT), buf + B::M, pi);
             dma16<CH * DK * sizeof(OT)>(a.ws + L.o_wm + cid * L.wm * sizeof(OT), buf + B::WM, pi);
             dma16<CH * DK * sizeof(OT)>(a.ws + L.o_qg + cid * L.qg * sizeof(OT), buf + B::QG, pi);
-            dma16<CH * CH * sizeof(OT)>(a.ws + L.o_t + cid * L.t * sizeof(OT), buf + B::T, pi);
+            if (!SUM) dma16<CH * CH * sizeof(OT)>(a.ws + L.o_t + cid * L.t * sizeof(OT), buf + B::T, pi);
             dma4<DK * 4>(a.ws + L.o_gc + cid * L.gc * 4, buf + B::GC, pi);
             // dO rows of this slice. Rows past the end of the sequence repeat its last row:
             // every product that reads dO (M^T dO, Qg^T dO) multiplies those rows by rows of
@@ -664,12 +759,12 @@ __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* 
     }
     const int l = lane_id(), li = l & 15, lq = l >> 4;
     lds_char* stage = stage_base + wv * RowStore<OT>::BYTES;
-    const size_t r0 = ((size_t)s * DK + 32 * wv + 4 * lq) * DV + 16 * j + li;
+    const int row0 = 32 * wv + 4 * lq, col = w.col + li;
     f32x4 dS0, dS1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        dS0[i] = a.dht ? a.dht[r0 + (size_t)i * DV] : 0.f;
-        dS1[i] = a.dht ? a.dht[r0 + (size_t)(16 + i) * DV] : 0.f;
+        dS0[i] = w.start ? w.start[(size_t)(row0 + i) * w.ld_start + col] : 0.f;
+        dS1[i] = w.start ? w.start[(size_t)(row0 + 16 + i) * w.ld_start + col] : 0.f;
     }
     lds_char* xs0 = xs;
     lds_char* xs1 = xs + NW * Xch<OT>::FRAG;
@@ -680,26 +775,27 @@ __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, lds_char* 
         for (int n = 0; n < NT; n += 2) {
             sync_lds();  // A_n
             bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
-            bwd_step<OT, DK, DV, NW>(last - n, b0, dS0, dS1, stage, xs0, xs1, pd);
+            bwd_step<OT, DK, DV, NW, SUM>(last - n, b0, dS0, dS1, stage, xs0, xs1, pd);
             if (n + 1 >= NT) break;
             sync_lds();  // A_{n+1}
             bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
-            bwd_step<OT, DK, DV, NW>(last - n - 1, b1, dS0, dS1, stage, xs1, xs0, pd);
+            bwd_step<OT, DK, DV, NW, SUM>(last - n - 1, b1, dS0, dS1, stage, xs1, xs0, pd);
         }
     } else {
         for (int n = 0; n < NT; ++n) {
             sync_lds();  // A_n
             bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
-            bwd_step<OT, DK, DV, NW>(last - n, b0, dS0, dS1, stage, (n & 1) ? xs1 : xs0, (n & 1) ? xs0 : xs1, pd);
+            bwd_step<OT, DK, DV, NW, SUM>(last - n, b0, dS0, dS1, stage, (n & 1) ? xs1 : xs0, (n & 1) ? xs0 : xs1,
+                                          pd);
             sync_lds();  // C_n
         }
     }
     bwd_flush<OT, DK, DV, NW>(a, s, j, pd);
-    if (a.dh0) {
+    if (w.end) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            a.dh0[r0 + (size_t)i * DV] = dS0[i];
-            a.dh0[r0 + (size_t)(16 + i) * DV] = dS1[i];
+            w.end[(size_t)(row0 + i) * w.ld_end + col] = dS0[i];
+            w.end[(size_t)(row0 + 16 + i) * w.ld_end + col] = dS1[i];
         }
     }
 }
@@ -716,16 +812,142 @@ __global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_bwd_chain(Args a) {
     __shared__ __align__(16) char xch[XBYTES];
     __shared__ __align__(16) char stage[SBYTES];
     __shared__ __align__(16) char pfslot[256];  // target of the L2 prefetch DMAs, never read
-    int s, j;
-    chain_map(blockIdx.x, a.B * a.H, NJ, s, j);
-    bwd_walk<OT, DK, DV, NW, DBUF>(a, s, j, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch, (lds_char*)stage,
-                                   (lds_char*)pfslot);
+    // one walk per (sequence, segment, slice), with all outputs
+    const int NSEG = a.nseg;
+    int u, j;
+    chain_map(blockIdx.x, a.B * a.H * NSEG, NJ, u, j);
+    const int s = u / NSEG, seg = u % NSEG;
+    const Layout& L = a.L;
+    const size_t sq = (size_t)DK * DV;
+    WalkSpec w;
+    w.c0 = seg * a.seg_len;
+    w.n = min(a.seg_len, a.NT - w.c0);
+    w.start = seg == NSEG - 1 ? (a.dht ? a.dht + s * sq : nullptr)
+                              : (const float*)(a.ws + L.o_segx) + ((size_t)s * NSEG + seg) * L.segx;
+    w.ld_start = DV;
+    w.ident = false;
+    w.end = (seg == 0 && a.dh0) ? a.dh0 + s * sq : nullptr;
+    w.ld_end = DV;
+    w.col = 16 * j;
+    w.noU = false;
+    bwd_walk<OT, DK, DV, NW, DBUF, false>(a, s, j, w, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch,
+                                          (lds_char*)stage, (lds_char*)pfslot);
+}
+
+// Summary walks of the backward scan, one per (sequence, segment k >= 1, slice): the
+// gradient with respect to the segment's start state when the gradient at its end is
+// zero (the last segment: dht), into the summary array.
+template <class OT, int DK, int DV>
+__global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_bwd_chain_sum(Args a) {
+    using B = BwdChainBuf<OT, DK, DV>;
+    constexpr int NW = DK / 32, NJ = DV / 16;
+    constexpr int XBYTES = Xch<OT>::bytes(NW);
+    constexpr bool DBUF = 2 * B::BYTES + XBYTES + 256 <= LDS_LIMIT;
+    __shared__ __align__(16) char buf0[B::BYTES];
+    __shared__ __align__(16) char buf1[DBUF ? B::BYTES : 16];
+    __shared__ __align__(16) char xch[XBYTES];
+    __shared__ __align__(16) char pfslot[256];  // target of the L2 prefetch DMAs, never read
+    const int NSEG = a.nseg;
+    int u, j;
+    chain_map(blockIdx.x, a.B * a.H * (NSEG - 1), NJ, u, j);
+    const int s = u / (NSEG - 1), seg = 1 + u % (NSEG - 1);
+    const Layout& L = a.L;
+    WalkSpec w;
+    w.c0 = seg * a.seg_len;
+    w.n = min(a.seg_len, a.NT - w.c0);
+    w.start = (seg == NSEG - 1 && a.dht) ? a.dht + (size_t)s * DK * DV : nullptr;
+    w.ld_start = DV;
+    w.ident = false;
+    w.end = (float*)(a.ws + L.o_segh) + ((size_t)s * NSEG + seg) * L.segh;
+    w.ld_end = DV;
+    w.col = 16 * j;
+    w.noU = false;
+    bwd_walk<OT, DK, DV, NW, DBUF, true>(a, s, j, w, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch, nullptr,
+                                         (lds_char*)pfslot);
+}
+
+// Scan over the segments of one (sequence, 16-column slice), in fp32. Forward: the true
+// start states X_1 = H_0, X_{k+1} = P_k X_k + H_k. Backward: the true end-state
+// gradients X_{NSEG-2} = H_{NSEG-1}, X_{k-1} = P_k^T X_k + H_k. P_k is staged in LDS
+// (row pitch DK + 1, so the row and the column reads are both free of bank conflicts).
+template <int DK, int DV, bool BWD>
+__global__ __launch_bounds__(256) void k_seg_scan(Args a) {
+    constexpr int NJ = DV / 16, TPR = 256 / DK, CPT = 16 / TPR;  // threads per row, columns per thread
+    constexpr int PP = DK + 1;
+    extern __shared__ __align__(16) char smem_[];
+    float* sP = (float*)smem_;     // [DK][PP]
+    float* sx = sP + DK * PP;      // [DK][16]
+    const int tid = threadIdx.x;
+    const int s = blockIdx.x / NJ, j = blockIdx.x % NJ;
+    const int NSEG = a.nseg;
+    const Layout& L = a.L;
+    const float* P = (const float*)(a.ws + L.o_segp) + (size_t)s * NSEG * L.segp;
+    const float* Hm = (const float*)(a.ws + L.o_segh) + (size_t)s * NSEG * L.segh;
+    float* X = (float*)(a.ws + L.o_segx) + (size_t)s * NSEG * L.segx;
+    const int r = tid / TPR, cl = (tid % TPR) * CPT;  // this thread's row and first column in the slice
+    const size_t e0 = (size_t)r * DV + 16 * j + cl;   // its first element in a [DK][DV] matrix
+    float x[CPT];
+    {
+        const int first = BWD ? NSEG - 1 : 0, out = BWD ? NSEG - 2 : 1;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            x[c] = Hm[(size_t)first * L.segh + e0 + c];
+            X[(size_t)out * L.segx + e0 + c] = x[c];
+        }
+    }
+    for (int step = 1; step <= NSEG - 2; ++step) {
+        const int k = BWD ? NSEG - 1 - step : step;  // the segment whose transition is applied
+        const int out = BWD ? k - 1 : k + 1;        // the boundary it gives
+        __syncthreads();                            // the previous step is done with sP and sx
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) sx[r * 16 + cl + c] = x[c];
+        const float* Pk = P + (size_t)k * L.segp;
+        for (int e = 4 * tid; e < DK * DK; e += 4 * 256) {
+            const f32x4 v = *(const f32x4*)(Pk + e);
+            const int pr = e / DK, pc = e % DK;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sP[pr * PP + pc + i] = v[i];
+        }
+        __syncthreads();
+        float acc[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] = Hm[(size_t)k * L.segh + e0 + c];
+        for (int i = 0; i < DK; ++i) {
+            const float p = BWD ? sP[i * PP + r] : sP[r * PP + i];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) acc[c] += p * sx[i * 16 + cl + c];
+        }
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            x[c] = acc[c];
+            X[(size_t)out * L.segx + e0 + c] = acc[c];
+        }
+    }
+}
+
+template <int DK, int DV, bool BWD>
+static hipError_t launch_seg_scan(const Args& a, hipStream_t stream) {
+    const size_t lds = ((size_t)DK * (DK + 1) + DK * 16) * 4;
+    hipError_t e = hipFuncSetAttribute((const void*)k_seg_scan<DK, DV, BWD>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_seg_scan<DK, DV, BWD>), dim3((unsigned)(a.B * a.H * (DV / 16))), dim3(256), lds, stream,
+                       a);
+    return hipGetLastError();
 }
 
 // ============================================================================ launchers
 template <class OT, int DK, int DV>
 hipError_t launch_fwd_chain_t(const Args& a, bool train, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.B * a.H * (DV / 16))), block(64 * (DK / 32 + NP));
+    const unsigned S = (unsigned)(a.B * a.H), NJ = DV / 16, NJP = DK / 16;
+    const dim3 block(64 * (DK / 32 + NP));
+    hipError_t e;
+    if (a.nseg > 1) {
+        hipLaunchKernelGGL((k_fwd_chain_sum<OT, DK, DV>), dim3(S * (a.nseg - 1) * (NJ + NJP)), block, 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_seg_scan<DK, DV, false>(a, stream)) != hipSuccess) return e;
+    }
+    const dim3 grid(S * a.nseg * NJ);
     if (train)
         hipLaunchKernelGGL((k_fwd_chain<OT, DK, DV, true>), grid, block, 0, stream, a);
     else
@@ -734,8 +956,15 @@ hipError_t launch_fwd_chain_t(const Args& a, bool train, hipStream_t stream) {
 }
 template <class OT, int DK, int DV>
 hipError_t launch_bwd_chain_t(const Args& a, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.B * a.H * (DV / 16))), block(64 * (DK / 32 + NP));
-    hipLaunchKernelGGL((k_bwd_chain<OT, DK, DV>), grid, block, 0, stream, a);
+    const unsigned S = (unsigned)(a.B * a.H), NJ = DV / 16;
+    const dim3 block(64 * (DK / 32 + NP));
+    hipError_t e;
+    if (a.nseg > 1) {
+        hipLaunchKernelGGL((k_bwd_chain_sum<OT, DK, DV>), dim3(S * (a.nseg - 1) * NJ), block, 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_seg_scan<DK, DV, true>(a, stream)) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_bwd_chain<OT, DK, DV>), dim3(S * a.nseg * NJ), block, 0, stream, a);
     return hipGetLastError();
 }
 

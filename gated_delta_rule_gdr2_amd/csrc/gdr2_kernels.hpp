@@ -26,6 +26,7 @@ struct Args {
     char* ws;           // workspace base
     Layout L;
     int B, T, H, NT;
+    int nseg, seg_len;  // state chains: segments per sequence and chunks per segment (nseg = 1: one walk)
     long long NC;       // B * H * NT chunks
     hipEvent_t const* events;  // optional: recorded before the first and after each kernel
 };

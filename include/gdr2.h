@@ -55,7 +55,7 @@ enum gdr2_status {
     GDR2_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
     GDR2_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
     GDR2_ERR_HIP = -6,         /* a HIP launch failed */
-    GDR2_ERR_VALUE = -7        /* a gate scale is out of range (*_logits entry points) */
+    GDR2_ERR_VALUE = -7        /* a scalar argument is out of range (gate scales, segments) */
 };
 
 /* Bytes of workspace gdr2_fwd needs. save_for_bwd = 1 sizes it for a later
@@ -87,6 +87,40 @@ int gdr2_bwd(const void* q, const void* k, const void* v, const void* g, const v
              void* dg, void* db, void* dw, float* dh0, int B, int T, int H, int dk, int dv, int chunk,
              int dtype, int fwd_saved, void* workspace, size_t workspace_bytes, void* stream,
              void* const* stage_events);
+
+/* Chunk-parallel scan of the state chains. gdr2_fwd / gdr2_bwd walk each sequence's
+ * chunks in order, one chain per sequence and 16-column slice of the value axis, so a
+ * call with few sequences and many chunks leaves most of the GPU idle. Only the state
+ * is carried between chunks ("Gated DeltaNet-2", anthology record LIT-802, "Key
+ * takeaways", second bullet; digg thread post 9/), and the carry is affine in it:
+ * S_{c+1} = P_c S_c + H_c with P_c = diag(exp gamma_C) - Kd^T Wm and H_c = Kd^T U. These
+ * variants cut every sequence into `segments` pieces of ceil(NT / segments) chunks
+ * (NT = ceil(T / chunk); fewer pieces if T is short) and walk them at the same time:
+ * summaries of each piece (its end state from a zero start and its transition, the
+ * product of its P_c), an fp32 scan over the pieces for their true start states, then
+ * the usual walk of every piece. The backward does the same in reverse with P^T.
+ * Results equal the one-walk chains up to rounding order. The work grows (about 3x the
+ * chain's), so it pays only when the sequences are too few to fill the GPU: gdr2_fwd,
+ * gdr2_bwd and their _logits variants use it by themselves when B * H * dv / 16 <= 128,
+ * with 256 / (B * H * dv / 16) segments, at most 8, of at least 8 chunks each (their
+ * workspace sizes include it), and walk the chains whole otherwise; segments = 1 here
+ * forces one walk. Workspace: gdr2_seg_workspace_bytes (with
+ * save_for_bwd = 1 for the backward; a gdr2_bwd_seg(..., fwd_saved = 1) needs the
+ * workspace of a gdr2_fwd_seg(..., save_for_bwd = 1) with the same segments). Errors
+ * as gdr2_fwd / gdr2_bwd; segments < 1 returns GDR2_ERR_VALUE. */
+size_t gdr2_seg_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int segments, int dtype,
+                                int save_for_bwd);
+
+int gdr2_fwd_seg(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+                 const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk,
+                 int segments, int dtype, int save_for_bwd, void* workspace, size_t workspace_bytes,
+                 void* stream, void* const* stage_events);
+
+int gdr2_bwd_seg(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+                 const float* h0, const void* dout, const float* dht, void* dq, void* dk_, void* dv_,
+                 void* dg, void* db, void* dw, float* dh0, int B, int T, int H, int dk, int dv, int chunk,
+                 int segments, int dtype, int fwd_saved, void* workspace, size_t workspace_bytes,
+                 void* stream, void* const* stage_events);
 
 /* Recurrent step, for decoding: processes the T tokens of q, k, v, g, b, w one at a
  * time, starting from the state in `state` (fp32 [B][H][dk][dv], required), which is
@@ -130,13 +164,14 @@ int gdr2_step_logits(const void* q, const void* k, const void* v, const void* zg
                      const void* zw, float g_scale, float b_scale, float* state, void* o, int B, int T,
                      int H, int dk, int dv, int dtype, void* stream);
 
-/* stage_events (gdr2_fwd and gdr2_bwd, and their _logits variants): NULL, or an array of hipEvent_t that the call
- * records on `stream` around its kernels, for per-kernel timing: element 0
- * before the first kernel and element i after the i-th kernel. gdr2_fwd runs
- * 2 kernels (intra-chunk, state chain), so it needs 3 events; gdr2_bwd runs
- * 2 kernels (reverse state chain, intra-chunk gradients) when fwd_saved = 1,
- * and 4 (the two forward kernels first) when fwd_saved = 0, so it needs 3 or 5.
- * The events belong to the caller. */
+/* stage_events (gdr2_fwd and gdr2_bwd, and their _logits and _seg variants): NULL, or
+ * an array of hipEvent_t that the call records on `stream` around its stages, for
+ * per-stage timing: element 0 before the first stage and element i after the i-th.
+ * gdr2_fwd runs 2 stages (intra-chunk, state chain), so it needs 3 events; gdr2_bwd
+ * runs 2 (reverse state chain, intra-chunk gradients) when fwd_saved = 1, and 4 (the
+ * two forward stages first) when fwd_saved = 0, so it needs 3 or 5. With segments > 1
+ * the chain stage also holds the summary and scan kernels. The events belong to the
+ * caller. */
 
 /* Static description of a status code. */
 const char* gdr2_strerror(int status);

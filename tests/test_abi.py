@@ -205,3 +205,61 @@ def test_logit_entry_points_validate_like_the_plain_ones(lib):
     p[6] = 0  # state
     assert step_logits(lib, p) == ERR_NULL
     assert step_logits(lib, dv=32) == ERR_UNSUP
+
+
+# ----------------------------------------------------------------------------- segmented chains
+
+def test_segment_workspace_sizes(lib):
+    BF = g2.DTYPE_BF16
+    # one segment: the plain sizes
+    assert g2.gdr2_seg_workspace_bytes(2, 4096, 16, 128, 128, 64, 1, BF, False) == \
+        g2.gdr2_fwd_workspace_bytes(2, 4096, 16, 128, 128, 64, BF, False)
+    assert g2.gdr2_seg_workspace_bytes(2, 4096, 16, 128, 128, 64, 1, BF, True) == \
+        g2.gdr2_bwd_workspace_bytes(2, 4096, 16, 128, 128, 64, BF)
+    # four segments add three fp32 matrices per (sequence, segment)
+    extra = g2.gdr2_seg_workspace_bytes(2, 4096, 16, 128, 128, 64, 4, BF, True) - \
+        g2.gdr2_seg_workspace_bytes(2, 4096, 16, 128, 128, 64, 1, BF, True)
+    assert extra == 32 * 4 * 3 * 128 * 128 * 4
+    # more segments than chunks: one per chunk
+    assert g2.gdr2_seg_workspace_bytes(1, 200, 1, 64, 64, 64, 9, BF, True) == \
+        g2.gdr2_seg_workspace_bytes(1, 200, 1, 64, 64, 64, 4, BF, True)
+    assert g2.gdr2_seg_workspace_bytes(1, 200, 1, 64, 64, 64, 0, BF, True) == 0
+
+
+def test_segment_entry_points_validate(lib):
+    v = [ctypes.c_void_p(FAKE)] * 9
+    for seg in (0, -3):
+        assert lib.gdr2_fwd_seg(*v, 1, 64, 1, 64, 64, 64, seg, g2.DTYPE_BF16, 0, ctypes.c_void_p(FAKE), 1 << 40,
+                                None, None) == ERR_VALUE
+        assert lib.gdr2_bwd_seg(*([ctypes.c_void_p(FAKE)] * 16), 1, 64, 1, 64, 64, 64, seg, g2.DTYPE_BF16, 1,
+                                ctypes.c_void_p(FAKE), 1 << 40, None, None) == ERR_VALUE
+    # the workspace check uses the segmented size
+    need = g2.gdr2_seg_workspace_bytes(1, 640, 1, 64, 64, 64, 4, g2.DTYPE_BF16, False)
+    assert lib.gdr2_fwd_seg(*v, 1, 640, 1, 64, 64, 64, 4, g2.DTYPE_BF16, 0, ctypes.c_void_p(FAKE), need - 1,
+                            None, None) == ERR_WS
+    v2 = list(v)
+    v2[0] = ctypes.c_void_p(0)
+    assert lib.gdr2_fwd_seg(*v2, 1, 640, 1, 64, 64, 64, 4, g2.DTYPE_BF16, 0, ctypes.c_void_p(FAKE), 1 << 40,
+                            None, None) == ERR_NULL
+
+
+def test_automatic_segments(lib):
+    """The plain entry points size (and run) the chunk-parallel scan by themselves only
+    when the chain workgroups (B * H * dv / 16) are at most 128: 256 / workgroups
+    segments, at most 8, of at least 8 chunks each."""
+    BF = g2.DTYPE_BF16
+
+    def auto(B, T, H, dv):
+        n = g2.gdr2_bwd_workspace_bytes(B, T, H, 128, dv, 64, BF)
+        hits = [s for s in range(1, 17) if g2.gdr2_seg_workspace_bytes(B, T, H, 128, dv, 64, s, BF, True) == n]
+        return hits[0]
+
+    assert auto(2, 4096, 16, 128) == 1       # 256 workgroups
+    assert auto(1, 16384, 16, 128) == 2      # 128
+    assert auto(1, 2048, 16, 128) == 2       # 128, 32 chunks
+    assert auto(8, 2048, 16, 128) == 1       # 1024
+    assert auto(1, 16384, 4, 128) == 8       # 32
+    assert auto(1, 16384, 2, 64) == 8        # 8
+    assert auto(1, 4096, 1, 128) == 8        # 64 chunks
+    assert auto(1, 1024, 1, 128) == 2        # 16 chunks: segments of 8
+    assert auto(1, 500, 1, 128) == 1         # 8 chunks
