@@ -168,19 +168,15 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     // the saved-state fragments are fetched up front too, except for fp32 operands,
     // where they would not fit in registers next to the rest
     constexpr bool EARLY_S = sizeof(OT) == 2;
+    static_assert(!EARLY_S || CPW == 1, "the load count below assumes one key-channel tile per wave");
     FT Sf[CPW][KV], dSf[CPW][KV];
-    if (EARLY_S) {
-#pragma unroll
-        for (int ac = 0; ac < CPW; ++ac) {
-            const int at = wv + NW * ac;
-            if (at >= DK / 16) break;
-#pragma unroll
-            for (int kb = 0; kb < KV; ++kb) {
-                Sf[ac][kb] = frag_fmaj<OT, DV>(Sg, at, kb);
-                dSf[ac][kb] = frag_fmaj<OT, DV>(dSg, at, kb);
-            }
-        }
-    }
+    // Issue order after the DMAs: the Delta / dY dumps (needed at the end of phase 1), v and
+    // w (end of phase 3a), the saved states (phase 3a). The scheduling fences keep the DMAs
+    // first, so the wait below covers them alone and the later loads stay in flight
+    // through phases 1 and 2. Each of these loads is one instruction (8 or 16 bytes).
+    __builtin_amdgcn_sched_barrier(0);
+    undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_delta) + cid * L.delta, rdl);
+    undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_dy) + cid * L.dy, rdy);
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
         const int pc = tid + NTHR * i, r = pc / NCV, rr = r < nvalid ? r : nvalid - 1;
@@ -188,12 +184,19 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         rv[i] = *(const RW*)((const OT*)a.v + off);
         rw[i] = *(const RW*)((const OT*)a.w + off);
     }
-    undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_delta) + cid * L.delta, rdl);
-    undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_dy) + cid * L.dy, rdy);
+    if (EARLY_S) {  // waves without a key-channel tile (d_k = 64) load tile 0 and ignore it
+        const int at = wv < DK / 16 ? wv : 0;
+#pragma unroll
+        for (int kb = 0; kb < KV; ++kb) {
+            Sf[0][kb] = frag_fmaj<OT, DV>(Sg, at, kb);
+            dSf[0][kb] = frag_fmaj<OT, DV>(dSg, at, kb);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // zero the padding rows of a partial chunk (positions no DMA writes); then wait for
-    // this wave's copies, and the barrier below for everyone's
-    wait_vm<0>();
+    // wait for this wave's copies (and the barrier below for everyone's), then zero the
+    // padding rows of a partial chunk (positions no DMA writes)
+    wait_vm<2 * UD::NU + 2 * NPW + (EARLY_S ? 2 * KV : 0)>();
     if (nvalid < CH) {
         zero_tail_rows<OT, DK, NTHR>(sG, nvalid);
         zero_tail_rows<OT, DK, NTHR>(sQ, nvalid);
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         zero_tail_rows<OT, DK, NTHR>(sB, nvalid);
         zero_tail_rows<OT, DV, NTHR>(sDO, nvalid);
     }
-    __syncthreads();
+    sync_lds();  // LDS only: the later loads stay in flight
     // this lane's 4-channel pieces (rows 16 t + li, channels ch0 .. ch0 + 3) of a staged tile
     const LSwz<OT, DK> vG{sG}, vQ{sQ}, vK{sK}, vB{sB};
     auto rows4 = [&](const LSwz<OT, DK>& v, int ch0, float (&out)[4][4]) {
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             lds_store<OT>(sDM + swz<OT, CH>(r, cc) * (int)sizeof(OT), to_ot<OT>(0.f));
         }
     }
-    __syncthreads();
+    sync_lds();  // LDS only: the later loads stay in flight
 
     // ---- phase 2: dA = -strict_lower(dY Delta^T), dM = lower(dO Delta^T)
     // The diagonal of M, q_r . k_r, does not depend on the decay; its gradient is
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         }
         lds_put4<OT>((isM ? sDM : sDA) + swz<OT, CH>(row, col0) * (int)sizeof(OT), v);
     }
-    __syncthreads();
+    sync_lds();  // LDS only: the later loads stay in flight
 
     // ---- phase 3a: products with the saved states, dv and dw
     // Per key-channel tile, transposed tiles (rows = key channel, columns = token):

@@ -48,10 +48,6 @@
 
 namespace gdr2 {
 
-// Workgroup barrier after this wave's LDS stores have completed (the compiler's own
-// barrier would also wait for every DMA in flight).
-__device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // this wave's index in the workgroup, as a wave-uniform (scalar) value
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 

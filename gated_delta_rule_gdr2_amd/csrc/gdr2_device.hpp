@@ -53,6 +53,12 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier after this wave's LDS operations have completed. Unlike
+// __syncthreads it does not wait for the wave's global loads (or DMAs) in flight, so
+// loads issued earlier keep running through it; LDS written by DMA must be waited for
+// (wait_vm) before it.
+__device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // pair index -> (R, I), I <= R, in the order (0,0),(1,0),(1,1),(2,0),...
 __device__ __forceinline__ void pair_ri(int p, int& R, int& I) {
     R = (p >= 6) ? 3 : (p >= 3) ? 2 : (p >= 1) ? 1 : 0;
