@@ -346,7 +346,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             *(RW*)((OT*)a.dw + rowk0 * DV + (size_t)r * rsv + ch) = dww;
         }
     }
-    __syncthreads();  // dO, Delta, dY are dead; their slots take the key/query factors
+    sync_lds();  // dO, Delta, dY are dead; their slots take the key/query factors
 
     // ---- phase 3b: XA = b*k*E1, XM = q*E1, Y = k*E2 into LDS
 #pragma unroll
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         if (ACT) activate_rows<OT, GATE_B>(bv, nvalid, a.g_scale, a.b_scale);
         scaled_factors_from<OT, DK, false>(qv, kv, bv, ch0, gam[ac], g0, ge, sXA, sXM, sY, nullptr, nullptr, nullptr);
     }
-    __syncthreads();
+    sync_lds();
 
     // ---- phase 3c: bilinear back-propagation, then the elementwise finals
     const LSwz<OT, DK> vXA{sXA}, vXM{sXM}, vY{sY};
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             lds_put4<OT>(sG + vG.off(16 * t + li, ch0), dg);
         }
     }
-    __syncthreads();
+    sync_lds();
 
     // ---- dq, dk, db, dg out of the staged tiles in whole rows
     store_rows_tiles<OT, DK, NTHR>(sQ, (OT*)a.dq + rowk0 * DK, rsk, nvalid);

@@ -67,7 +67,7 @@ __device__ __forceinline__ void blocked_inverse(const lds_char* sA, lds_char* sT
 #pragma unroll
         for (int r = 0; r < 16; ++r) lds_store<float>(Tp(16 * D + r, 16 * D + j), x[r]);
     }
-    __syncthreads();
+    sync_lds();
 #pragma unroll
     for (int lev = 1; lev < NBLK; ++lev) {
         if (wv < NBLK - lev) {
@@ -87,7 +87,7 @@ __device__ __forceinline__ void blocked_inverse(const lds_char* sA, lds_char* sT
 #pragma unroll
             for (int i = 0; i < 4; ++i) lds_store<float>(Tp(16 * R + 4 * lq + i, 16 * I + li), -t[i]);
         }
-        __syncthreads();
+        sync_lds();
     }
 }
 
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
             }
         }
     }
-    __syncthreads();
+    sync_lds();
 
     // ---- phase 2a: M = lower(Qg Khat^T), computed as M^T tiles, out to global
     const LSwz<OT, DK> vXA{sXA}, vXM{sXM}, vY{sY};
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
         const float z[4] = {0.f, 0.f, 0.f, 0.f};
         st4(m_out + swz<OT, CH>(16 * R + li, 16 * I + 4 * lq), z);
     }
-    __syncthreads();  // XM is dead from here on; its slot becomes A
+    sync_lds();  // XM is dead from here on; its slot becomes A
 
     // ---- phase 2b: A = strict_lower(Kb Khat^T), fp32 into LDS
     for (int p = wv; p < NPAIR; p += 4) {
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
         for (int i = 0; i < 4; ++i) v[i] = (R == I && 4 * lq + i >= li) ? 0.f : acc[i];
         lds_put4<float>(sA + swz<float, CH>(16 * R + li, 16 * I + 4 * lq) * 4, v);
     }
-    __syncthreads();  // Y is dead from here on; its slot becomes T
+    sync_lds();  // Y is dead from here on; its slot becomes T
 
     // ---- phase 3: T = (I + A)^-1
     for (int idx = tid; idx < 6 * 64; idx += 256) {  // zero the upper blocks of T
