@@ -185,10 +185,12 @@ def cpu_baseline(wl, inputs, min_seconds=10.0):
 
 
 def _short(name):
-    for k in KERNELS + ("copyBuffer",):
-        if k in name:
+    """The step kernel a dispatch name belongs to (k_<name> with its template arguments next,
+    so that k_fwd_chain_sum is not k_fwd_chain), the device copy, or None."""
+    for k in KERNELS:
+        if "k_" + k + "I" in name:
             return k
-    return None
+    return "copyBuffer" if "copyBuffer" in name else None
 
 
 def summarize_profile(d, workload, copy_mib, command):
@@ -417,6 +419,9 @@ def main():
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
                     help="summarise a rocprofv3 run (no GPU needed) into profiles/")
     ap.add_argument("--profile-command", default="", help="the command line recorded with --summarize-profile")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the step alone (no decode, gate-logit or chain-scan side measurements): "
+                         "the run that rocprofv3 traces")
     ap.add_argument("--scan-sweep", action="store_true",
                     help="print fwd+bwd step times against the chain segment count (chunk-parallel scan) and exit")
     args = ap.parse_args()
@@ -531,10 +536,11 @@ def main():
                           "frac": t_roof_ms / ms_step},
         "kernels_avg_ms": avg_ms,
         "ms_per_step_cache_evicted": flushed_ms,
-        "decode_step": decode_step_measurement(torch, g2),
-        "gate_logits": gate_logits_measurement(torch, g2, wl, K, stream),
-        "chain_scan": chain_scan_measurement(torch, g2, K, stream),
     }
+    if not args.headline_only:
+        out["decode_step"] = decode_step_measurement(torch, g2)
+        out["gate_logits"] = gate_logits_measurement(torch, g2, wl, K, stream)
+        out["chain_scan"] = chain_scan_measurement(torch, g2, K, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, host)
     print(json.dumps(out), flush=True)
