@@ -177,3 +177,22 @@ def test_plain_entry_points_segment_few_sequences():
     ref = oracle_all(inp, None)
     for key in ["o", "ht"] + GRADS + ["dh0"]:
         check(key, np64(plain[key]), ref[key], wl.dtype)
+
+
+def test_segmented_inference_forward_without_initial_state():
+    """An inference forward (no backward arrays in the workspace) with 6 segments and no h0,
+    then a training forward + backward with no h0 and no dht: both against the oracle."""
+    wl = small(DK=128, DV=128, T=1300, dtype="bf16", B=1, H=2, seed=37)
+    inp = make_inputs(wl)
+    x = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    args = [x[n] for n in NAMES] + [None]
+    ws = torch.empty(g2.gdr2_seg_workspace_bytes(1, 1300, 2, 128, 128, 64, 6, g2.DTYPE_BF16, False),
+                     dtype=torch.uint8, device="cuda")
+    o, ht, _ = g2.gdr2_fwd_seg(*args, segments=6, save_for_bwd=False, ws=ws)
+    torch.cuda.synchronize()
+    ref = oracle_all(inp, None)
+    check("o", np64(o), ref["o"], wl.dtype)
+    check("ht", np64(ht), ref["ht"], wl.dtype)
+    tr = run_seg(x, 6, None, need_dh0=False)
+    for key in ["o", "ht"] + GRADS:
+        check(key, np64(tr[key]), ref[key], wl.dtype)
