@@ -48,6 +48,7 @@ KERNELS = ("fwd_intra", "fwd_chain", "bwd_chain", "bwd_intra")
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, published
+MFMA_F32_PEAK_TFLOPS = 157.3    # dense fp32 MFMA, published
 METRIC = "GDR-2 fwd+bwd tokens/s at H=16,d=128,T=4K; % of MFMA/HBM roofline"
 
 
@@ -250,6 +251,41 @@ def summarize_profile(d, workload, copy_mib, command):
     print("wrote", traffic_summary_path(workload), "and the kernel table")
 
 
+def summarize_mfma(d, workload, command):
+    """Write profiles/mfma_<workload>.md from a rocprofv3 run with the derived counters
+    MfmaUtil, MfmaFlopsBF16 and MfmaFlopsF32 (pmc_mfma/) and a kernel trace (trace/)."""
+    stats = {}
+    for r in csv.DictReader(open(os.path.join(d, "trace", "run_kernel_stats.csv"))):
+        k = _short(r["Name"])
+        if k in KERNELS:
+            stats[k] = float(r["AverageNs"]) / 1e6
+    vals = {}
+    for r in csv.DictReader(open(os.path.join(d, "pmc_mfma", "run_counter_collection.csv"))):
+        k = _short(r["Kernel_Name"])
+        if k in KERNELS:
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = ["# MFMA use per kernel: fwd+bwd step, workload %s" % workload, "",
+             "Command (repository root, one MI355X):", "", "    " + command.replace("\n", "\n    "), "",
+             "MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), as rocprofv3 derives it;",
+             "MFMA TFLOP/s = MfmaFlopsBF16 (or F32) per dispatch / the kernel-trace average duration,",
+             "against the dense peaks (bf16 %.0f, fp32 %.1f TFLOP/s)." % (MFMA_BF16_PEAK_TFLOPS, MFMA_F32_PEAK_TFLOPS), "",
+             "| kernel | avg ms | MfmaUtil % | bf16 MFMA TFLOP/s | of bf16 peak | fp32 MFMA TFLOP/s | of fp32 peak |",
+             "|---|---|---|---|---|---|---|"]
+    for k in KERNELS:
+        v = {c: sum(x) / len(x) for c, x in vals.get(k, {}).items()}
+        ms = stats[k]
+        bf = v.get("MfmaFlopsBF16", 0.0) / (ms * 1e-3) / 1e12
+        f32 = v.get("MfmaFlopsF32", 0.0) / (ms * 1e-3) / 1e12
+        lines.append("| %s | %.4f | %.1f | %.1f | %.3f | %.2f | %.4f |" % (
+            k, ms, v.get("MfmaUtil", float("nan")), bf, bf / MFMA_BF16_PEAK_TFLOPS, f32, f32 / MFMA_F32_PEAK_TFLOPS))
+    lines += ["", "Kernel source digest (sha256 over gated_delta_rule_gdr2_amd/csrc): `%s`" % source_digest()]
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, "mfma_%s.md" % workload)
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("wrote", out)
+
+
 def decode_step_measurement(torch, g2, reps=50):
     """Recurrent step (gdr2_step, decoding): one token per call for B = 512 sequences of H = 16
     heads at d_k = d_v = 128, bf16, state fp32 and updated in place. Algorithmic bytes per call:
@@ -419,12 +455,18 @@ def main():
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
                     help="summarise a rocprofv3 run (no GPU needed) into profiles/")
     ap.add_argument("--profile-command", default="", help="the command line recorded with --summarize-profile")
+    ap.add_argument("--summarize-mfma", metavar="DIR", default=None,
+                    help="summarise a rocprofv3 MfmaUtil/MfmaFlops run (pmc_mfma/, trace/) into profiles/")
     ap.add_argument("--headline-only", action="store_true",
                     help="time the step alone (no decode, gate-logit or chain-scan side measurements): "
                          "the run that rocprofv3 traces")
     ap.add_argument("--scan-sweep", action="store_true",
                     help="print fwd+bwd step times against the chain segment count (chunk-parallel scan) and exit")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        from gated_delta_rule_gdr2_amd.inputs import HEADLINE
+        summarize_mfma(args.summarize_mfma, args.workload or HEADLINE, args.profile_command)
+        return
     if args.summarize_profile:
         from gated_delta_rule_gdr2_amd.inputs import HEADLINE
         summarize_profile(args.summarize_profile, args.workload or HEADLINE, args.copy_calibration or 256,

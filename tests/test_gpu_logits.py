@@ -167,3 +167,22 @@ def test_logits_training_shape_full_size():
     sel = sorted({(int(rng.integers(wl.B)), int(rng.integers(wl.H))) for _ in range(2)})
     ref = oracle_ref(inp, wl, sel=sel)
     compare(gpu, ref, wl.dtype, ["o", "ht", "dq", "dk", "dv", "dg", "db", "dw"], sel=sel)
+
+
+def test_logits_with_automatic_segments():
+    """One sequence of 65 chunks: the logit entry points cut the chains into segments by
+    themselves (as gdr2_fwd / gdr2_bwd do), with the gates activated in the kernels."""
+    wl = small(DK=128, DV=128, T=4100, dtype="bf16", B=1, H=1, h0_std=0.05, seed=43, b_scale=2.0, g_scale=0.3)
+    assert g2.gdr2_fwd_workspace_bytes(1, 4100, 1, 128, 128, 64, g2.DTYPE_BF16, True) == \
+        g2.gdr2_seg_workspace_bytes(1, 4100, 1, 128, 128, 64, 8, g2.DTYPE_BF16, True)
+    inp = make_inputs(wl, gates="logits")
+    args = gpu_args(inp)
+    h0, do = inp["h0"].cuda(), inp["do"].cuda()
+    sc = dict(g_scale=wl.g_scale, b_scale=wl.b_scale)
+    o, ht, ws = g2.gdr2_fwd_logits(*args, h0, save_for_bwd=True, **sc)
+    gr = g2.gdr2_bwd_logits(*args, h0, do, ws=ws, fwd_saved=True, **sc)
+    torch.cuda.synchronize()
+    gpu = {"o": np64(o), "ht": np64(ht)}
+    gpu.update({k: np64(v) for k, v in gr.items()})
+    ref = oracle_ref(inp, wl)
+    compare(gpu, ref, wl.dtype, ["o", "ht", "dq", "dk", "dv", "dg", "db", "dw", "dh0"])
