@@ -24,8 +24,9 @@
 //                 dS' (fragment-major) and dY (tiles) per chunk.
 //   k_bwd_intra : one workgroup per chunk, fully parallel; reads the saved S,
 //                 Delta, dS', dY and the inputs, writes dq, dk, dv, dg, db, dw.
-//                 With gates passed as logits (ACT) it activates them where they
-//                 are read and multiplies dg, db, dw by the activations' derivatives
+//                 With gates passed as logits (ACT) it activates g and b once, in
+//                 phase 1 (b, and d g / d z_g, go back into the staged tiles), w where
+//                 it is read, and multiplies dg, db, dw by the activations' derivatives
 //                 before they are stored (gradients with respect to the logits).
 #include "gdr2_intra_common.hpp"
 #include "gdr2_kernels.hpp"
@@ -220,7 +221,28 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         const int ch0 = 16 * (wv + NW * ac) + 4 * lq;
         float gv[4][4], g0[4][4], ge[4][4];
         rows4(vG, ch0, gv);
-        if (ACT) activate_rows<OT, GATE_G>(gv, nvalid, a.g_scale, a.b_scale);
+        if (ACT) {
+            // Gates given as logits, activated once here for this wave's columns: g from
+            // z_g, with d g / d z = -g_scale sigmoid(z_g) written over z_g in the g tile
+            // (the finals need it), and b over z_b in the b tile (phases 3b and 3c read it).
+            float dz[4][4], bv[4][4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float sp, sg;
+                    gate_softplus_sigmoid<OT>(gv[t][i], sp, sg);
+                    gv[t][i] = 16 * t + li < nvalid ? -a.g_scale * sp : 0.f;
+                    dz[t][i] = -a.g_scale * sg;
+                }
+            rows4(vB, ch0, bv);
+            activate_rows<OT, GATE_B>(bv, nvalid, a.g_scale, a.b_scale);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                lds_put4<OT>(sG + vG.off(16 * t + li, ch0), dz[t]);
+                lds_put4<OT>(sB + vB.off(16 * t + li, ch0), bv[t]);
+            }
+        }
         gamma_scan(gv, gam[ac], g0, ge);
         RowExp rx;
         row_exps<DK>(sF, ch0, g0, ge, rx);
@@ -364,8 +386,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         float qv[4][4], kv[4][4], bv[4][4];
         rows4(vQ, ch0, qv);
         rows4(vK, ch0, kv);
-        rows4(vB, ch0, bv);
-        if (ACT) activate_rows<OT, GATE_B>(bv, nvalid, a.g_scale, a.b_scale);
+        rows4(vB, ch0, bv);  // (activated in phase 1 when the gates came as logits)
         scaled_factors_from<OT, DK, false>(qv, kv, bv, ch0, gam[ac], g0, ge, sXA, sXM, sY, nullptr, nullptr, nullptr);
     }
     sync_lds();
@@ -415,7 +436,6 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         rows4(vQ, ch0, qv);
         rows4(vK, ch0, kv);
         rows4(vB, ch0, bv);
-        if (ACT) activate_rows<OT, GATE_B>(bv, nvalid, a.g_scale, a.b_scale);
         float dgam[4][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -460,14 +480,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
                 pre[t][i] = x;
                 tot[i] = row_bcast<15>(x);
             }
-        float gf[4][4];  // ACT: d g / d z = -g_scale sigmoid(z), from the logits still in sG
-        if (ACT) {
-            rows4(vG, ch0, gf);
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) gf[t][i] = -a.g_scale * gate_sigmoid<OT>(gf[t][i]);
-        }
+        float gf[4][4];  // ACT: d g / d z, left in the g tile by phase 1
+        if (ACT) rows4(vG, ch0, gf);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             float dg[4];

@@ -117,6 +117,15 @@ __device__ __forceinline__ float gate_softplus(float z) {
     if constexpr (sizeof(OT) == 4) return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
     else return fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z)));
 }
+// softplus(z) and sigmoid(z) from one exponential: with e = exp(-|z|),
+// softplus = max(z, 0) + log(1 + e) and sigmoid = 1 / (1 + e) (z >= 0) or e / (1 + e)
+template <class OT>
+__device__ __forceinline__ void gate_softplus_sigmoid(float z, float& sp, float& sg) {
+    const float e = sizeof(OT) == 4 ? expf(-fabsf(z)) : __expf(-fabsf(z));
+    sp = fmaxf(z, 0.f) + (sizeof(OT) == 4 ? log1pf(e) : __logf(1.f + e));
+    const float r = sizeof(OT) == 4 ? 1.f / (1.f + e) : __builtin_amdgcn_rcpf(1.f + e);
+    sg = z >= 0.f ? r : e * r;
+}
 enum GateKind { GATE_G, GATE_B, GATE_W };
 template <class OT, int KIND>
 __device__ __forceinline__ float gate_act(float z, float g_scale, float b_scale) {
