@@ -35,6 +35,13 @@
  * Errors: every argument is checked on the host before any HIP call; a failed
  * check returns a negative status and enqueues nothing. A failed launch
  * returns GDR2_ERR_HIP. Non-finite inputs are not checked; they propagate.
+ *
+ * Decay range: the chunkwise kernels split each chunk into 16-token blocks and scale
+ * the factors of a block by exp of its cumulative log-decay, which must stay finite
+ * in fp32: for every channel, g summed over any 15 consecutive tokens of a block must
+ * be above about -88 (an average log-decay above -5.9 per token, decay exp g above
+ * 0.0028). Stronger decays give non-finite results. gdr2_step (token by token) has no
+ * such bound.
  */
 #ifndef GDR2_H
 #define GDR2_H

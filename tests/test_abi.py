@@ -263,3 +263,10 @@ def test_automatic_segments(lib):
     assert auto(1, 4096, 1, 128) == 8        # 64 chunks
     assert auto(1, 1024, 1, 128) == 2        # 16 chunks: segments of 8
     assert auto(1, 500, 1, 128) == 1         # 8 chunks
+
+
+def test_sizes_that_overflow_are_rejected(lib):
+    # more than 2^31 - 1 chunks, or more than 2^40 token rows: invalid shape, nothing enqueued
+    assert fwd(lib, B=1 << 16, T=1 << 20, H=1 << 10) == ERR_SHAPE
+    assert fwd(lib, B=1 << 20, T=1 << 20, H=1) == ERR_SHAPE
+    assert g2.gdr2_fwd_workspace_bytes(1 << 16, 1 << 20, 1 << 10, 64, 64, 64, g2.DTYPE_BF16, False) == 0

@@ -247,3 +247,32 @@ def test_autograd_function_matches_direct_calls():
     torch.cuda.synchronize()
     for t, key in zip(ts + [h0], ["dq", "dk", "dv", "dg", "db", "dw", "dh0"]):
         assert torch.equal(t.grad, gr[key]), key
+
+
+DEGENERATE = [
+    # no erase: decayed linear attention (b = 0)
+    ("no_erase", dict(b=0.0)),
+    # no decay and the gates fully open (g = 0, b = w = 1): the delta rule that overwrites
+    ("overwrite", dict(g=0.0, b=1.0, w=1.0)),
+    # strong forgetting at every token: bf16 at the edge of the supported range (exp(-5.5) = 0.004,
+    # 82.5 of log-decay over the 15 steps of a 16-token block; the bound is about 88); fp32 at
+    # exp(-1.5), where the fp32 running log-decay (|gamma| up to 96 in a chunk) still keeps the
+    # factors inside the 1e-5 tolerance
+    ("forget", dict(g={"bf16": -5.5, "f32": -1.5})),
+    # zero keys: nothing is written or erased; the state only decays and is read out
+    ("zero_keys", dict(k=0.0)),
+]
+
+
+@pytest.mark.parametrize("dtype,DK,DV", [("bf16", 128, 128), ("f32", 64, 64)])
+@pytest.mark.parametrize("name,fill", DEGENERATE, ids=[d[0] for d in DEGENERATE])
+def test_degenerate_gates(dtype, DK, DV, name, fill):
+    """Special cases of the recurrence with closed forms, forward and backward against the oracle."""
+    wl = small(DK=DK, DV=DV, T=150, dtype=dtype, B=1, H=2, h0_std=0.1, backward=True, seed=53)
+    inp = make_inputs(wl)
+    for key, val in fill.items():
+        inp[key] = torch.full_like(inp[key], val[dtype] if isinstance(val, dict) else val)
+    dht = torch.from_numpy(np.random.default_rng(6).standard_normal((wl.B, wl.H, wl.DK, wl.DV))).float()
+    gpu = run_gpu(inp, True, dht)
+    ref = run_oracle(inp, True, dht)
+    compare(gpu, ref, wl.dtype, True)
