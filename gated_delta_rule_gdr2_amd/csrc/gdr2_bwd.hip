@@ -46,7 +46,8 @@ struct BwdLds {  // all matrices are swizzled tiles (see swz())
     static constexpr int DM = DA + CH * CH * ES;
     static constexpr int F = DM + CH * CH * ES;
     static constexpr int DMD = F + F_ROWS * DK * 4;  // diagonal of dM, fp32
-    static constexpr int G = DMD + CH * 4;           // g, q, k, b of the chunk [CH][DK]
+    static constexpr int CARRY = DMD + CH * 4;       // per key channel, fp32: sum dKd*Kd, rowsum(dS'*S)
+    static constexpr int G = CARRY + 2 * DK * 4;     // g, q, k, b of the chunk [CH][DK]
     static constexpr int Q = G + KMAT;
     static constexpr int K = Q + KMAT;
     static constexpr int B = K + KMAT;
@@ -292,7 +293,11 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     //   Pk = exp(gam_C - gam_Rend) * (Delta dS'^T)^T
     // The bilinear terms are accumulated into the same registers in phase 3c.
     f32x4 Pq[CPW][4], Pb[CPW][4], Pk[CPW][4];
+    // Two per-channel sums go from here to the finals: in registers, or through LDS (sCarry)
+    // when the gates come as logits, where the registers would not hold them.
+    constexpr bool CARRY_LDS = ACT;
     float rsum[CPW], kdx[CPW][4];
+    lds_char* sCarry = smem + LS::CARRY;
 #pragma unroll
     for (int ac = 0; ac < CPW; ++ac) {
         const int at = wv + NW * ac;
@@ -311,7 +316,10 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             for (int e = 0; e < 8; ++e) pr += to_f(Sf[ac][kb][e]) * to_f(dSf[ac][kb][e]);
         pr += __shfl_xor(pr, 16, 64);
         pr += __shfl_xor(pr, 32, 64);  // rowsum(dS' * S) of key channel 16at + li
-        rsum[ac] = pr;
+        if (!CARRY_LDS)
+            rsum[ac] = pr;
+        else if (lq == 0)
+            lds_store<float>(sCarry + (DK + 16 * at + li) * 4, pr);
         float g0[4][4], ge[4][4];
 #pragma unroll
         for (int R = 0; R < 4; ++R)
@@ -348,7 +356,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) kx[i] += Pk[ac][t][i] * kv[t][i] * __expf(ge[t][i] - gam[ac][t][i]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kdx[ac][i] = row_sum16(kx[i]);
+        for (int i = 0; i < 4; ++i) kx[i] = kdx[ac][i] = row_sum16(kx[i]);
+        if (CARRY_LDS && li == 0) lds_put4<float>(sCarry + ch0 * 4, kx);
     }
     // dv = dY * w, dw = dY * v, in the row-piece layout of v and w
 #pragma unroll
@@ -398,27 +407,63 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     for (int ac = 0; ac < CPW; ++ac) {
         const int at = wv + NW * ac;
         if (at >= DK / 16) break;
-        const int mcol = 16 * at + li;  // key channel held as operand row by this lane
-        auto sfac = [&](int R, int I) { return lds_load<float>(sF + ((F_S + pair_id(R, I)) * DK + mcol) * 4); };
+        // The block-pair factor s(R, I) is per key channel, which is the row of every product
+        // below: each 32-deep fragment pair is split into its two 16-token blocks, multiplied
+        // unscaled, and the factor applied to the fp32 result (rows 16 at + 4 lq + i of a lane).
+        auto sfac4 = [&](int R, int I, float (&s4)[4]) {
+            lds_get4<float>(sF + ((F_S + pair_id(R, I)) * DK + 16 * at + 4 * lq) * 4, s4);
+        };
 #pragma unroll
         for (int R = 0; R < 4; ++R) {  // Xbar (erase / query side) for target block R
             for (int kb = 0; kb <= R / 2; ++kb) {
-                const int I0 = 2 * kb, I1 = 2 * kb + 1;
-                FT ay = lfrag_colk<OT, OT>(vY, 16 * at, 32 * kb, sfac(R, I0), I1 <= R ? sfac(R, I1) : 0.f);
-                mma(Pb[ac][R], ay, lfrag_rowk<OT, OT>(vDA, 16 * R, 32 * kb));
-                mma(Pq[ac][R], ay, lfrag_rowk<OT, OT>(vDM, 16 * R, 32 * kb));
+                const FT ay = lfrag_colk<OT, OT>(vY, 16 * at, 32 * kb);
+                const FT da = lfrag_rowk<OT, OT>(vDA, 16 * R, 32 * kb), dm = lfrag_rowk<OT, OT>(vDM, 16 * R, 32 * kb);
+                f32x4 tb = {0.f, 0.f, 0.f, 0.f}, tq = tb;
+                float sc[4];
+                mma_half<0>(tb, ay, da);
+                mma_half<0>(tq, ay, dm);
+                sfac4(R, 2 * kb, sc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    Pb[ac][R][i] = fmaf(sc[i], tb[i], Pb[ac][R][i]);
+                    Pq[ac][R][i] = fmaf(sc[i], tq[i], Pq[ac][R][i]);
+                }
+                if (2 * kb + 1 <= R) {
+                    tb = f32x4{0.f, 0.f, 0.f, 0.f};
+                    tq = tb;
+                    mma_half<1>(tb, ay, da);
+                    mma_half<1>(tq, ay, dm);
+                    sfac4(R, 2 * kb + 1, sc);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        Pb[ac][R][i] = fmaf(sc[i], tb[i], Pb[ac][R][i]);
+                        Pq[ac][R][i] = fmaf(sc[i], tq[i], Pq[ac][R][i]);
+                    }
+                }
             }
         }
 #pragma unroll
         for (int I = 0; I < 4; ++I) {  // Ybar (key side) for source block I
             for (int kb = I / 2; kb < 2; ++kb) {
-                const int R0 = 2 * kb, R1 = 2 * kb + 1;
-                const float r0 = R0 >= I ? sfac(R0, I) : 0.f;
-                const float r1 = R1 >= I ? sfac(R1, I) : 0.f;
-                mma(Pk[ac][I], lfrag_colk<OT, OT>(vXA, 16 * at, 32 * kb, r0, r1),
-                    lfrag_colk<OT, OT>(vDA, 16 * I, 32 * kb));
-                mma(Pk[ac][I], lfrag_colk<OT, OT>(vXM, 16 * at, 32 * kb, r0, r1),
-                    lfrag_colk<OT, OT>(vDM, 16 * I, 32 * kb));
+                const FT xa = lfrag_colk<OT, OT>(vXA, 16 * at, 32 * kb), xm = lfrag_colk<OT, OT>(vXM, 16 * at, 32 * kb);
+                const FT dat = lfrag_colk<OT, OT>(vDA, 16 * I, 32 * kb), dmt = lfrag_colk<OT, OT>(vDM, 16 * I, 32 * kb);
+                float sc[4];
+                if (2 * kb >= I) {  // target block R = 2 kb
+                    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+                    mma_half<0>(t, xa, dat);
+                    mma_half<0>(t, xm, dmt);
+                    sfac4(2 * kb, I, sc);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Pk[ac][I][i] = fmaf(sc[i], t[i], Pk[ac][I][i]);
+                }
+                {  // target block R = 2 kb + 1 (always >= I)
+                    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+                    mma_half<1>(t, xa, dat);
+                    mma_half<1>(t, xm, dmt);
+                    sfac4(2 * kb + 1, I, sc);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Pk[ac][I][i] = fmaf(sc[i], t[i], Pk[ac][I][i]);
+                }
             }
         }
 
@@ -466,8 +511,11 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         // scaling of the carried state at the chunk's last row: sum_r dKd*Kd + exp(gam_C) rowsum(dS'*S)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float rs_i = __shfl(rsum[ac], (l & 48) | (4 * lq + i), 64);  // row sum of channel ch0 + i
-            const float extra = kdx[ac][i] + __expf(ge[3][i]) * rs_i;
+            // row sum of channel ch0 + i, and the dKd*Kd sum of that channel
+            const float rs_i = CARRY_LDS ? lds_load<float>(sCarry + (DK + ch0 + i) * 4)
+                                         : __shfl(rsum[ac], (l & 48) | (4 * lq + i), 64);
+            const float kd_i = CARRY_LDS ? lds_load<float>(sCarry + (ch0 + i) * 4) : kdx[ac][i];
+            const float extra = kd_i + __expf(ge[3][i]) * rs_i;
             if (li == 15) dgam[3][i] += extra;
         }
         // dg = reverse running sum of dgam over the chunk's tokens

@@ -79,6 +79,21 @@ __device__ __forceinline__ void mma_k16_f32(f32x4& acc, const float a[4], const 
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
 }
+// Product over one half of the K slots of two 32-deep fragments: half H holds the K
+// indices 16 H + 4*lq + e (e < 4), one 16-row block of the K axis.
+template <int H>
+__device__ __forceinline__ void mma_half(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 ah = __builtin_shufflevector(a, a, 4 * H, 4 * H + 1, 4 * H + 2, 4 * H + 3);
+    const bf16x4 bh = __builtin_shufflevector(b, b, 4 * H, 4 * H + 1, 4 * H + 2, 4 * H + 3);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, ah), __builtin_bit_cast(s16x4, bh), acc,
+                                                    0, 0, 0);
+}
+template <int H>
+__device__ __forceinline__ void mma_half(f32x4& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * H + e], b[4 * H + e], acc, 0, 0, 0);
+}
 
 // ----------------------------------------------------------------------------- conversions
 template <class OT> __device__ __forceinline__ OT to_ot(float x);
