@@ -296,7 +296,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     // Two per-channel sums go from here to the finals: in registers, or through LDS (sCarry)
     // when the gates come as logits, where the registers would not hold them.
     constexpr bool CARRY_LDS = ACT;
-    float rsum[CPW], kdx[CPW][4];
+    f32x4 rsum[CPW];  // S dS'^T over this wave's 16 key channels; its diagonal is rowsum(dS' * S)
+    float kdx[CPW][4];
     lds_char* sCarry = smem + LS::CARRY;
 #pragma unroll
     for (int ac = 0; ac < CPW; ++ac) {
@@ -309,17 +310,18 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
                 dSf[ac][kb] = frag_fmaj<OT, DV>(dSg, at, kb);
             }
         }
-        float pr = 0.f;
+        // lane (li, lq) element i: sum over v of S[16at + 4lq + i][v] dS'[16at + li][v], so the
+        // diagonal (channel 16at + 4lq + i) is element i of lane (4lq + i, lq)
+        f32x4 sd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KV; ++kb)
+        for (int kb = 0; kb < KV; ++kb) mma(sd, Sf[ac][kb], dSf[ac][kb]);
+        if (!CARRY_LDS) {
+            rsum[ac] = sd;
+        } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pr += to_f(Sf[ac][kb][e]) * to_f(dSf[ac][kb][e]);
-        pr += __shfl_xor(pr, 16, 64);
-        pr += __shfl_xor(pr, 32, 64);  // rowsum(dS' * S) of key channel 16at + li
-        if (!CARRY_LDS)
-            rsum[ac] = pr;
-        else if (lq == 0)
-            lds_store<float>(sCarry + (DK + 16 * at + li) * 4, pr);
+            for (int i = 0; i < 4; ++i)
+                if (li == 4 * lq + i) lds_store<float>(sCarry + (DK + 16 * at + li) * 4, sd[i]);
+        }
         float g0[4][4], ge[4][4];
 #pragma unroll
         for (int R = 0; R < 4; ++R)
@@ -513,7 +515,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         for (int i = 0; i < 4; ++i) {
             // row sum of channel ch0 + i, and the dKd*Kd sum of that channel
             const float rs_i = CARRY_LDS ? lds_load<float>(sCarry + (DK + ch0 + i) * 4)
-                                         : __shfl(rsum[ac], (l & 48) | (4 * lq + i), 64);
+                                         : __shfl(rsum[ac][i], (l & 48) | (4 * lq + i), 64);
             const float kd_i = CARRY_LDS ? lds_load<float>(sCarry + (ch0 + i) * 4) : kdx[ac][i];
             const float extra = kd_i + __expf(ge[3][i]) * rs_i;
             if (li == 15) dgam[3][i] += extra;
