@@ -231,6 +231,30 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
     }
     sync_lds();  // Y is dead from here on; its slot becomes T
 
+    // ---- XA -> K_b = b k exp(gam) for phase 4, once and in place (no phase reads XA before
+    // then): row r takes the factor exp(gam at the first row of its 16-row block), per key
+    // channel, rounded to the operand type as a rescaled fragment would be
+    {
+        constexpr int EPC = 16 / (int)sizeof(OT), NCK = DK / EPC;  // 16-byte chunks per row
+        using RT = typename Raw16<OT>::type;
+        for (int e = tid; e < CH * NCK; e += 256) {
+            const int r = e / NCK, pos = e % NCK, c0 = (pos ^ swz_f<OT, DK>(r)) * EPC;
+            lds_char* p = sXA + (r * DK + pos * EPC) * (int)sizeof(OT);
+            RT x = lds_load<RT>(p);
+            float f[EPC];
+#pragma unroll
+            for (int h = 0; h < EPC / 4; ++h) {
+                float f4[4];
+                lds_get4<float>(sF + ((F_ER0 + r / 16) * DK + c0 + 4 * h) * 4, f4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) f[4 * h + i] = f4[i];
+            }
+#pragma unroll
+            for (int i = 0; i < EPC; ++i) x[i] = to_ot<OT>((float)x[i] * f[i]);
+            lds_store<RT>(p, x);
+        }
+    }
+
     // ---- phase 3: T = (I + A)^-1
     for (int idx = tid; idx < 6 * 64; idx += 256) {  // zero the upper blocks of T
         int R, I;
@@ -259,14 +283,9 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
         }
 #pragma unroll
         for (int at = 0; at < DK / 16; ++at) {
-            const int col = 16 * at + li;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const float f0 = lds_load<float>(sF + ((F_ER0 + 2 * kb) * DK + col) * 4);
-                const float f1 = lds_load<float>(sF + ((F_ER0 + 2 * kb + 1) * DK + col) * 4);
-                mma(acc, lfrag_colk<OT, OT>(vXA, 16 * at, 32 * kb, f0, f1), aT[kb]);
-            }
+            for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vXA, 16 * at, 32 * kb), aT[kb]);  // XA holds K_b
             float v[4] = {acc[0], acc[1], acc[2], acc[3]};  // Wm[16tt + li][16at + 4lq + i]
             st4(wm_out + swz<OT, DK>(16 * tt + li, 16 * at + 4 * lq), v);
         }
