@@ -159,7 +159,10 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* g, const v
     a.events = (hipEvent_t const*)stage_events;
     if (!fwd_saved) {
         e = gdr2::launch_fwd(a, bf, true, (hipStream_t)stream);
-        if (a.events) a.events += 2;  // the backward kernels record after the two forward ones
+        if (a.events) {  // the backward stages follow the two forward ones, whose end is their start
+            a.events += 2;
+            a.events_continue = 1;
+        }
     }
     if (e == hipSuccess) e = gdr2::launch_bwd(a, bf, (hipStream_t)stream);
     return e == hipSuccess ? GDR2_OK : GDR2_ERR_HIP;

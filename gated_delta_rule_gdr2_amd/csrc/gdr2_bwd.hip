@@ -567,12 +567,11 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t stream) {
     auto intra = a.act ? k_bwd_intra<OT, DK, DV, true> : k_bwd_intra<OT, DK, DV, false>;
     hipError_t e = hipFuncSetAttribute((const void*)intra, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    if ((e = mark(a, 0, stream)) != hipSuccess) return e;
-    if ((e = launch_bwd_chain_t<OT, DK, DV>(a, stream)) != hipSuccess) return e;
-    if ((e = mark(a, 1, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(intra, dim3((unsigned)a.NC), dim3(64 * BWD_NW), lds, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    return mark(a, 2, stream);
+    // stage events: 0 at the start of the chain, 1 at its end, 2 at the end of the intra-chunk kernel
+    if ((e = launch_bwd_chain_t<OT, DK, DV>(a, stream, stage_event(a, 0), stage_event(a, 1))) != hipSuccess) return e;
+    hipExtLaunchKernelGGL(intra, dim3((unsigned)a.NC), dim3(64 * BWD_NW), lds, stream, nullptr, stage_event(a, 2),
+                          0, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd(const Args& a, bool bf16_, hipStream_t stream) {

@@ -922,7 +922,7 @@ __global__ __launch_bounds__(256) void k_seg_scan(Args a) {
 }
 
 template <int DK, int DV, bool BWD>
-static hipError_t launch_seg_scan(const Args& a, hipStream_t stream) {
+static hipError_t launch_seg_scan(const Args& a, hipStream_t stream) {  // never first or last of a stage
     const size_t lds = ((size_t)DK * (DK + 1) + DK * 16) * 4;
     hipError_t e = hipFuncSetAttribute((const void*)k_seg_scan<DK, DV, BWD>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -934,39 +934,43 @@ static hipError_t launch_seg_scan(const Args& a, hipStream_t stream) {
 
 // ============================================================================ launchers
 template <class OT, int DK, int DV>
-hipError_t launch_fwd_chain_t(const Args& a, bool train, hipStream_t stream) {
+hipError_t launch_fwd_chain_t(const Args& a, bool train, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     const unsigned S = (unsigned)(a.B * a.H), NJ = DV / 16, NJP = DK / 16;
     const dim3 block(64 * (DK / 32 + NP));
     hipError_t e;
     if (a.nseg > 1) {
-        hipLaunchKernelGGL((k_fwd_chain_sum<OT, DK, DV>), dim3(S * (a.nseg - 1) * (NJ + NJP)), block, 0, stream, a);
+        hipExtLaunchKernelGGL((k_fwd_chain_sum<OT, DK, DV>), dim3(S * (a.nseg - 1) * (NJ + NJP)), block, 0, stream,
+                              start, nullptr, 0, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_seg_scan<DK, DV, false>(a, stream)) != hipSuccess) return e;
+        start = nullptr;
     }
     const dim3 grid(S * a.nseg * NJ);
     if (train)
-        hipLaunchKernelGGL((k_fwd_chain<OT, DK, DV, true>), grid, block, 0, stream, a);
+        hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, true>), grid, block, 0, stream, start, stop, 0, a);
     else
-        hipLaunchKernelGGL((k_fwd_chain<OT, DK, DV, false>), grid, block, 0, stream, a);
+        hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, false>), grid, block, 0, stream, start, stop, 0, a);
     return hipGetLastError();
 }
 template <class OT, int DK, int DV>
-hipError_t launch_bwd_chain_t(const Args& a, hipStream_t stream) {
+hipError_t launch_bwd_chain_t(const Args& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     const unsigned S = (unsigned)(a.B * a.H), NJ = DV / 16;
     const dim3 block(64 * (DK / 32 + NP));
     hipError_t e;
     if (a.nseg > 1) {
-        hipLaunchKernelGGL((k_bwd_chain_sum<OT, DK, DV>), dim3(S * (a.nseg - 1) * NJ), block, 0, stream, a);
+        hipExtLaunchKernelGGL((k_bwd_chain_sum<OT, DK, DV>), dim3(S * (a.nseg - 1) * NJ), block, 0, stream, start,
+                              nullptr, 0, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_seg_scan<DK, DV, true>(a, stream)) != hipSuccess) return e;
+        start = nullptr;
     }
-    hipLaunchKernelGGL((k_bwd_chain<OT, DK, DV>), dim3(S * a.nseg * NJ), block, 0, stream, a);
+    hipExtLaunchKernelGGL((k_bwd_chain<OT, DK, DV>), dim3(S * a.nseg * NJ), block, 0, stream, start, stop, 0, a);
     return hipGetLastError();
 }
 
 #define GDR2_CHAIN_INST(OT_, DK_, DV_)                                                      \
-    template hipError_t launch_fwd_chain_t<OT_, DK_, DV_>(const Args&, bool, hipStream_t); \
-    template hipError_t launch_bwd_chain_t<OT_, DK_, DV_>(const Args&, hipStream_t);
+    template hipError_t launch_fwd_chain_t<OT_, DK_, DV_>(const Args&, bool, hipStream_t, hipEvent_t, hipEvent_t); \
+    template hipError_t launch_bwd_chain_t<OT_, DK_, DV_>(const Args&, hipStream_t, hipEvent_t, hipEvent_t);
 GDR2_CHAIN_INST(bf16, 64, 64)
 GDR2_CHAIN_INST(bf16, 64, 128)
 GDR2_CHAIN_INST(bf16, 128, 64)

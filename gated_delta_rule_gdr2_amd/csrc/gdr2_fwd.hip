@@ -317,12 +317,11 @@ static hipError_t launch_fwd_t(const Args& a, bool train, hipStream_t stream) {
                        : (train ? k_fwd_intra<OT, DK, DV, true, false> : k_fwd_intra<OT, DK, DV, false, false>);
     hipError_t e = hipFuncSetAttribute((const void*)intra, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    if ((e = mark(a, 0, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(intra, dim3((unsigned)a.NC), dim3(256), lds, stream, a);
+    // stage events: 0 at the start of the intra-chunk kernel, 1 at its end, 2 at the end of the chain
+    hipExtLaunchKernelGGL(intra, dim3((unsigned)a.NC), dim3(256), lds, stream, stage_event(a, 0), stage_event(a, 1),
+                          0, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = mark(a, 1, stream)) != hipSuccess) return e;
-    if ((e = launch_fwd_chain_t<OT, DK, DV>(a, train, stream)) != hipSuccess) return e;
-    return mark(a, 2, stream);
+    return launch_fwd_chain_t<OT, DK, DV>(a, train, stream, nullptr, stage_event(a, 2));
 }
 
 hipError_t launch_fwd(const Args& a, bool bf16_, bool train, hipStream_t stream) {

@@ -1,5 +1,6 @@
 // Kernel arguments and launcher declarations (internal to libgdr2).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "gdr2_layout.hpp"
@@ -28,19 +29,24 @@ struct Args {
     int B, T, H, NT;
     int nseg, seg_len;  // state chains: segments per sequence and chunks per segment (nseg = 1: one walk)
     long long NC;       // B * H * NT chunks
-    hipEvent_t const* events;  // optional: recorded before the first and after each kernel
+    hipEvent_t const* events;  // optional: per-stage timing events (see stage_event)
+    int events_continue;       // 1: events[0] was recorded by the stages before (backward after a recompute)
 };
 
-// record events[i] on the stream when per-kernel timing was requested
-inline hipError_t mark(const Args& a, int i, hipStream_t stream) {
-    return a.events ? hipEventRecord(a.events[i], stream) : hipSuccess;
+// events[i] when per-stage timing was requested, else null. The launches attach them to
+// their kernels (hipExtLaunchKernelGGL start / stop events), so timing adds no packets to
+// the stream between the kernels.
+inline hipEvent_t stage_event(const Args& a, int i) {
+    return a.events && !(i == 0 && a.events_continue) ? a.events[i] : nullptr;
 }
 
 // Launchers: enqueue on `stream`, return hipSuccess or the launch error.
+// The chain launchers take the events for the start of their first kernel and the end of
+// their last (either may be null).
 template <class OT, int DK, int DV>
-hipError_t launch_fwd_chain_t(const Args& a, bool train, hipStream_t stream);
+hipError_t launch_fwd_chain_t(const Args& a, bool train, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 template <class OT, int DK, int DV>
-hipError_t launch_bwd_chain_t(const Args& a, hipStream_t stream);
+hipError_t launch_bwd_chain_t(const Args& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_fwd(const Args& a, bool bf16, bool train, hipStream_t stream);
 hipError_t launch_bwd(const Args& a, bool bf16, hipStream_t stream);
 hipError_t launch_step(const Args& a, bool bf16, hipStream_t stream);

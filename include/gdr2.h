@@ -172,8 +172,11 @@ int gdr2_step_logits(const void* q, const void* k, const void* v, const void* zg
                      int H, int dk, int dv, int dtype, void* stream);
 
 /* stage_events (gdr2_fwd and gdr2_bwd, and their _logits and _seg variants): NULL, or
- * an array of hipEvent_t that the call records on `stream` around its stages, for
- * per-stage timing: element 0 before the first stage and element i after the i-th.
+ * an array of hipEvent_t for per-stage timing on `stream`: element 0 marks the start of
+ * the first stage and element i the end of the i-th. The events are attached to the
+ * stages' kernel launches (start of the first kernel, end of the last), so timing puts no
+ * extra commands between the kernels; a stage's interval therefore includes the launch
+ * gap before its first kernel.
  * gdr2_fwd runs 2 stages (intra-chunk, state chain), so it needs 3 events; gdr2_bwd
  * runs 2 (reverse state chain, intra-chunk gradients) when fwd_saved = 1, and 4 (the
  * two forward stages first) when fwd_saved = 0, so it needs 3 or 5. With segments > 1
