@@ -276,3 +276,25 @@ def test_degenerate_gates(dtype, DK, DV, name, fill):
     gpu = run_gpu(inp, True, dht)
     ref = run_oracle(inp, True, dht)
     compare(gpu, ref, wl.dtype, True)
+
+
+MANY_SHORT = [
+    # many sequences of two chunks, the second ragged: large grids (4096 chain workgroups for
+    # the first), every sequence's last chunk partial, random h0 and dht
+    dict(DK=128, DV=128, T=65, dtype="bf16", B=16, H=16, h0_std=0.05),
+    dict(DK=64, DV=64, T=70, dtype="f32", B=8, H=8, h0_std=0.05),
+]
+
+
+@pytest.mark.parametrize("p", MANY_SHORT, ids=lambda p: "-".join("%s%s" % kv for kv in p.items()))
+def test_many_short_sequences(p):
+    kw = dict(p)
+    wl = small(DK=kw.pop("DK"), DV=kw.pop("DV"), T=kw.pop("T"), dtype=kw.pop("dtype"), B=kw.pop("B"),
+               H=kw.pop("H"), backward=True, seed=61, **kw)
+    inp = make_inputs(wl)
+    dht = torch.from_numpy(np.random.default_rng(5).standard_normal((wl.B, wl.H, wl.DK, wl.DV))).float()
+    gpu = run_gpu(inp, True, dht)
+    rng = np.random.default_rng(wl.seed + 300)
+    sel = sorted({(int(rng.integers(wl.B)), int(rng.integers(wl.H))) for _ in range(6)})
+    ref = run_oracle(inp, True, dht, sel=sel)
+    compare(gpu, ref, wl.dtype, True, sel=sel)
