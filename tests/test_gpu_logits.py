@@ -186,3 +186,36 @@ def test_logits_with_automatic_segments():
     gpu.update({k: np64(v) for k, v in gr.items()})
     ref = oracle_ref(inp, wl)
     compare(gpu, ref, wl.dtype, ["o", "ht", "dq", "dk", "dv", "dg", "db", "dw", "dh0"])
+
+
+@pytest.mark.parametrize("p", [CASES[1], CASES[5]], ids=_id)
+def test_logits_in_the_tails(p):
+    """A fifth of the logits far in the tails: z_b, z_w = +-30 (gates exactly off or fully on,
+    zero derivative), z_g from -30 (no decay) to 12 (decay g_scale * 12 per token, inside the
+    supported range); the rest as drawn. Forward and backward against the oracle."""
+    wl = _wl(p)
+    inp = make_inputs(wl, gates="logits")
+    if inp["h0"] is None:
+        inp["h0"] = torch.zeros(wl.B, wl.H, wl.DK, wl.DV)
+    rng = np.random.default_rng(77)
+    for n, lo, hi in (("zb", None, None), ("zw", None, None), ("zg", -30.0, 12.0)):
+        z = inp[n].float().numpy().copy()
+        m = rng.random(z.shape) < 0.2
+        if lo is None:
+            z[m] = np.where(rng.random(int(m.sum())) < 0.5, -30.0, 30.0)
+        else:
+            z[m] = rng.uniform(lo, hi, int(m.sum()))
+        inp[n] = torch.from_numpy(z).to(inp[n].dtype)
+    dht = torch.from_numpy(np.random.default_rng(9).standard_normal((wl.B, wl.H, wl.DK, wl.DV))).float()
+    args = gpu_args(inp)
+    h0, do = inp["h0"].cuda(), inp["do"].cuda()
+    sc = dict(g_scale=wl.g_scale, b_scale=wl.b_scale)
+    o, ht, ws = g2.gdr2_fwd_logits(*args, h0, save_for_bwd=True, **sc)
+    gr = g2.gdr2_bwd_logits(*args, h0, do, dht.cuda(), ws=ws, fwd_saved=True, **sc)
+    torch.cuda.synchronize()
+    gpu = {"o": np64(o), "ht": np64(ht)}
+    gpu.update({k: np64(v) for k, v in gr.items()})
+    for k, v in gpu.items():
+        assert np.all(np.isfinite(v)), k
+    ref = oracle_ref(inp, wl, dht=dht)
+    compare(gpu, ref, wl.dtype, ["o", "ht", "dq", "dk", "dv", "dg", "db", "dw", "dh0"])
