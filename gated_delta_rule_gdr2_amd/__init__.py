@@ -137,6 +137,18 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _keep_for(stream, *tensors):
+    """Tensors allocated here come from torch's current stream; when the kernels run on
+    another stream, tell the caching allocator that this stream uses them too, so that their
+    memory is not handed out again (after the caller, or this module, drops them) before the
+    work enqueued on that stream has finished with it."""
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def workspace(B, T, H, dk, dv, dtype, train, device="cuda", segments=None):
     """Allocate a workspace tensor (uint8) big enough for gdr2_fwd(save_for_bwd=train) / gdr2_bwd
     (segments=None), or for their _seg variants with that many segments."""
@@ -185,12 +197,17 @@ def _fwd(scales, q, k, v, g, b, w, h0, chunk, save_for_bwd, ws, o, output_final_
                       (b, "b", (B, T, H, dk)), (v, "v", (B, T, H, dv)), (w, "w", (B, T, H, dv))):
         _check(t, n, q.dtype, shp)
     _check(h0, "h0", torch.float32, (B, H, dk, dv))
+    new = []
     if o is None:
         o = torch.empty(B, T, H, dv, dtype=q.dtype, device=q.device)
+        new.append(o)
     _check(o, "o", q.dtype, (B, T, H, dv))
     ht = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device) if output_final_state else None
+    new.append(ht)
     if ws is None:
         ws = workspace(B, T, H, dk, dv, dt, save_for_bwd, q.device, segments)
+        new.append(ws)
+    _keep_for(stream, *new)
     tail = (_ptr(h0), _ptr(o), _ptr(ht), B, T, H, dk, dv, chunk, dt, int(bool(save_for_bwd)), _ptr(ws),
             ws.numel(), _stream(stream), stage_events)
     if segments is not None:
@@ -228,6 +245,7 @@ def _step(scales, q, k, v, g, b, w, state, o, stream):
     _check(state, "state", torch.float32, (B, H, dk, dv))
     if o is None:
         o = torch.empty(B, T, H, dv, dtype=q.dtype, device=q.device)
+        _keep_for(stream, o)
     _check(o, "o", q.dtype, (B, T, H, dv))
     tail = (_ptr(state), _ptr(o), B, T, H, dk, dv, dt, _stream(stream))
     if scales is None:
@@ -274,14 +292,19 @@ def _bwd(scales, q, k, v, g, b, w, h0, dout, dht, chunk, ws, fwd_saved, need_dh0
         _check(t, n, q.dtype, shp)
     _check(h0, "h0", torch.float32, (B, H, dk, dv))
     _check(dht, "dht", torch.float32, (B, H, dk, dv))
+    new = []
     if grads is None:
         grads = {n: torch.empty_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("db", b),
                                                      ("dw", w))}
+        new += list(grads.values())
     grads["dh0"] = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device) if need_dh0 else None
+    new.append(grads["dh0"])
     if ws is None:
         if fwd_saved:
             raise ValueError("fwd_saved=True needs the forward's workspace")
         ws = workspace(B, T, H, dk, dv, dt, True, q.device, segments)
+        new.append(ws)  # dropped on return: its memory must outlive the kernels on `stream`
+    _keep_for(stream, *new)
     tail = (_ptr(h0), _ptr(dout), _ptr(dht), _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]),
             _ptr(grads["dg"]), _ptr(grads["db"]), _ptr(grads["dw"]), _ptr(grads["dh0"]), B, T, H, dk, dv, chunk,
             dt, int(bool(fwd_saved)), _ptr(ws), ws.numel(), _stream(stream), stage_events)

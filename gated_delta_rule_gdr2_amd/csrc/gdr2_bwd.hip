@@ -12,10 +12,17 @@
 //                   dX = dY (dv = dY*w, dw = dY*v),
 //                   plus the back-propagation of the two decay-scaled bilinear
 //                   forms A = (b*k, k) and M = (q, k) with the gates inside.
-// The log-decay gradient follows elementwise: gam enters only through the
-// factors of q, b*k and k, so dgam = q*dq + 2*b*db - k*dk on every row, plus
-// at the chunk's last row the scaling of the carried state,
-// sum_r dKd*Kd + exp(gam_C) * rowsum(dS' * S); dg is its reverse running sum.
+// The log-decay gradient: gam enters only through the factors Qg = q*exp(gam),
+// Kb = b*k*exp(gam), Khat = k*exp(-gam) and Kd = k*exp(gam_C - gam), and through
+// the carried state's exp(gam_C). dg_t (the gradient of g at token t = sum over
+// the rows r >= t of the gradient of gam_r) is assembled from terms that never
+// cancel, so it stays accurate when it is tiny (strong decay):
+//   dg_t = sum_{r >= t} (Qg.dQg + Kb.dKb - Khat.dKhat)_r      (suffix sum)
+//        + sum_{r < t} (Kd.dKd)_r                             (exclusive prefix sum)
+//        + exp(gam_C) * rowsum(dS' * S)
+// (the Kd term enters gam_r with a minus sign and gam_C with a plus sign, so only
+// rows before t keep it; the diagonal of dM, q_r . k_r, does not depend on the
+// decay and is left out).
 //
 // Kernels:
 //   k_bwd_chain : (gdr2_chain.hip) one workgroup per (sequence, 16-column value
@@ -46,12 +53,13 @@ struct BwdLds {  // all matrices are swizzled tiles (see swz())
     static constexpr int DM = DA + CH * CH * ES;
     static constexpr int F = DM + CH * CH * ES;
     static constexpr int DMD = F + F_ROWS * DK * 4;  // diagonal of dM, fp32
-    static constexpr int CARRY = DMD + CH * 4;       // per key channel, fp32: sum dKd*Kd, rowsum(dS'*S)
+    static constexpr int CARRY = DMD + CH * 4;       // per key channel, fp32: rowsum(dS'*S) (at DK + channel)
     static constexpr int G = CARRY + 2 * DK * 4;     // g, q, k, b of the chunk [CH][DK]
     static constexpr int Q = G + KMAT;
     static constexpr int K = Q + KMAT;
     static constexpr int B = K + KMAT;
-    static constexpr int BYTES = B + KMAT;
+    static constexpr int FLAG = B + KMAT;  // one int per wave: strong decay seen
+    static constexpr int BYTES = FLAG + 32;
 };
 
 // tile dump [DV/16][4][64 lanes][4] -> swizzled LDS tile [CH][DV], in two steps so the
@@ -214,13 +222,15 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         for (int t = 0; t < 4; ++t) lds_get4<OT>(v.p + v.off(16 * t + li, ch0), out[t]);
     };
 
-    // ---- phase 1: cumulative decay and factors; Delta, dY into LDS
+    // ---- phase 1: block sums of the log-decay (see gdr2_intra_common.hpp) and factors;
+    // Delta, dY into LDS. gam keeps this lane's log-decays (activated) for the later phases.
     float gam[CPW][4][4];
+    float span = 0.f;  // largest s(R, R) exponent of this lane's channels
 #pragma unroll
     for (int ac = 0; ac < CPW; ++ac) {
         if (wv + NW * ac >= DK / 16) break;
         const int ch0 = 16 * (wv + NW * ac) + 4 * lq;
-        float gv[4][4], g0[4][4], ge[4][4];
+        float gv[4][4], gf[4][4], gt[4][4], gi[4][4];
         rows4(vG, ch0, gv);
         if (ACT) {
             // Gates given as logits, activated once here for this wave's columns: g from
@@ -244,9 +254,18 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
                 lds_put4<OT>(sB + vB.off(16 * t + li, ch0), bv[t]);
             }
         }
-        gamma_scan(gv, gam[ac], g0, ge);
+        gamma_scan(gv, gf, gt, gi);
+        span = fmaxf(span, diag_span(gi));
         RowExp rx;
-        row_exps<DK>(sF, ch0, g0, ge, rx);
+        row_exps<DK>(sF, ch0, gf, gt, gi, rx);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gam[ac][t][i] = gv[t][i];
+    }
+    {  // every wave reports whether a diagonal block of its channels needs the slow path
+        const bool strong = __ballot(span > span_max<OT>()) != 0;
+        if (l == 0) lds_store<int>(smem + LS::FLAG + 4 * wv, strong ? 1 : 0);
     }
     undump_store<OT, DV, NTHR>(rdl, sDL);
     undump_store<OT, DV, NTHR>(rdy, sDY);
@@ -258,6 +277,15 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         }
     }
     sync_lds();  // LDS only: the later loads stay in flight
+    // Strong decay (slow path): the diagonal block pairs of the bilinear products are left
+    // out of phase 3c (their factor s(R, R) is set to zero here; it may be infinite) and
+    // added in the finals from per-element exponentials instead.
+    bool slow = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) slow |= lds_load<int>(smem + LS::FLAG + 4 * w) != 0;
+    if (slow)
+        for (int e = tid; e < NBLK * DK; e += NTHR)
+            lds_store<float>(sF + ((F_S + pair_id(e / DK, e / DK)) * DK + e % DK) * 4, 0.f);
 
     // ---- phase 2: dA = -strict_lower(dY Delta^T), dM = lower(dO Delta^T)
     // The diagonal of M, q_r . k_r, does not depend on the decay; its gradient is
@@ -291,13 +319,13 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     // Per key-channel tile, transposed tiles (rows = key channel, columns = token):
     //   Pq = exp(gam_R0) * (dO S^T)^T, Pb = -exp(gam_R0) * (dY S^T)^T,
     //   Pk = exp(gam_C - gam_Rend) * (Delta dS'^T)^T
-    // The bilinear terms are accumulated into the same registers in phase 3c.
-    f32x4 Pq[CPW][4], Pb[CPW][4], Pk[CPW][4];
-    // Two per-channel sums go from here to the finals: in registers, or through LDS (sCarry)
-    // when the gates come as logits, where the registers would not hold them.
+    // The bilinear terms are accumulated into Pq, Pb and (the key side, starting from zero)
+    // Pk in phase 3c; the carried-state term of the key side stays apart in PkS.
+    f32x4 Pq[CPW][4], Pb[CPW][4], Pk[CPW][4], PkS[CPW][4];
+    // A per-channel sum goes from here to the finals: in registers, or through LDS (sCarry)
+    // when the gates come as logits, where the registers would not hold it.
     constexpr bool CARRY_LDS = ACT;
     f32x4 rsum[CPW];  // S dS'^T over this wave's 16 key channels; its diagonal is rowsum(dS' * S)
-    float kdx[CPW][4];
     lds_char* sCarry = smem + LS::CARRY;
 #pragma unroll
     for (int ac = 0; ac < CPW; ++ac) {
@@ -322,14 +350,6 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             for (int i = 0; i < 4; ++i)
                 if (li == 4 * lq + i) lds_store<float>(sCarry + (DK + 16 * at + li) * 4, sd[i]);
         }
-        float g0[4][4], ge[4][4];
-#pragma unroll
-        for (int R = 0; R < 4; ++R)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                g0[R][i] = row_bcast<0>(gam[ac][R][i]);
-                ge[R][i] = row_bcast<15>(gam[ac][R][i]);
-            }
         const int ch0 = 16 * at + 4 * lq;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -347,19 +367,10 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             for (int i = 0; i < 4; ++i) {
                 Pq[ac][t][i] = e0v[i] * q4[i];
                 Pb[ac][t][i] = -e0v[i] * b4[i];
-                Pk[ac][t][i] = ecv[i] * k4[i];
+                PkS[ac][t][i] = ecv[i] * k4[i];
+                Pk[ac][t][i] = 0.f;
             }
         }
-        // sum over the chunk's tokens of dKd * Kd (Kd = k * exp(gam_C - gam)), per channel
-        float kx[4] = {0.f, 0.f, 0.f, 0.f}, kv[4][4];
-        rows4(vK, ch0, kv);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) kx[i] += Pk[ac][t][i] * kv[t][i] * __expf(ge[t][i] - gam[ac][t][i]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kx[i] = kdx[ac][i] = row_sum16(kx[i]);
-        if (CARRY_LDS && li == 0) lds_put4<float>(sCarry + ch0 * 4, kx);
     }
     // dv = dY * w, dw = dY * v, in the row-piece layout of v and w
 #pragma unroll
@@ -386,19 +397,11 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     for (int ac = 0; ac < CPW; ++ac) {
         if (wv + NW * ac >= DK / 16) break;
         const int ch0 = 16 * (wv + NW * ac) + 4 * lq;
-        float g0[4][4], ge[4][4];
-#pragma unroll
-        for (int R = 0; R < 4; ++R)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                g0[R][i] = row_bcast<0>(gam[ac][R][i]);
-                ge[R][i] = row_bcast<15>(gam[ac][R][i]);
-            }
         float qv[4][4], kv[4][4], bv[4][4];
         rows4(vQ, ch0, qv);
         rows4(vK, ch0, kv);
         rows4(vB, ch0, bv);  // (activated in phase 1 when the gates came as logits)
-        scaled_factors_from<OT, DK, false>(qv, kv, bv, ch0, gam[ac], g0, ge, sXA, sXM, sY, nullptr, nullptr, nullptr);
+        scaled_factors_from<OT, DK, false>(qv, kv, bv, ch0, gam[ac], sXA, sXM, sY, nullptr, nullptr, nullptr);
     }
     sync_lds();
 
@@ -471,19 +474,75 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
 
         // finals at (key channel 16at + 4lq + i, token 16t + li)
         const int ch0 = 16 * at + 4 * lq;
-        float g0[4][4], ge[4][4];
-#pragma unroll
-        for (int R = 0; R < 4; ++R)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                g0[R][i] = row_bcast<0>(gam[ac][R][i]);
-                ge[R][i] = row_bcast<15>(gam[ac][R][i]);
-            }
         float qv[4][4], kv[4][4], bv[4][4];
         rows4(vQ, ch0, qv);
         rows4(vK, ch0, kv);
         rows4(vB, ch0, bv);
-        float dgam[4][4];
+        // First the token-side sums in place, without the diagonal of dM: Pq -> dq, Pb -> the
+        // K_b gradient times exp(gam) (gbk), Pk -> the Khat part of dk, PkS -> the Kd part.
+        {
+            float e1[4][4], e2[4][4];
+            block_factors(gam[ac], e1, e2);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    Pq[ac][t][i] = e1[t][i] * Pq[ac][t][i];
+                    Pb[ac][t][i] = e1[t][i] * Pb[ac][t][i];
+                    Pk[ac][t][i] = e2[t][i] * Pk[ac][t][i];
+                    PkS[ac][t][i] = e2[t][i] * PkS[ac][t][i];
+                }
+            }
+        }
+        if (slow) {
+            // Strong decay: the diagonal blocks' terms from per-element factors. With
+            // e(r, j) = exp(gam_r - gam_j) = product of alpha_t = exp(g_t) over t in (j, r]
+            // (<= 1 for j < r), per channel of this lane and token r:
+            //   dq  += sum_{j<r} dM[r][j] k_j e(r, j)
+            //   gbk += sum_{j<r} dA[r][j] k_j e(r, j)
+            //   dk  += sum_{j>r} (dA[j][r] (b k)_j + dM[j][r] q_j) e(j, r)
+            // the values of token j taken from lane j of the row; the products grow one
+            // factor per step, j going down from r for the first two and up from r for dk.
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = 16 * t + li;
+                float al[4], pl[4] = {1.f, 1.f, 1.f, 1.f}, ph[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) al[i] = exp_op<OT>(gam[ac][t][i]);
+#pragma unroll 1
+                for (int j = 15; j >= 0; --j) {  // j < r: e(r, j) = alpha_r ... alpha_{j+1}
+                    const int src1 = (l & 48) | ((j + 1) & 15);
+                    const int cj = 16 * t + j, src = (l & 48) | j;
+                    const float aR = lds_get1<OT>(sDA + swz<OT, CH>(r, cj) * (int)sizeof(OT));
+                    const float mR = lds_get1<OT>(sDM + swz<OT, CH>(r, cj) * (int)sizeof(OT));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float a1 = __shfl(al[i], src1, 64);
+                        const float kj = __shfl(kv[t][i], src, 64);
+                        if (j + 1 <= li) pl[i] *= a1;
+                        const float lo = j < li ? pl[i] : 0.f;
+                        Pq[ac][t][i] = fmaf(mR * kj, lo, Pq[ac][t][i]);
+                        Pb[ac][t][i] = fmaf(aR * kj, lo, Pb[ac][t][i]);
+                    }
+                }
+#pragma unroll 1
+                for (int j = 0; j < 16; ++j) {  // j > r: e(j, r) = alpha_{r+1} ... alpha_j
+                    const int cj = 16 * t + j, src = (l & 48) | j;
+                    const float aC = lds_get1<OT>(sDA + swz<OT, CH>(cj, r) * (int)sizeof(OT));
+                    const float mC = lds_get1<OT>(sDM + swz<OT, CH>(cj, r) * (int)sizeof(OT));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float aj = __shfl(al[i], src, 64);
+                        const float qj = __shfl(qv[t][i], src, 64);
+                        const float bkj = __shfl(bv[t][i] * kv[t][i], src, 64);
+                        if (j > li) ph[i] *= aj;
+                        const float hi = j > li ? ph[i] : 0.f;
+                        Pk[ac][t][i] = fmaf(aC * bkj + mC * qj, hi, Pk[ac][t][i]);
+                    }
+                }
+            }
+        }
+        float dgp[4][4], kk[4][4];  // per row: Qg.dQg + Kb.dKb - Khat.dKhat, and Kd.dKd
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int r = 16 * t + li;
@@ -491,13 +550,12 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             float dq[4], dk[4], db[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float e1 = __expf(gam[ac][t][i] - g0[t][i]);
-                const float e2 = __expf(ge[t][i] - gam[ac][t][i]);
-                const float gbk = e1 * Pb[ac][t][i];
-                dq[i] = e1 * Pq[ac][t][i] + dmd * kv[t][i];
+                const float gbk = Pb[ac][t][i];
                 db[i] = gbk * kv[t][i];
-                dk[i] = gbk * bv[t][i] + e2 * Pk[ac][t][i] + dmd * qv[t][i];
-                dgam[t][i] = qv[t][i] * dq[i] + 2.f * bv[t][i] * db[i] - kv[t][i] * dk[i];
+                dgp[t][i] = qv[t][i] * Pq[ac][t][i] + bv[t][i] * db[i] - kv[t][i] * Pk[ac][t][i];
+                kk[t][i] = kv[t][i] * PkS[ac][t][i];
+                dq[i] = Pq[ac][t][i] + dmd * kv[t][i];
+                dk[i] = gbk * bv[t][i] + Pk[ac][t][i] + PkS[ac][t][i] + dmd * qv[t][i];
             }
             if (ACT) {  // db through the erase gate's scaled sigmoid: b_scale s (1 - s), s = b / b_scale
                 const float rb = 1.f / a.b_scale;
@@ -510,25 +568,34 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             lds_put4<OT>(sK + o, dk);
             lds_put4<OT>(sB + o, db);
         }
-        // scaling of the carried state at the chunk's last row: sum_r dKd*Kd + exp(gam_C) rowsum(dS'*S)
+        // dg_t = suffix sum of dgp from t + exclusive prefix sum of kk before t + the carried
+        // state's term exp(gam_C) rowsum(dS' * S), per channel (blocks of 16 rows, then
+        // carries across the blocks; no subtraction anywhere)
+        float cst[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            // row sum of channel ch0 + i, and the dKd*Kd sum of that channel
             const float rs_i = CARRY_LDS ? lds_load<float>(sCarry + (DK + ch0 + i) * 4)
                                          : __shfl(rsum[ac][i], (l & 48) | (4 * lq + i), 64);
-            const float kd_i = CARRY_LDS ? lds_load<float>(sCarry + (ch0 + i) * 4) : kdx[ac][i];
-            const float extra = kd_i + __expf(ge[3][i]) * rs_i;
-            if (li == 15) dgam[3][i] += extra;
+            const float gamC = (row_sum16(gam[ac][0][i]) + row_sum16(gam[ac][1][i])) +
+                               (row_sum16(gam[ac][2][i]) + row_sum16(gam[ac][3][i]));  // the chunk's total
+            cst[i] = __expf(gamC) * rs_i;
         }
-        // dg = reverse running sum of dgam over the chunk's tokens
-        float tot[4] = {0.f, 0.f, 0.f, 0.f}, pre[4][4];
+        float later[4] = {0.f, 0.f, 0.f, 0.f}, before[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 3; t >= 0; --t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = row_suffix16(dgp[t][i]) + later[i];
+                dgp[t][i] = x;
+                later[i] = row_bcast<0>(x);
+            }
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float x = row_scan16(dgam[t][i]) + tot[i];
-                pre[t][i] = x;
-                tot[i] = row_bcast<15>(x);
+                const float x = row_scan16(row_shr1(kk[t][i])) + before[i];
+                before[i] = row_bcast<15>(x + kk[t][i]);
+                kk[t][i] = x;
             }
         float gf[4][4];  // ACT: d g / d z, left in the g tile by phase 1
         if (ACT) rows4(vG, ch0, gf);
@@ -537,7 +604,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             float dg[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                dg[i] = tot[i] - pre[t][i] + dgam[t][i];
+                dg[i] = dgp[t][i] + kk[t][i] + cst[i];
                 if (ACT) dg[i] *= gf[t][i];
             }
             lds_put4<OT>(sG + vG.off(16 * t + li, ch0), dg);

@@ -141,6 +141,13 @@ __device__ __forceinline__ void gate_softplus_sigmoid(float z, float& sp, float&
     const float r = sizeof(OT) == 4 ? 1.f / (1.f + e) : __builtin_amdgcn_rcpf(1.f + e);
     sg = z >= 0.f ? r : e * r;
 }
+// exp in the operand path's precision: the accurate library exp for fp32 operands, the
+// hardware approximation for bf16 (its error is far below bf16 rounding)
+template <class OT>
+__device__ __forceinline__ float exp_op(float x) {
+    if constexpr (sizeof(OT) == 4) return expf(x);
+    else return __expf(x);
+}
 enum GateKind { GATE_G, GATE_B, GATE_W };
 template <class OT, int KIND>
 __device__ __forceinline__ float gate_act(float z, float g_scale, float b_scale) {
@@ -492,6 +499,30 @@ __device__ __forceinline__ float row_scan16(float x) {
     v = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, false);  // row_shr:8
     x += __int_as_float(v);
     return x;
+}
+// inclusive suffix sum across the 16 lanes of each DPP row (lane li gets the sum over
+// lanes li .. 15)
+__device__ __forceinline__ float row_suffix16(float x) {
+    int v;
+    v = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x101, 0xF, 0xF, false);  // row_shl:1
+    x += __int_as_float(v);
+    v = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x102, 0xF, 0xF, false);  // row_shl:2
+    x += __int_as_float(v);
+    v = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x104, 0xF, 0xF, false);  // row_shl:4
+    x += __int_as_float(v);
+    v = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x108, 0xF, 0xF, false);  // row_shl:8
+    x += __int_as_float(v);
+    return x;
+}
+// value of the next lane of the row (lane 15 gets 0): with row_suffix16 an exclusive suffix
+// sum that never subtracts
+__device__ __forceinline__ float row_shl1(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x101, 0xF, 0xF, false));
+}
+// value of the previous lane of the row (lane 0 gets 0): with row_scan16 an exclusive prefix
+// sum that never subtracts
+__device__ __forceinline__ float row_shr1(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, false));
 }
 // value held by lane SRC of the caller's 16-lane row (DPP row_newbcast, a VALU move)
 template <int SRC>

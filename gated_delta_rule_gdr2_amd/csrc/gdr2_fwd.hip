@@ -38,7 +38,12 @@ struct FwdLds {  // all matrices are swizzled tiles (see swz())
     static constexpr int SLOTY = SLOTM + SLOT;  // Y, later T
     static constexpr int X = SLOTY + SLOT;
     static constexpr int F = X + CH * DV * ES;
-    static constexpr int BYTES = F + F_ROWS * DK * 4;
+    static constexpr int FLAG = F + F_ROWS * DK * 4;  // one int per wave: strong decay seen
+    static constexpr int BYTES = FLAG + 16;
+    // slow-path scratch: exp(g) of one block's rows [16][DK] fp32 over F, b*k [16][DK] fp32
+    // then q, k [16][DK] in the operand type over the Y/T slot (both dead then)
+    static_assert(16 * DK * 4 <= F_ROWS * DK * 4, "slow-path decay rows fit in the factor area");
+    static_assert(16 * DK * 4 + 2 * 16 * DK * ES <= SLOT, "slow-path rows fit in the Y/T slot");
 };
 
 // Blocked inverse of the unit lower-triangular (I + A), A in sA (fp32), into sT.
@@ -91,6 +96,78 @@ __device__ __forceinline__ void blocked_inverse(const lds_char* sA, lds_char* sT
     }
 }
 
+// Slow path for strong decay: the four diagonal 16x16 blocks of A and M from per-element
+// factors exp(gam_r - gam_i) = product of alpha_t = exp(g_t) over t in (i, r] (each <= 1,
+// so nothing overflows, and no running sums are subtracted), exact for any decay,
+// instead of the block-split factors whose s(R, R) overflows. Block by block, the block's
+// rows are staged -- alpha in fp32 (sD), b*k in fp32 and q, k in the operand type (sS)
+// -- and thread (r, i) of the block's 16 x 16 entries sums over the key channels
+//   A[r][i] = sum_c (b k)_{r,c} k_{i,c} prod_{t in (i, r]} alpha_{t,c}   (i < r, else 0)
+//   M[r][i] = sum_c q_{r,c} k_{i,c} prod_{t in (i, r]} alpha_{t,c}       (i <= r, else 0)
+// in a fixed channel order (staggered by i so that the 16 lanes of a row group read
+// different LDS banks). A goes to its fp32 LDS tile, M to the workspace.
+template <class OT, int DK, bool ACT>
+__device__ __forceinline__ void fwd_diag_exact(const Args& a, size_t rowk0, int nvalid, lds_char* sD, lds_char* sS,
+                                               lds_char* sA, OT* m_out) {
+    const int tid = threadIdx.x;
+    const size_t rsk = (size_t)a.H * DK;
+    const OT* gp = (const OT*)a.g + rowk0 * DK;
+    const OT* qp = (const OT*)a.q + rowk0 * DK;
+    const OT* kp = (const OT*)a.k + rowk0 * DK;
+    const OT* bp = (const OT*)a.b + rowk0 * DK;
+    lds_char* sBK = sS;                      // [16][DK] fp32
+    lds_char* sQ = sS + 16 * DK * 4;         // [16][DK] OT
+    lds_char* sK = sQ + 16 * DK * sizeof(OT);
+    const int r = tid >> 4, i = tid & 15;
+#pragma unroll 1
+    for (int R = 0; R < NBLK; ++R) {
+#pragma unroll 1
+        for (int e = tid; e < 16 * DK; e += 256) {
+            const int rr = e / DK, c = e % DK, row = 16 * R + rr;
+            const bool ok = row < nvalid;  // padding rows: g = 0 (alpha = 1), q = k = b = 0
+            const size_t off = (size_t)row * rsk + c;
+            float gv = ok ? to_f(gp[off]) : 0.f;
+            if (ACT && ok) gv = gate_act<OT, GATE_G>(gv, a.g_scale, a.b_scale);
+            const float kv = ok ? to_f(kp[off]) : 0.f, qv = ok ? to_f(qp[off]) : 0.f;
+            float bv = ok ? to_f(bp[off]) : 0.f;
+            if (ACT && ok) bv = gate_act<OT, GATE_B>(bv, a.g_scale, a.b_scale);
+            lds_store<float>(sD + e * 4, exp_op<OT>(gv));
+            lds_store<float>(sBK + e * 4, bv * kv);
+            lds_store<OT>(sQ + e * sizeof(OT), to_ot<OT>(qv));
+            lds_store<OT>(sK + e * sizeof(OT), to_ot<OT>(kv));
+        }
+        sync_lds();
+        float am = 0.f, mm = 0.f;
+        if (i <= r) {
+#pragma unroll 1
+            for (int cc = 0; cc < DK; cc += 4) {
+                const int c = (cc + 4 * i) & (DK - 1);
+                float pr[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll 1
+                for (int t = i + 1; t <= r; ++t) {
+                    float al[4];
+                    lds_get4<float>(sD + (t * DK + c) * 4, al);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) pr[u] *= al[u];
+                }
+                float bk[4], qr[4], ki[4];
+                lds_get4<float>(sBK + (r * DK + c) * 4, bk);
+                lds_get4<OT>(sQ + (r * DK + c) * sizeof(OT), qr);
+                lds_get4<OT>(sK + (i * DK + c) * sizeof(OT), ki);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float ke = ki[u] * pr[u];
+                    am = fmaf(bk[u], ke, am);
+                    mm = fmaf(qr[u], ke, mm);
+                }
+            }
+        }
+        lds_store<float>(sA + swz<float, CH>(16 * R + r, 16 * R + i) * 4, i < r ? am : 0.f);
+        m_out[swz<OT, CH>(16 * R + r, 16 * R + i)] = to_ot<OT>(i <= r ? mm : 0.f);
+        sync_lds();
+    }
+}
+
 // upper 16x16 block (R, I), I > R, number u = 0..5
 __device__ __forceinline__ void upper_ri(int u, int& R, int& I) {
     R = u < 3 ? 0 : (u < 5 ? 1 : 2);
@@ -139,6 +216,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
         constexpr int NA = (NGK + 3) / 4, NJ = (NGV + 3) / 4;
         using RT = typename Raw16<OT>::type;
         RT rg[NA][4], rq[NA][4], rk[NA][4], rb[NA][4], rv[NJ][4], rw[NJ][4];
+        float span = 0.f;  // largest s(R, R) exponent of this lane's channels
 #pragma unroll
         for (int ai = 0; ai < NA; ++ai) {
             if (wv + 4 * ai >= NGK) break;
@@ -161,19 +239,20 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
 #pragma unroll
             for (int hq = 0; hq < W / 4; ++hq) {
                 const int ch0 = GC * (wv + 4 * ai) + W * lq + 4 * hq;
-                float gv[4][4], gam[4][4], g0[4][4], ge[4][4];
+                float gv[4][4], gf[4][4], gt[4][4], gi[4][4];
                 cvt_rows16<OT>(rg[ai], hq, nvalid, gv);
                 if (ACT) activate_rows<OT, GATE_G>(gv, nvalid, a.g_scale, a.b_scale);
-                gamma_scan(gv, gam, g0, ge);
+                gamma_scan(gv, gf, gt, gi);
+                span = fmaxf(span, diag_span(gi));
                 RowExp rx;
-                row_exps<DK>(sF, ch0, g0, ge, rx);
+                row_exps<DK>(sF, ch0, gf, gt, gi, rx);
                 if (li == 1) st4(gc_out + ch0, rx.x1);  // exp(gam_C)
                 float qv[4][4], kv[4][4], bv[4][4];
                 cvt_rows16<OT>(rq[ai], hq, nvalid, qv);
                 cvt_rows16<OT>(rk[ai], hq, nvalid, kv);
                 cvt_rows16<OT>(rb[ai], hq, nvalid, bv);
                 if (ACT) activate_rows<OT, GATE_B>(bv, nvalid, a.g_scale, a.b_scale);
-                scaled_factors_from<OT, DK, true>(qv, kv, bv, ch0, gam, g0, ge, sXA, sXM, sY, qg_out, kd_out, &rx);
+                scaled_factors_from<OT, DK, true>(qv, kv, bv, ch0, gv, sXA, sXM, sY, qg_out, kd_out, &rx);
             }
         }
 #pragma unroll
@@ -188,8 +267,13 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
                 x_tile_from<OT, DV>(vv, ww, GC * (wv + 4 * ji) + W * lq + 4 * hq, sX);
             }
         }
+        // every wave reports whether a diagonal block of its channels needs the slow path
+        const bool strong = __ballot(span > span_max<OT>()) != 0;
+        if (l == 0) lds_store<int>(smem + LS::FLAG + 4 * wv, strong ? 1 : 0);
     }
     sync_lds();
+    const bool slow = (lds_load<int>(smem + LS::FLAG) | lds_load<int>(smem + LS::FLAG + 4) |
+                       lds_load<int>(smem + LS::FLAG + 8) | lds_load<int>(smem + LS::FLAG + 12)) != 0;
 
     // ---- phase 2a: M = lower(Qg Khat^T), computed as M^T tiles, out to global
     const LSwz<OT, DK> vXA{sXA}, vXM{sXM}, vY{sY};
@@ -197,6 +281,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
     for (int p = wv; p < NPAIR; p += 4) {
         int R, I;
         pair_ri(p, R, I);
+        if (slow && R == I) continue;  // written by the slow path
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -219,6 +304,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
     for (int p = wv; p < NPAIR; p += 4) {
         int R, I;
         pair_ri(p, R, I);
+        if (slow && R == I) continue;  // written by the slow path
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -253,6 +339,13 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
             for (int i = 0; i < EPC; ++i) x[i] = to_ot<OT>((float)x[i] * f[i]);
             lds_store<RT>(p, x);
         }
+    }
+
+    // ---- strong decay: the diagonal blocks of A and M, exactly (the factor rows in sF and
+    // the Y slot are dead once K_b has been formed)
+    if (slow) {
+        sync_lds();
+        fwd_diag_exact<OT, DK, ACT>(a, rowk0, nvalid, sF, sT, sA, m_out);
     }
 
     // ---- phase 3: T = (I + A)^-1

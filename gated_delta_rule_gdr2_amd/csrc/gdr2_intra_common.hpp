@@ -12,6 +12,16 @@
 //   E1_r = exp(gam_r - gam_R0)   (<= 1; R0 = first row of r's block R)
 //   E2_i = exp(gam_Iend - gam_i) (<= 1; Iend = last row of i's block I)
 //   s(R, I) = exp(gam_R0 - gam_Iend) (<= 1 for I < R; covers < 16 tokens for I = R)
+// Every exponent is formed as a sum of exactly the log-decays it spans -- E1_r from
+// the block's g summed over (R0, r], E2_i over (i, Iend], s(R, I) from the first g of
+// block R and the totals of the blocks in between -- never as a difference of two
+// running sums, so an exponent carries the rounding of its own terms only, however
+// large the decay elsewhere in the chunk.
+// For I = R the factor s(R, R) = exp(-(sum of g over (R0, Rend])) >= 1 grows with the
+// decay inside the block. When it passes exp(span_max()) somewhere in the chunk
+// (strong decay), the kernels compute the four diagonal 16x16 blocks from
+// per-element factors exp(gam_r - gam_i) = product of exp(g_t) over t in (i, r], each
+// <= 1, instead ("slow path"), which is exact for any decay.
 // Lane layout of these phases: wave w owns key-channel tiles w, w + NW, ...
 // and lane (li, lq) holds channels 16a + 4lq + (0..3) of token rows 16t + li,
 // t = 0..3 -- the accumulator-tile layout of a (channel x time) product, so the
@@ -113,28 +123,54 @@ __device__ __forceinline__ void lds_put4(lds_char* p, const float v[4]) {
     }
 }
 
-// Per-lane cumulative log-decay for channel tile `at` (4 channels ch0..ch0+3, rows 16t+li)
-// from the log-decays gv[t][i] of those rows: gam[t][i] (inclusive running sum over the
-// chunk), g0[R][i] = gam at row 16R, ge[R][i] = gam at row 16R+15.
-__device__ __forceinline__ void gamma_scan(const float (&gv)[4][4], float (&gam)[4][4], float (&g0)[4][4],
-                                           float (&ge)[4][4]) {
-    float run[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float x = row_scan16(gv[t][i]) + run[i];
-            gam[t][i] = x;
-            run[i] = row_bcast<15>(x);
-        }
+// Per-lane block sums of the log-decay for channel tile `at` (4 channels ch0..ch0+3,
+// rows 16t+li) from the log-decays gv[t][i] of those rows: f[R][i] = g at row 16R (the
+// block's first), tot[R][i] = sum of g over the block, inn[R][i] = sum of g over the
+// block without its first row (so s(R, R) = exp(-inn)).
+__device__ __forceinline__ void gamma_scan(const float (&gv)[4][4], float (&f)[4][4], float (&tot)[4][4],
+                                           float (&inn)[4][4]) {
+    const bool first = (lane_id() & 15) == 0;
 #pragma unroll
     for (int R = 0; R < 4; ++R)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            g0[R][i] = row_bcast<0>(gam[R][i]);
-            ge[R][i] = row_bcast<15>(gam[R][i]);
+            f[R][i] = row_bcast<0>(gv[R][i]);
+            tot[R][i] = row_sum16(gv[R][i]);
+            inn[R][i] = row_sum16(first ? 0.f : gv[R][i]);
         }
 }
+// E1_r = exp(sum of g over (R0, r]) and E2_r = exp(sum of g over (r, Rend]) of a lane's
+// row r = 16t + li, one channel (inclusive prefix without the block's first row;
+// exclusive suffix).
+__device__ __forceinline__ float block_e1(float g) {
+    return __expf(row_scan16((lane_id() & 15) == 0 ? 0.f : g));
+}
+__device__ __forceinline__ float block_e2(float g) { return __expf(row_suffix16(row_shl1(g))); }
+__device__ __forceinline__ void block_factors(const float (&gv)[4][4], float (&e1)[4][4], float (&e2)[4][4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            e1[t][i] = block_e1(gv[t][i]);
+            e2[t][i] = block_e2(gv[t][i]);
+        }
+}
+// Largest s(R, R) exponent -inn_R of a lane's channels (>= 0 for a decay g <= 0).
+__device__ __forceinline__ float diag_span(const float (&inn)[4][4]) {
+    float m = 0.f;
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, -inn[R][i]);
+    return m;
+}
+// Above this s(R, R) exponent the diagonal blocks take the slow path. bf16 operands:
+// the factors stay far inside the fp32/bf16 range; fp32 operands: the fast path's
+// product of three exponentials keeps about span * 1e-7 relative error, so it stops
+// early enough for the 1e-5 fp32 tolerance.
+template <class OT>
+constexpr float span_max() { return sizeof(OT) == 2 ? 60.f : 12.f; }
+
 // Row-uniform exponentials of four channels ch0..ch0+3. They are the same in all 16
 // lanes of a row, so each lane computes a different one: lane li holds, for channel
 // ch0 + i,
@@ -145,7 +181,10 @@ __device__ __forceinline__ void gamma_scan(const float (&gv)[4][4], float (&gam)
 //          li = 1           exp(gam_C)
 //          li = 2           exp(gam_C - gam_3end) = 1
 // (gam_C = gam at the chunk's last row = gam_3end.) row_bcast moves them to the
-// lanes that use them.
+// lanes that use them. Each exponent is a sum of the block totals tot_J and block
+// first values f_R it spans (gam_R0 - gam_Iend = f_R + sum_{I<J<R} tot_J, gam_R0 =
+// f_R + sum_{J<R} tot_J, gam_C - gam_Rend = sum_{J>R} tot_J; for I = R,
+// gam_R0 - gam_Rend = -inn_R), so no two large running sums are subtracted.
 struct RowExp {
     float x0[4], x1[4];
 };
@@ -181,47 +220,64 @@ __device__ __forceinline__ float rx_ece(const RowExp& x, int R, int i) {
 }
 
 // Computes the row-uniform exponentials and writes the factor arrays of channels
-// ch0..ch0+3 (eR0, eCe and s rows of sF).
+// ch0..ch0+3 (eR0, eCe and s rows of sF) from the block first values f and totals tot.
 template <int DK>
-__device__ __forceinline__ void row_exps(lds_char* sF, int ch0, const float (&g0)[4][4], const float (&ge)[4][4],
-                                         RowExp& x) {
+__device__ __forceinline__ void row_exps(lds_char* sF, int ch0, const float (&f)[4][4], const float (&tot)[4][4],
+                                         const float (&inn)[4][4], RowExp& x) {
     const int li = lane_id() & 15;
-    // lane li's value is exp(A - B): ra = 0..3 -> A = gam_{ra,0}, 4 -> A = gam_C;
-    // ib = 0..3 -> B = gam_{ib,end}, 4 -> B = 0
-    // (all selects, no branches: pair_ri written out for li < NPAIR)
-    const int pr = li >= 6 ? 3 : li >= 3 ? 2 : li >= 1 ? 1 : 0, pi = li - pr * (pr + 1) / 2;
-    const int ra = li < NPAIR ? pr : li < NPAIR + NBLK ? li - NPAIR : 4;
-    const int ib = li < NPAIR ? pi : li < NPAIR + NBLK ? 4 : li - NPAIR - NBLK;
-    const bool a0 = ra == 0, a1 = ra == 1, a2 = ra == 2, a3 = ra == 3;
-    const bool b0 = ib == 0, b1 = ib == 1, b2 = ib == 2, b3 = ib == 3;
+    // Lane li's exponent is -inn_R for a diagonal pair, else (F_R, the first value of
+    // block R, if useF) + sum of tot_J over the J in mask. Lanes: pairs (R, I) in pair_ri
+    // order, then gam_R0 for R = 0..3, then gam_C - gam_Rend for R = 0, 1.
+    //                      li:  0  1  2  3  4  5  6  7  8  9 10 11 12 13 14 15
+    // R (row of F)         :    0  1  1  2  2  2  3  3  3  3  0  1  2  3  -  -
+    // diag                 :    1  0  1  0  0  1  0  0  0  1  0  0  0  0  0  0
+    // mask of tot_J        :    0  0  0  2  0  0  6  4  0  0  0  1  3  7 14 12
+    const int Rof = li < 1 ? 0 : li < 3 ? 1 : li < 6 ? 2 : li < 10 ? 3 : li - 10;  // li >= 14: no F
+    const bool r0 = Rof == 0, r1 = Rof == 1, r2 = Rof == 2, r3 = Rof == 3;  // (selects, no indexing)
+    const bool useF = li < 14;
+    const bool diag = li == 0 || li == 2 || li == 5 || li == 9;
+    const int mask = li == 3 ? 2 : li == 6 ? 6 : li == 7 ? 4 : li == 11 ? 1 : li == 12 ? 3 : li == 13 ? 7
+                   : li == 14 ? 14 : li == 15 ? 12 : 0;
+    const bool m0 = mask & 1, m1 = mask & 2, m2 = mask & 4, m3 = mask & 8;
+    const bool x1a = li == 0, x1b = li == 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float A = ge[3][i], B = 0.f;
-        A = a3 ? g0[3][i] : A;
-        A = a2 ? g0[2][i] : A;
-        A = a1 ? g0[1][i] : A;
-        A = a0 ? g0[0][i] : A;
-        B = b3 ? ge[3][i] : B;
-        B = b2 ? ge[2][i] : B;
-        B = b1 ? ge[1][i] : B;
-        B = b0 ? ge[0][i] : B;
-        x.x0[i] = __expf(A - B);
-        const float B1 = li == 0 ? ge[2][i] : li == 2 ? ge[3][i] : 0.f;
-        x.x1[i] = __expf(ge[3][i] - B1);
+        float F = 0.f, In = 0.f;
+        F = r3 ? f[3][i] : F;
+        F = r2 ? f[2][i] : F;
+        F = r1 ? f[1][i] : F;
+        F = r0 ? f[0][i] : F;
+        In = r3 ? inn[3][i] : In;
+        In = r2 ? inn[2][i] : In;
+        In = r1 ? inn[1][i] : In;
+        In = r0 ? inn[0][i] : In;
+        float e = useF ? F : 0.f;
+        e = diag ? -In : e;
+        e += m0 ? tot[0][i] : 0.f;
+        e += m1 ? tot[1][i] : 0.f;
+        e += m2 ? tot[2][i] : 0.f;
+        e += m3 ? tot[3][i] : 0.f;
+        x.x0[i] = __expf(e);
+        // x1: li 0 -> gam_C - gam_2end = tot_3; li 1 -> gam_C = sum of all totals; else 0
+        const float all = (tot[0][i] + tot[1][i]) + (tot[2][i] + tot[3][i]);
+        float e1 = 0.f;
+        e1 = x1a ? tot[3][i] : e1;
+        e1 = x1b ? all : e1;
+        x.x1[i] = __expf(e1);
     }
     const int row = li < NPAIR ? F_S + li : li < NPAIR + NBLK ? F_ER0 + (li - NPAIR) : F_ECE + (li - NPAIR - NBLK);
     lds_put4<float>(sF + (row * DK + ch0) * 4, x.x0);
     if (li == 0 || li == 2) lds_put4<float>(sF + ((F_ECE + 2 + li / 2) * DK + ch0) * 4, x.x1);
 }
 
-// XA = b*k*E1, XM = q*E1, Y = k*E2 for channel tile rows of this lane, into swizzled LDS
+// XA = b*k*E1, XM = q*E1, Y = k*E2 (E1, E2 from the lane's log-decays gv, see block_e1 /
+// block_e2) for channel tile rows of this lane, into swizzled LDS
 // tiles [CH][DK]; with OUTS also Qg = q*exp(gam) and Kd = k*exp(gam_C - gam) as swizzled
 // tiles in global memory (exp(gam) = E1 * exp(gam_R0), exp(gam_C - gam) = E2 *
 // exp(gam_C - gam_Rend), the row-uniform factors taken from rx).
 template <class OT, int DK, bool OUTS>
 __device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], const float (&kv)[4][4],
-                                                    const float (&bv)[4][4], int ch0, const float (&gam)[4][4],
-                                                    const float (&g0)[4][4], const float (&ge)[4][4],
+                                                    const float (&bv)[4][4], int ch0, const float (&gv)[4][4],
                                                     lds_char* sXA, lds_char* sXM, lds_char* sY, OT* qg_out,
                                                     OT* kd_out, const RowExp* rx) {
     const int li = lane_id() & 15;
@@ -231,8 +287,7 @@ __device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], con
         float xa[4], xm[4], y[4], qg[4], kd[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float e1 = __expf(gam[t][i] - g0[t][i]);
-            const float e2 = __expf(ge[t][i] - gam[t][i]);
+            const float e1 = block_e1(gv[t][i]), e2 = block_e2(gv[t][i]);
             xa[i] = bv[t][i] * kv[t][i] * e1;
             xm[i] = qv[t][i] * e1;
             y[i] = kv[t][i] * e2;

@@ -36,12 +36,12 @@
  * check returns a negative status and enqueues nothing. A failed launch
  * returns GDR2_ERR_HIP. Non-finite inputs are not checked; they propagate.
  *
- * Decay range: the chunkwise kernels split each chunk into 16-token blocks and scale
- * the factors of a block by exp of its cumulative log-decay, which must stay finite
- * in fp32: for every channel, g summed over any 15 consecutive tokens of a block must
- * be above about -88 (an average log-decay above -5.9 per token, decay exp g above
- * 0.0028). Stronger decays give non-finite results. gdr2_step (token by token) has no
- * such bound.
+ * Decay: g is a log-decay (g <= 0, exp g in (0, 1]) of any finite size. The chunkwise
+ * kernels scale their factors by exponentials of the decay summed over 16-token blocks;
+ * where a block's decay is strong enough that the diagonal block factor would leave the
+ * fp32 range, they form that block from per-element decay products instead, so every
+ * finite g <= 0 gives finite results (LIT-802 takeaway 1: the channel-wise decay of
+ * KDA, which bounds no decay strength).
  */
 #ifndef GDR2_H
 #define GDR2_H

@@ -45,16 +45,17 @@ def _pad(x, C):
 def chunk_factors(q, k, g, b, C):
     """Per-chunk factors from the chunk's rows (C x DK each)."""
     gam = np.cumsum(g, axis=0)
-    nb = C // BLK
+    blk = min(BLK, C)  # chunks shorter than a block are one block
+    nb = C // blk
     A = np.zeros((C, C))
     M = np.zeros((C, C))
     for R in range(nb):
-        r0 = R * BLK
-        rr = slice(r0, r0 + BLK)
+        r0 = R * blk
+        rr = slice(r0, r0 + blk)
         E1 = np.exp(gam[rr] - gam[r0])               # <= 1
         for I in range(R + 1):
-            ie = I * BLK + BLK - 1
-            ii = slice(I * BLK, I * BLK + BLK)
+            ie = I * blk + blk - 1
+            ii = slice(I * blk, I * blk + blk)
             s = np.exp(gam[r0] - gam[ie])             # <= 1 for I < R
             y = k[ii] * np.exp(gam[ie] - gam[ii])     # <= |k|
             A[rr, ii] = (b[rr] * k[rr] * E1 * s) @ y.T

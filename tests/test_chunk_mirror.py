@@ -30,7 +30,7 @@ def as4(x):
     return x[None, :, None, :]
 
 
-@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("C", [1, 2, 4, 8, 16, 32, 64])
 @pytest.mark.parametrize("T,gscale", [(64, 0.1), (150, 0.5), (200, 2.0)])
 def test_chunk_forward_equals_oracle(C, T, gscale):
     q, k, v, g, b, w, h0, _, _ = inputs(T + C, T, 16, 12, gscale)
@@ -39,12 +39,12 @@ def test_chunk_forward_equals_oracle(C, T, gscale):
     assert rel(o, oo[0, :, 0]) < 1e-12 and rel(S, So[0, 0]) < 1e-12
 
 
-@pytest.mark.parametrize("C", [16, 64])
+@pytest.mark.parametrize("C", [1, 2, 4, 8, 16, 32, 64])
 @pytest.mark.parametrize("T,gscale", [(64, 0.1), (150, 0.5)])
 def test_chunk_backward_equals_oracle(C, T, gscale):
     q, k, v, g, b, w, h0, do, dht = inputs(7 * T + C, T, 16, 12, gscale)
     gr = chunk_bwd(q, k, v, g, b, w, h0, do, dht, C)
     go = oracle.bwd(as4(q), as4(k), as4(v), as4(g), as4(b), as4(w), h0[None, None], as4(do), dht[None, None])
     for key in ["dq", "dk", "dv", "dg", "db", "dw"]:
-        assert rel(gr[key], go[key][0, :, 0]) < 1e-11, key
-    assert rel(gr["dh0"], go["dh0"][0, 0]) < 1e-11
+        assert rel(gr[key], go[key][0, :, 0]) < 1e-12, key
+    assert rel(gr["dh0"], go["dh0"][0, 0]) < 1e-12

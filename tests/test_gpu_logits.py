@@ -14,6 +14,7 @@ import torch
 import gated_delta_rule_gdr2_amd as g2
 import oracle
 from gated_delta_rule_gdr2_amd.inputs import WORKLOADS, make_inputs, small
+from parity_util import assert_chunks_close, sample_sequences
 
 pytestmark = pytest.mark.gpu
 
@@ -163,10 +164,36 @@ def test_logits_training_shape_full_size():
     torch.cuda.synchronize()
     gpu = {"o": np64(o), "ht": np64(ht)}
     gpu.update({k: np64(v) for k, v in gr.items() if v is not None})
-    rng = np.random.default_rng(wl.seed + 100)
-    sel = sorted({(int(rng.integers(wl.B)), int(rng.integers(wl.H))) for _ in range(2)})
+    sel = sample_sequences(wl)
     ref = oracle_ref(inp, wl, sel=sel)
     compare(gpu, ref, wl.dtype, ["o", "ht", "dq", "dk", "dv", "dg", "db", "dw"], sel=sel)
+    for key in ["o", "dq", "dk", "dv", "dg", "db", "dw"]:
+        for s, rv in zip(sel, ref[key]):
+            bb, h = s
+            assert_chunks_close("%s%s" % (key, s), gpu[key][bb, :, h], np.asarray(rv).reshape(wl.T, -1), wl.dtype,
+                                wl.T)
+
+
+@pytest.mark.parametrize("dtype,DK,DV", [("bf16", 128, 128), ("f32", 64, 64)])
+def test_logits_strong_decay(dtype, DK, DV):
+    """g_scale = 10: g = -10 softplus(zg) runs from about -0.5 to below -30 per token, so
+    most 16-token blocks exceed the range of the block-split factors and take the
+    per-element diagonal path; forward and backward against the oracle, all finite."""
+    wl = small(DK=DK, DV=DV, T=150, dtype=dtype, B=2, H=2, h0_std=0.1, g_scale=10.0, b_scale=2.0, seed=19)
+    inp = make_inputs(wl, gates="logits")
+    dht = torch.from_numpy(np.random.default_rng(9).standard_normal((wl.B, wl.H, wl.DK, wl.DV))).float()
+    args = gpu_args(inp)
+    h0, do = inp["h0"].cuda(), inp["do"].cuda()
+    sc = dict(g_scale=wl.g_scale, b_scale=wl.b_scale)
+    o, ht, ws = g2.gdr2_fwd_logits(*args, h0, save_for_bwd=True, **sc)
+    gr = g2.gdr2_bwd_logits(*args, h0, do, dht.cuda(), ws=ws, fwd_saved=True, **sc)
+    torch.cuda.synchronize()
+    gpu = {"o": np64(o), "ht": np64(ht)}
+    gpu.update({k: np64(v) for k, v in gr.items()})
+    for k, v in gpu.items():
+        assert np.all(np.isfinite(v)), k
+    ref = oracle_ref(inp, wl, dht=dht)
+    compare(gpu, ref, wl.dtype, ["o", "ht", "dq", "dk", "dv", "dg", "db", "dw", "dh0"])
 
 
 def test_logits_with_automatic_segments():
@@ -191,8 +218,8 @@ def test_logits_with_automatic_segments():
 @pytest.mark.parametrize("p", [CASES[1], CASES[5]], ids=_id)
 def test_logits_in_the_tails(p):
     """A fifth of the logits far in the tails: z_b, z_w = +-30 (gates exactly off or fully on,
-    zero derivative), z_g from -30 (no decay) to 12 (decay g_scale * 12 per token, inside the
-    supported range); the rest as drawn. Forward and backward against the oracle."""
+    zero derivative), z_g from -30 (no decay) to 12 (decay g_scale * 12 per token); the rest
+    as drawn. Forward and backward against the oracle."""
     wl = _wl(p)
     inp = make_inputs(wl, gates="logits")
     if inp["h0"] is None:
