@@ -20,9 +20,9 @@ import os
 import torch
 
 __all__ = ["gdr2_fwd", "gdr2_bwd", "gdr2_step", "gdr2_fwd_logits", "gdr2_bwd_logits", "gdr2_step_logits",
-           "gdr2_fwd_seg", "gdr2_bwd_seg", "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes",
-           "gdr2_seg_workspace_bytes", "gdr2_strerror", "gdr2_version", "GDR2Function", "library_path",
-           "load_library"]
+           "gdr2_fwd_seg", "gdr2_bwd_seg", "gdr2_fwd_noalloc", "gdr2_fwd_workspace_bytes",
+           "gdr2_bwd_workspace_bytes", "gdr2_seg_workspace_bytes", "gdr2_strerror", "gdr2_version", "GDR2Function",
+           "library_path", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr2.so")
@@ -31,8 +31,9 @@ _lib = None
 DTYPE_F32, DTYPE_BF16 = 0, 1
 _DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 EXPORTED = ["gdr2_fwd", "gdr2_bwd", "gdr2_step", "gdr2_fwd_logits", "gdr2_bwd_logits", "gdr2_step_logits",
-            "gdr2_fwd_seg", "gdr2_bwd_seg", "gdr2_fwd_workspace_bytes", "gdr2_bwd_workspace_bytes",
-            "gdr2_seg_workspace_bytes", "gdr2_strerror", "gdr2_version"]
+            "gdr2_fwd_seg", "gdr2_bwd_seg", "gdr2_fwd_noalloc", "gdr2_fwd_workspace_bytes",
+            "gdr2_bwd_workspace_bytes", "gdr2_seg_workspace_bytes", "gdr2_strerror", "gdr2_version"]
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDR2_NOALLOC_SCRATCH_BYTES in include/gdr2.h
 
 
 def library_path() -> str:
@@ -72,6 +73,8 @@ def load_library():
     lib.gdr2_fwd_seg.restype = i
     lib.gdr2_bwd_seg.argtypes = [vp] * 16 + [i] * 9 + [vp, sz, vp, vp]
     lib.gdr2_bwd_seg.restype = i
+    lib.gdr2_fwd_noalloc.argtypes = [vp] * 9 + [i] * 7 + [vp]
+    lib.gdr2_fwd_noalloc.restype = i
     lib.gdr2_strerror.argtypes = [i]
     lib.gdr2_strerror.restype = ctypes.c_char_p
     lib.gdr2_version.argtypes = []
@@ -221,6 +224,31 @@ def _fwd(scales, q, k, v, g, b, w, h0, chunk, save_for_bwd, ws, o, output_final_
         st = lib.gdr2_fwd_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), *scales, *tail)
     _raise(st, "gdr2_fwd" if scales is None else "gdr2_fwd_logits")
     return o, ht, ws
+
+
+def gdr2_fwd_noalloc(q, k, v, g, b, w, h0=None, *, chunk=64, o=None, output_final_state=True, stream=None):
+    """Inference forward whose workspace is the library's fixed device array (for callers that
+    cannot allocate device memory; see include/gdr2.h). The C call allocates nothing; this
+    wrapper allocates o and ht only when they are not passed. Calls that overlap on one GPU race
+    on the shared array. Returns (o, ht or None)."""
+    lib = load_library()
+    B, T, H, dk, dv, dt = _dims(q, v)
+    for t, n, shp in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)), (g, "g", (B, T, H, dk)),
+                      (b, "b", (B, T, H, dk)), (v, "v", (B, T, H, dv)), (w, "w", (B, T, H, dv))):
+        _check(t, n, q.dtype, shp)
+    _check(h0, "h0", torch.float32, (B, H, dk, dv))
+    new = []
+    if o is None:
+        o = torch.empty(B, T, H, dv, dtype=q.dtype, device=q.device)
+        new.append(o)
+    _check(o, "o", q.dtype, (B, T, H, dv))
+    ht = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device) if output_final_state else None
+    new.append(ht)
+    _keep_for(stream, *new)
+    st = lib.gdr2_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(h0), _ptr(o), _ptr(ht),
+                              B, T, H, dk, dv, chunk, dt, _stream(stream))
+    _raise(st, "gdr2_fwd_noalloc")
+    return o, ht
 
 
 def gdr2_step(q, k, v, g, b, w, state, *, o=None, stream=None):

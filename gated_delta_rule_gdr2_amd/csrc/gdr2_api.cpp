@@ -103,20 +103,33 @@ size_t gdr2_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, 
 
 namespace {
 
-int fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
-             const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk, int dtype,
-             int save_for_bwd, void* workspace, size_t workspace_bytes, void* stream,
-             void* const* stage_events, int act, float g_scale, float b_scale, int segments) {
+// Host validation of a forward call (everything but the workspace) and the workspace
+// bytes it needs; no HIP call.
+int fwd_check(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+              const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+              int save_for_bwd, int act, float g_scale, float b_scale, int& segments, size_t& need) {
     if (!q || !k || !v || !g || !b || !w || !o) return GDR2_ERR_NULL;
     if (act && !scales_ok(g_scale, b_scale)) return GDR2_ERR_VALUE;
     if (segments < 0) return GDR2_ERR_VALUE;  // 0: the automatic count
     int st = check_shape(B, T, H, dk, dv, chunk, dtype);
     if (st != GDR2_OK) return st;
     if (segments == 0) segments = auto_segments(B, T, H, dv);
-    const void* ptrs[] = {q, k, v, g, b, w, h0, o, ht, workspace};
+    const void* ptrs[] = {q, k, v, g, b, w, h0, o, ht};
     for (const void* p : ptrs)
         if (p && !aligned(p)) return GDR2_ERR_ALIGN;
-    const size_t need = gdr2_seg_workspace_bytes(B, T, H, dk, dv, chunk, segments, dtype, save_for_bwd);
+    need = gdr2_seg_workspace_bytes(B, T, H, dk, dv, chunk, segments, dtype, save_for_bwd);
+    return GDR2_OK;
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+             const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+             int save_for_bwd, void* workspace, size_t workspace_bytes, void* stream,
+             void* const* stage_events, int act, float g_scale, float b_scale, int segments) {
+    size_t need = 0;
+    int st = fwd_check(q, k, v, g, b, w, h0, o, ht, B, T, H, dk, dv, chunk, dtype, save_for_bwd, act, g_scale,
+                       b_scale, segments, need);
+    if (st != GDR2_OK) return st;
+    if (workspace && !aligned(workspace)) return GDR2_ERR_ALIGN;
     if (!workspace || workspace_bytes < need) return GDR2_ERR_WORKSPACE;
 
     gdr2::Args a = {};
@@ -188,6 +201,27 @@ int step_impl(const void* q, const void* k, const void* v, const void* g, const 
 }
 
 }  // namespace
+
+namespace gdr2 {
+
+int fwd_validate(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+                 const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+                 size_t* need) {
+    int segments = 0;
+    size_t n = 0;
+    const int st = fwd_check(q, k, v, g, b, w, h0, o, ht, B, T, H, dk, dv, chunk, dtype, 0, 0, 1.f, 1.f, segments, n);
+    *need = n;
+    return st;
+}
+
+int fwd_with_workspace(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+                       const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk,
+                       int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return fwd_impl(q, k, v, g, b, w, h0, o, ht, B, T, H, dk, dv, chunk, dtype, 0, workspace, workspace_bytes,
+                    stream, nullptr, 0, 1.f, 1.f, 0);
+}
+
+}  // namespace gdr2
 
 extern "C" {
 
@@ -266,6 +300,9 @@ const char* gdr2_strerror(int status) {
         case GDR2_ERR_HIP: return "HIP launch failed";
         case GDR2_ERR_VALUE:
             return "a scalar argument is out of range (g_scale > 0 finite, 0 < b_scale <= 2, segments >= 1)";
+        case GDR2_ERR_SCRATCH:
+            return "the call needs more workspace than the library's fixed device array "
+                   "(GDR2_NOALLOC_SCRATCH_BYTES) holds";
         default: return "unknown status";
     }
 }

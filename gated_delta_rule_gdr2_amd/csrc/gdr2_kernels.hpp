@@ -51,6 +51,15 @@ hipError_t launch_fwd(const Args& a, bool bf16, bool train, hipStream_t stream);
 hipError_t launch_bwd(const Args& a, bool bf16, hipStream_t stream);
 hipError_t launch_step(const Args& a, bool bf16, hipStream_t stream);
 size_t fwd_intra_lds_bytes(int DK, int DV, int esz);
+
+// The forward entry point's host validation (all but the workspace; *need = the workspace
+// bytes of an inference forward) and the forward on a given workspace (gdr2_api.cpp).
+int fwd_validate(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+                 const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+                 size_t* need);
+int fwd_with_workspace(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+                       const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk,
+                       int dtype, void* workspace, size_t workspace_bytes, void* stream);
 size_t bwd_intra_lds_bytes(int DK, int DV, int esz);
 
 }  // namespace gdr2

@@ -62,7 +62,8 @@ enum gdr2_status {
     GDR2_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
     GDR2_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
     GDR2_ERR_HIP = -6,         /* a HIP launch failed */
-    GDR2_ERR_VALUE = -7        /* a scalar argument is out of range (gate scales, segments) */
+    GDR2_ERR_VALUE = -7,       /* a scalar argument is out of range (gate scales, segments) */
+    GDR2_ERR_SCRATCH = -8      /* gdr2_fwd_noalloc: the call needs more than the fixed scratch */
 };
 
 /* Bytes of workspace gdr2_fwd needs. save_for_bwd = 1 sizes it for a later
@@ -182,6 +183,25 @@ int gdr2_step_logits(const void* q, const void* k, const void* v, const void* zg
  * two forward stages first) when fwd_saved = 0, so it needs 3 or 5. With segments > 1
  * the chain stage also holds the summary and scan kernels. The events belong to the
  * caller. */
+
+/* For callers that cannot allocate device memory -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc: the inference forward (gdr2_fwd with
+ * save_for_bwd = 0) without a workspace argument. Its workspace is a fixed array of
+ * GDR2_NOALLOC_SCRATCH_BYTES (64 MiB) of device memory inside the library; each GPU the
+ * library runs on holds its own copy until the process ends. The call allocates nothing
+ * (no hipMalloc, no hipFree, no allocating library routine); the caller still passes
+ * every input and output. A call whose workspace, gdr2_fwd_workspace_bytes(B, T, H, dk,
+ * dv, chunk, dtype, 0), exceeds the array returns GDR2_ERR_SCRATCH and enqueues nothing
+ * (at d_k = d_v = 128 in bf16 about 72.5 KB per chunk of 64 tokens and head, so e.g.
+ * B = 1, H = 16, T = 2048 fits); other errors as gdr2_fwd. All calls on one GPU share the
+ * array, which keeps the last call's contents: calls that overlap on one GPU (several
+ * streams, or several host threads) race on it and must be serialised by the caller.
+ * Arguments, layouts and results otherwise as gdr2_fwd (bitwise the same results). */
+#define GDR2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int gdr2_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
+                     const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk,
+                     int dtype, void* stream);
 
 /* Static description of a status code. */
 const char* gdr2_strerror(int status);

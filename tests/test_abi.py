@@ -12,7 +12,7 @@ import gated_delta_rule_gdr2_amd as g2
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdr2.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_HIP, ERR_VALUE = 0, -1, -2, -3, -4, -5, -6, -7
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_HIP, ERR_VALUE, ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 
 @pytest.fixture(scope="module")
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_strerror(lib):
     assert g2.gdr2_version() >= 100
-    for st in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_HIP, ERR_VALUE):
+    for st in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_HIP, ERR_VALUE, ERR_SCRATCH):
         assert g2.gdr2_strerror(st) and g2.gdr2_strerror(st) != "unknown status"
     assert g2.gdr2_strerror(-99) == "unknown status"
 
@@ -270,3 +270,40 @@ def test_sizes_that_overflow_are_rejected(lib):
     assert fwd(lib, B=1 << 16, T=1 << 20, H=1 << 10) == ERR_SHAPE
     assert fwd(lib, B=1 << 20, T=1 << 20, H=1) == ERR_SHAPE
     assert g2.gdr2_fwd_workspace_bytes(1 << 16, 1 << 20, 1 << 10, 64, 64, 64, g2.DTYPE_BF16, False) == 0
+
+
+def noalloc(lib, ptrs=None, B=1, T=64, H=1, dk=64, dv=64, chunk=64, dtype=g2.DTYPE_BF16):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    return lib.gdr2_fwd_noalloc(*[ctypes.c_void_p(x) for x in p], B, T, H, dk, dv, chunk, dtype, None)
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    m = re.search(r"#define GDR2_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == g2.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_validates_like_the_forward_and_rejects_oversized_calls(lib):
+    """Every check happens on the host before any HIP call (so no GPU is needed here): the
+    forward's own errors, and GDR2_ERR_SCRATCH for a call whose workspace exceeds the fixed
+    array -- the largest that fits and the smallest that does not, from the size query."""
+    for idx in range(7):  # q, k, v, g, b, w and o (index 7 of the pointer list) are required
+        p = [FAKE] * 9
+        p[idx if idx < 6 else 7] = 0
+        assert noalloc(lib, p) == ERR_NULL
+    assert noalloc(lib, B=0) == ERR_SHAPE
+    assert noalloc(lib, dk=96) == ERR_UNSUP
+    assert noalloc(lib, dtype=g2.DTYPE_F32, dk=128, dv=128) == ERR_UNSUP
+    p = [FAKE] * 9
+    p[2] = FAKE + 8
+    assert noalloc(lib, p) == ERR_ALIGN
+    BF = g2.DTYPE_BF16
+    cap = g2.NOALLOC_SCRATCH_BYTES
+    # grow T until the inference workspace no longer fits
+    T = 64
+    while g2.gdr2_fwd_workspace_bytes(1, T + 64, 16, 128, 128, 64, BF, False) <= cap:
+        T += 64
+    assert g2.gdr2_fwd_workspace_bytes(1, T, 16, 128, 128, 64, BF, False) <= cap
+    assert noalloc(lib, B=1, T=T + 64, H=16, dk=128, dv=128) == ERR_SCRATCH
+    assert noalloc(lib, B=64, T=65536, H=16, dk=128, dv=128) == ERR_SCRATCH
+    # the B=1, H=16, T=2048, d=128 bf16 forward workload fits
+    assert g2.gdr2_fwd_workspace_bytes(1, 2048, 16, 128, 128, 64, BF, False) <= cap
