@@ -223,7 +223,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     };
 
     // ---- phase 1: block sums of the log-decay (see gdr2_intra_common.hpp) and factors;
-    // Delta, dY into LDS. gam keeps this lane's log-decays (activated) for the later phases.
+    // Delta, dY into LDS. gam keeps this lane's log-decays (activated; in their stored form,
+    // see DecayRep) for the later phases.
     float gam[CPW][4][4];
     float span = 0.f;  // largest s(R, R) exponent of this lane's channels
 #pragma unroll
@@ -254,14 +255,11 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
                 lds_put4<OT>(sB + vB.off(16 * t + li, ch0), bv[t]);
             }
         }
-        gamma_scan(gv, gf, gt, gi);
+        DecayRep<OT>::store(gv, gam[ac]);
+        DecayRep<OT>::scan(gam[ac], gf, gt, gi);
         span = fmaxf(span, diag_span(gi));
         RowExp rx;
         row_exps<DK>(sF, ch0, gf, gt, gi, rx);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gam[ac][t][i] = gv[t][i];
     }
     {  // every wave reports whether a diagonal block of its channels needs the slow path
         const bool strong = __ballot(span > span_max<OT>()) != 0;
@@ -482,7 +480,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         // K_b gradient times exp(gam) (gbk), Pk -> the Khat part of dk, PkS -> the Kd part.
         {
             float e1[4][4], e2[4][4];
-            block_factors(gam[ac], e1, e2);
+            block_factors<OT>(gam[ac], e1, e2);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -508,7 +506,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
                 const int r = 16 * t + li;
                 float al[4], pl[4] = {1.f, 1.f, 1.f, 1.f}, ph[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) al[i] = exp_op<OT>(gam[ac][t][i]);
+                for (int i = 0; i < 4; ++i) al[i] = DecayRep<OT>::alpha(gam[ac][t][i]);
 #pragma unroll 1
                 for (int j = 15; j >= 0; --j) {  // j < r: e(r, j) = alpha_r ... alpha_{j+1}
                     const int src1 = (l & 48) | ((j + 1) & 15);
@@ -576,8 +574,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         for (int i = 0; i < 4; ++i) {
             const float rs_i = CARRY_LDS ? lds_load<float>(sCarry + (DK + ch0 + i) * 4)
                                          : __shfl(rsum[ac][i], (l & 48) | (4 * lq + i), 64);
-            const float gamC = (row_sum16(gam[ac][0][i]) + row_sum16(gam[ac][1][i])) +
-                               (row_sum16(gam[ac][2][i]) + row_sum16(gam[ac][3][i]));  // the chunk's total
+            const float gamC = (DecayRep<OT>::total(gam[ac][0][i]) + DecayRep<OT>::total(gam[ac][1][i])) +
+                               (DecayRep<OT>::total(gam[ac][2][i]) + DecayRep<OT>::total(gam[ac][3][i]));
             cst[i] = __expf(gamC) * rs_i;
         }
         float later[4] = {0.f, 0.f, 0.f, 0.f}, before[4] = {0.f, 0.f, 0.f, 0.f};

@@ -242,7 +242,9 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
                 float gv[4][4], gf[4][4], gt[4][4], gi[4][4];
                 cvt_rows16<OT>(rg[ai], hq, nvalid, gv);
                 if (ACT) activate_rows<OT, GATE_G>(gv, nvalid, a.g_scale, a.b_scale);
-                gamma_scan(gv, gf, gt, gi);
+                float rep[4][4];
+                DecayRep<OT>::store(gv, rep);
+                DecayRep<OT>::scan(rep, gf, gt, gi);
                 span = fmaxf(span, diag_span(gi));
                 RowExp rx;
                 row_exps<DK>(sF, ch0, gf, gt, gi, rx);
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
                 cvt_rows16<OT>(rk[ai], hq, nvalid, kv);
                 cvt_rows16<OT>(rb[ai], hq, nvalid, bv);
                 if (ACT) activate_rows<OT, GATE_B>(bv, nvalid, a.g_scale, a.b_scale);
-                scaled_factors_from<OT, DK, true>(qv, kv, bv, ch0, gv, sXA, sXM, sY, qg_out, kd_out, &rx);
+                scaled_factors_from<OT, DK, true>(qv, kv, bv, ch0, rep, sXA, sXM, sY, qg_out, kd_out, &rx);
             }
         }
 #pragma unroll

@@ -123,37 +123,76 @@ __device__ __forceinline__ void lds_put4(lds_char* p, const float v[4]) {
     }
 }
 
-// Per-lane block sums of the log-decay for channel tile `at` (4 channels ch0..ch0+3,
-// rows 16t+li) from the log-decays gv[t][i] of those rows: f[R][i] = g at row 16R (the
-// block's first), tot[R][i] = sum of g over the block, inn[R][i] = sum of g over the
-// block without its first row (so s(R, R) = exp(-inn)).
-__device__ __forceinline__ void gamma_scan(const float (&gv)[4][4], float (&f)[4][4], float (&tot)[4][4],
-                                           float (&inn)[4][4]) {
-    const bool first = (lane_id() & 15) == 0;
-#pragma unroll
-    for (int R = 0; R < 4; ++R)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[R][i] = row_bcast<0>(gv[R][i]);
-            tot[R][i] = row_sum16(gv[R][i]);
-            inn[R][i] = row_sum16(first ? 0.f : gv[R][i]);
-        }
-}
-// E1_r = exp(sum of g over (R0, r]) and E2_r = exp(sum of g over (r, Rend]) of a lane's
-// row r = 16t + li, one channel (inclusive prefix without the block's first row;
-// exclusive suffix).
-__device__ __forceinline__ float block_e1(float g) {
+// A lane's log-decays (rows 16t + li, channels ch0 + i) are kept in one of two forms,
+// chosen by the operand precision (DecayRep<OT>):
+//   bf16 operands: p = the block-local inclusive running sum of g (one row scan); the
+//     factors are exp of differences of p (E1 = exp(p_r - p_R0), E2 = exp(p_Rend - p_r)),
+//     whose rounding (a few ulp of the block's running sum) stays far below bf16's;
+//   fp32 operands: the raw g; every factor is exp of a sum of exactly the log-decays it
+//     spans (E1 from a prefix scan without the block's first row, E2 from a suffix scan
+//     after the row), never a difference of running sums, so one very strong decay in a
+//     block costs no fp32 accuracy in the factors of the others.
+// From either form: f[R][i] = g at row 16R (the block's first), tot[R][i] = sum of g over
+// the block, inn[R][i] = sum of g over the block without its first row (s(R, R) = exp(-inn)).
+__device__ __forceinline__ float block_e1(float g) {  // exact form: exp(sum of g over (R0, r])
     return __expf(row_scan16((lane_id() & 15) == 0 ? 0.f : g));
 }
 __device__ __forceinline__ float block_e2(float g) { return __expf(row_suffix16(row_shl1(g))); }
-__device__ __forceinline__ void block_factors(const float (&gv)[4][4], float (&e1)[4][4], float (&e2)[4][4]) {
+
+template <class OT>
+struct DecayRep {
+    static constexpr bool EXACT = sizeof(OT) == 4;
+    // the stored form from the log-decays
+    static __device__ __forceinline__ void store(const float (&gv)[4][4], float (&rep)[4][4]) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rep[t][i] = EXACT ? gv[t][i] : row_scan16(gv[t][i]);
+    }
+    static __device__ __forceinline__ void scan(const float (&rep)[4][4], float (&f)[4][4], float (&tot)[4][4],
+                                                float (&inn)[4][4]) {
+        const bool first = (lane_id() & 15) == 0;
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f[R][i] = row_bcast<0>(rep[R][i]);
+                if constexpr (EXACT) {
+                    tot[R][i] = row_sum16(rep[R][i]);
+                    inn[R][i] = row_sum16(first ? 0.f : rep[R][i]);
+                } else {
+                    tot[R][i] = row_bcast<15>(rep[R][i]);
+                    inn[R][i] = tot[R][i] - f[R][i];
+                }
+            }
+    }
+    // E1 and E2 of a lane's row in block t, one channel
+    static __device__ __forceinline__ void e12(float x, float& e1, float& e2) {
+        if constexpr (EXACT) {
+            e1 = block_e1(x);
+            e2 = block_e2(x);
+        } else {
+            e1 = __expf(x - row_bcast<0>(x));
+            e2 = __expf(row_bcast<15>(x) - x);
+        }
+    }
+    // exp(g) of the lane's own row
+    static __device__ __forceinline__ float alpha(float x) {
+        if constexpr (EXACT) return expf(x);
+        else return __expf(x - row_shr1(x));
+    }
+    // the block's total sum of g, in every lane
+    static __device__ __forceinline__ float total(float x) {
+        if constexpr (EXACT) return row_sum16(x);
+        else return row_bcast<15>(x);
+    }
+};
+template <class OT>
+__device__ __forceinline__ void block_factors(const float (&rep)[4][4], float (&e1)[4][4], float (&e2)[4][4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            e1[t][i] = block_e1(gv[t][i]);
-            e2[t][i] = block_e2(gv[t][i]);
-        }
+        for (int i = 0; i < 4; ++i) DecayRep<OT>::e12(rep[t][i], e1[t][i], e2[t][i]);
 }
 // Largest s(R, R) exponent -inn_R of a lane's channels (>= 0 for a decay g <= 0).
 __device__ __forceinline__ float diag_span(const float (&inn)[4][4]) {
@@ -270,14 +309,14 @@ __device__ __forceinline__ void row_exps(lds_char* sF, int ch0, const float (&f)
     if (li == 0 || li == 2) lds_put4<float>(sF + ((F_ECE + 2 + li / 2) * DK + ch0) * 4, x.x1);
 }
 
-// XA = b*k*E1, XM = q*E1, Y = k*E2 (E1, E2 from the lane's log-decays gv, see block_e1 /
-// block_e2) for channel tile rows of this lane, into swizzled LDS
+// XA = b*k*E1, XM = q*E1, Y = k*E2 (E1, E2 from the lane's log-decays in their stored form
+// rep, see DecayRep) for channel tile rows of this lane, into swizzled LDS
 // tiles [CH][DK]; with OUTS also Qg = q*exp(gam) and Kd = k*exp(gam_C - gam) as swizzled
 // tiles in global memory (exp(gam) = E1 * exp(gam_R0), exp(gam_C - gam) = E2 *
 // exp(gam_C - gam_Rend), the row-uniform factors taken from rx).
 template <class OT, int DK, bool OUTS>
 __device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], const float (&kv)[4][4],
-                                                    const float (&bv)[4][4], int ch0, const float (&gv)[4][4],
+                                                    const float (&bv)[4][4], int ch0, const float (&rep)[4][4],
                                                     lds_char* sXA, lds_char* sXM, lds_char* sY, OT* qg_out,
                                                     OT* kd_out, const RowExp* rx) {
     const int li = lane_id() & 15;
@@ -287,7 +326,8 @@ __device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], con
         float xa[4], xm[4], y[4], qg[4], kd[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float e1 = block_e1(gv[t][i]), e2 = block_e2(gv[t][i]);
+            float e1, e2;
+            DecayRep<OT>::e12(rep[t][i], e1, e2);
             xa[i] = bv[t][i] * kv[t][i] * e1;
             xm[i] = qv[t][i] * e1;
             y[i] = kv[t][i] * e2;
