@@ -462,6 +462,25 @@ __device__ __forceinline__ typename Frag<OT>::type lfrag_colk(const V& m, int co
     return f;
 }
 
+// colk8: the contiguous K-slot map (k = k0 + 8*lq + e, as rowk8) over a matrix whose K
+// index runs down the rows: lane (li, lq) gets X[k0 + 8*lq + e][col0 + li], e = 0..7.
+// bf16: two transposing reads (rows k0 + 8 lq .. + 3 and + 4 .. + 7); fp32: eight scalar reads.
+template <class OT, class V>
+__device__ __forceinline__ typename Frag<OT>::type lfrag_colk8(const V& m, int col0, int k0) {
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    if constexpr (sizeof(OT) == 2) {
+        const int r = k0 + 8 * lq + (li >> 2), c = col0 + 4 * (li & 3);
+        bf16x4 v0 = lds_read_tr16(m.p + m.off(r, c));
+        bf16x4 v1 = lds_read_tr16(m.p + m.off(r + 4, c));
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        typename Frag<OT>::type f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = lds_load<float>(m.p + m.off(k0 + 8 * lq + e, col0 + li));
+        return f;
+    }
+}
+
 // ----------------------------------------------------------------------------- global fragments
 // A fragment block (one 16x32 operand) is stored lane-major: 64 lanes x 8 elements.
 template <class OT>
@@ -471,6 +490,42 @@ __device__ __forceinline__ void store_frag(OT* base, const typename Frag<OT>::ty
 template <class OT>
 __device__ __forceinline__ typename Frag<OT>::type load_frag(const OT* base) {
     return *(const typename Frag<OT>::type*)(base + lane_id() * 8);
+}
+// Fragment image of a matrix X [R][K] (K contiguous, R and K multiples of 16 and 32):
+// X stored as its row-K MFMA operand fragments, fragment (r / 16, c / 32) after
+// fragment, each as P pieces of 64 x 16 bytes (P = 1 for bf16, 2 for fp32). Lane
+// (li, lq) of a fragment holds X[16 rb + li][32 kb + 8 lq + e], e = 0..7, in 16-byte
+// slot 16 lq + (li ^ 4 (lq & 1)) of each piece. A fragment is hence one contiguous
+// 1 KB load per piece from global memory, and in LDS the transposing reads (16 lanes
+// on 4 consecutive rows x 2 adjacent column groups of 4) touch 8 slots in two 64-byte
+// runs 256 + 64 bytes apart, which share no bank; 4 consecutive columns starting at a
+// multiple of 4 are contiguous.
+template <class OT, int K>
+__host__ __device__ __forceinline__ int fimg(int r, int c) {
+    constexpr int EPP = 16 / (int)sizeof(OT);  // elements per 16-byte piece
+    constexpr int P = 8 / EPP;                 // pieces per lane and fragment
+    static_assert(K % 32 == 0, "fragment images have whole 32-column blocks");
+    const int lq = (c >> 3) & 3;
+    const int slot = 16 * lq + ((r & 15) ^ (4 * (lq & 1)));
+    const int frag = (r >> 4) * (K / 32) + (c >> 5);
+    return ((frag * P + (c & 7) / EPP) * 64 + slot) * EPP + (c & 7) % EPP;
+}
+template <class XT, int K>
+struct LImg {  // fragment image in LDS
+    const lds_char* p;
+    __device__ __forceinline__ int off(int r, int c) const { return fimg<XT, K>(r, c) * (int)sizeof(XT); }
+};
+// Row-K fragment (as lfrag_rowk8) read straight from a fragment image in global memory.
+template <class OT, int K>
+__device__ __forceinline__ typename Frag<OT>::type gfrag_img(const OT* m, int row0, int k0) {
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    if constexpr (sizeof(OT) == 2) {
+        return *(const bf16x8*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq));
+    } else {
+        const f32x4 x0 = *(const f32x4*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq));
+        const f32x4 x1 = *(const f32x4*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq + 4));
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
 }
 // accumulator tile dump: 64 lanes x 4 elements
 template <class OT>

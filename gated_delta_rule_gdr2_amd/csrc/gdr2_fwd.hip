@@ -163,7 +163,7 @@ __device__ __forceinline__ void fwd_diag_exact(const Args& a, size_t rowk0, int 
             }
         }
         lds_store<float>(sA + swz<float, CH>(16 * R + r, 16 * R + i) * 4, i < r ? am : 0.f);
-        m_out[swz<OT, CH>(16 * R + r, 16 * R + i)] = to_ot<OT>(i <= r ? mm : 0.f);
+        m_out[fimg<OT, CH>(16 * R + r, 16 * R + i)] = to_ot<OT>(i <= r ? mm : 0.f);
         sync_lds();
     }
 }
@@ -292,13 +292,13 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
         float v[4];  // lane holds M[16R + li][16I + 4lq + i]
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = (R == I && 4 * lq + i > li) ? 0.f : acc[i];
-        st4(m_out + swz<OT, CH>(16 * R + li, 16 * I + 4 * lq), v);
+        st4(m_out + fimg<OT, CH>(16 * R + li, 16 * I + 4 * lq), v);
     }
     for (int u = wv; u < 6; u += 4) {
         int R, I;
         upper_ri(u, R, I);
         const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        st4(m_out + swz<OT, CH>(16 * R + li, 16 * I + 4 * lq), z);
+        st4(m_out + fimg<OT, CH>(16 * R + li, 16 * I + 4 * lq), z);
     }
     sync_lds();  // XM is dead from here on; its slot becomes A
 
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vXA, 16 * at, 32 * kb), aT[kb]);  // XA holds K_b
             float v[4] = {acc[0], acc[1], acc[2], acc[3]};  // Wm[16tt + li][16at + 4lq + i]
-            st4(wm_out + swz<OT, DK>(16 * tt + li, 16 * at + 4 * lq), v);
+            st4(wm_out + fimg<OT, DK>(16 * tt + li, 16 * at + 4 * lq), v);
         }
     }
     if (TRAIN) {  // T for the backward chain

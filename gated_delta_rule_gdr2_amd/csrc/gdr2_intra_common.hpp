@@ -311,8 +311,8 @@ __device__ __forceinline__ void row_exps(lds_char* sF, int ch0, const float (&f)
 
 // XA = b*k*E1, XM = q*E1, Y = k*E2 (E1, E2 from the lane's log-decays in their stored form
 // rep, see DecayRep) for channel tile rows of this lane, into swizzled LDS
-// tiles [CH][DK]; with OUTS also Qg = q*exp(gam) and Kd = k*exp(gam_C - gam) as swizzled
-// tiles in global memory (exp(gam) = E1 * exp(gam_R0), exp(gam_C - gam) = E2 *
+// tiles [CH][DK]; with OUTS also Qg = q*exp(gam) as a swizzled tile [CH][DK] and
+// Kd = k*exp(gam_C - gam) transposed, as a swizzled tile Kd^T [DK][CH], in global memory (exp(gam) = E1 * exp(gam_R0), exp(gam_C - gam) = E2 *
 // exp(gam_C - gam_Rend), the row-uniform factors taken from rx).
 template <class OT, int DK, bool OUTS>
 __device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], const float (&kv)[4][4],
@@ -341,8 +341,9 @@ __device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], con
         lds_put4<OT>(sXM + o, xm);
         lds_put4<OT>(sY + o, y);
         if constexpr (OUTS) {
-            st4(qg_out + swz<OT, DK>(r, ch0), qg);
-            st4(kd_out + swz<OT, DK>(r, ch0), kd);
+            st4(qg_out + fimg<OT, DK>(r, ch0), qg);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kd_out[fimg<OT, CH>(ch0 + i, r)] = to_ot<OT>(kd[i]);  // Kd^T [DK][CH]
         }
     }
 }

@@ -1,11 +1,12 @@
 // Workspace layout shared by the host launcher and the kernels.
 //
 // Every array is chunk-major: element offset = chunk_id * per_chunk + local,
-// chunk_id = (b * H + h) * NT + c. Per-chunk matrices are stored once each as
-// swizzled row-major tiles (see swz() in gdr2_device.hpp) in the operand type;
-// the state chains read them in either orientation from LDS. Accumulator-tile
-// dumps (U, Delta, dY) hold 16x16 tiles as 64 lanes x 4 elements, ordered
-// [value-column tile][token tile]. The saved states S and dS' are fragment-major
+// chunk_id = (b * H + h) * NT + c. Per-chunk matrices are stored once each in the
+// operand type: Wm, Kd^T, Qg and M as fragment images (fimg() in gdr2_device.hpp),
+// which the forward chain loads fragment by fragment into registers and the backward
+// chain copies into LDS and reads transposed; T as a swizzled row-major tile (swz()).
+// Accumulator-tile dumps (U, Delta, dY) hold 16x16 tiles as 64 lanes x 4 elements,
+// ordered [value-column tile][token tile]. The saved states S and dS' are fragment-major
 // (fmaj_off in gdr2_device.hpp). Each array starts on a 256-byte boundary.
 //
 // With the chains split into NSEG segments per sequence (chunk-parallel scan), three
@@ -23,7 +24,7 @@ namespace gdr2 {
 struct Layout {
     int DK, DV, esz;  // esz: bytes per operand element (2 for bf16, 4 for fp32)
     // per-chunk element counts
-    size_t wm, kd, qg, m, u, gc;     // forward: Wm [64][DK], Kd [64][DK], Qg [64][DK], M [64][64], U tiles, exp(gam_C)
+    size_t wm, kd, qg, m, u, gc;     // forward: Wm [64][DK], Kd^T [DK][64], Qg [64][DK], M [64][64], U tiles, exp(gam_C)
     size_t t;                        // backward: T = (I + A)^-1 [64][64]
     size_t s, ds, delta, dy;         // chunk start state / end-state gradient [DK][DV], Delta / dY tiles
     size_t o_wm, o_kd, o_qg, o_m, o_u, o_gc, o_t, o_s, o_ds, o_delta, o_dy;  // byte offsets
