@@ -25,7 +25,8 @@ __all__ = ["gdr2_fwd", "gdr2_bwd", "gdr2_step", "gdr2_fwd_logits", "gdr2_bwd_log
            "library_path", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libgdr2.so")
+# GDR2_LIB names another build of the same library (e.g. one with host-side sanitizers)
+_LIB_PATH = os.environ.get("GDR2_LIB") or os.path.join(_HERE, "libgdr2.so")
 _lib = None
 
 DTYPE_F32, DTYPE_BF16 = 0, 1

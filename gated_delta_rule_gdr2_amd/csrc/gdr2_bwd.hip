@@ -130,6 +130,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     constexpr int CPW = (DK / 16 + NW - 1) / NW;  // key-channel tiles per wave
     extern __shared__ __align__(16) char smem_[];
     lds_char* smem = (lds_char*)smem_;
+    poison_lds(smem, LS::BYTES);
+    poison_lds_done();
     lds_char* sDO = smem + LS::S0;
     lds_char* sDL = smem + LS::S1;
     lds_char* sDY = smem + LS::S2;

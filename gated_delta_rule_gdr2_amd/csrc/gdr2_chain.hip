@@ -600,6 +600,9 @@ __global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_fwd_chain(Args a) {
     __shared__ __align__(16) char xch[Xch<OT>::bytes(NW, NC)];
     __shared__ __align__(16) char stage[NW * RowStore<OT>::BYTES];
     __shared__ __align__(16) char pfslot[256];  // target of the L2 prefetch DMAs, never read
+    poison_lds((lds_char*)xch, sizeof(xch));
+    poison_lds((lds_char*)stage, sizeof(stage));
+    poison_lds_done();
     // one walk per (sequence, segment, slice), with all outputs
     const int NSEG = a.nseg;
     int u, j;
@@ -634,6 +637,8 @@ __global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_fwd_chain_sum(Args a) {
     constexpr int NW = DK / 32, NJ = DV / 16, NJP = DK / 16;
     __shared__ __align__(16) char xch[Xch<OT>::bytes(NW, 1)];
     __shared__ __align__(16) char pfslot[256];  // target of the L2 prefetch DMAs, never read
+    poison_lds((lds_char*)xch, sizeof(xch));
+    poison_lds_done();
     const int NSEG = a.nseg;
     int u, j;
     chain_map(blockIdx.x, a.B * a.H * (NSEG - 1), NJ + NJP, u, j);
@@ -938,6 +943,11 @@ __global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_bwd_chain(Args a) {
     __shared__ __align__(16) char xch[LZ::XBYTES];
     __shared__ __align__(16) char stage[LZ::SBYTES];
     __shared__ __align__(16) char pfslot[256];  // target of the L2 prefetch DMAs, never read
+    poison_lds((lds_char*)buf0, sizeof(buf0));
+    poison_lds((lds_char*)buf1, sizeof(buf1));
+    poison_lds((lds_char*)xch, sizeof(xch));
+    poison_lds((lds_char*)stage, sizeof(stage));
+    poison_lds_done();
     // one walk per (sequence, segment, slice), with all outputs
     const int NSEG = a.nseg;
     int u, j;
@@ -973,6 +983,10 @@ __global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_bwd_chain_sum(Args a) {
     __shared__ __align__(16) char buf1[DBUF ? B::BYTES : 16];
     __shared__ __align__(16) char xch[LZ::XBYTES];
     __shared__ __align__(16) char pfslot[256];  // target of the L2 prefetch DMAs, never read
+    poison_lds((lds_char*)buf0, sizeof(buf0));
+    poison_lds((lds_char*)buf1, sizeof(buf1));
+    poison_lds((lds_char*)xch, sizeof(xch));
+    poison_lds_done();
     const int NSEG = a.nseg;
     int u, j;
     chain_map(blockIdx.x, a.B * a.H * (NSEG - 1), NJ, u, j);
@@ -1001,6 +1015,8 @@ __global__ __launch_bounds__(256) void k_seg_scan(Args a) {
     constexpr int NJ = DV / 16, TPR = 256 / DK, CPT = 16 / TPR;  // threads per row, columns per thread
     constexpr int PP = DK + 1;
     extern __shared__ __align__(16) char smem_[];
+    poison_lds((lds_char*)smem_, (DK * PP + DK * 16) * 4);
+    poison_lds_done();
     float* sP = (float*)smem_;     // [DK][PP]
     float* sx = sP + DK * PP;      // [DK][16]
     const int tid = threadIdx.x;

@@ -59,6 +59,7 @@ __device__ __forceinline__ void wait_vm() {
 // (wait_vm) before it.
 __device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+
 // pair index -> (R, I), I <= R, in the order (0,0),(1,0),(1,1),(2,0),...
 __device__ __forceinline__ void pair_ri(int p, int& R, int& I) {
     R = (p >= 6) ? 3 : (p >= 3) ? 2 : (p >= 1) ? 1 : 0;
@@ -282,6 +283,26 @@ __device__ __forceinline__ typename Frag<OT>::type frag_colk(const XT* X, int ld
 
 // ----------------------------------------------------------------------------- LDS address space
 typedef __attribute__((address_space(3))) char lds_char;
+
+// Debug builds with -DGDR2_POISON_LDS: a kernel first fills its LDS with all-ones bytes (a
+// NaN in bf16 and in fp32), so that a read of LDS that no write has reached turns the
+// results into NaN. poison_lds fills one region; poison_lds_done ends the fill with a
+// barrier of the whole workgroup. Without the flag both are empty.
+__device__ __forceinline__ void poison_lds(lds_char* p, int bytes) {
+#ifdef GDR2_POISON_LDS
+    typedef __attribute__((address_space(3))) unsigned U32;
+    U32* q = (U32*)p;
+    for (int i = threadIdx.x; i < bytes / 4; i += blockDim.x) q[i] = 0xFFFFFFFFu;
+#else
+    (void)p;
+    (void)bytes;
+#endif
+}
+__device__ __forceinline__ void poison_lds_done() {
+#ifdef GDR2_POISON_LDS
+    __syncthreads();
+#endif
+}
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <class T>

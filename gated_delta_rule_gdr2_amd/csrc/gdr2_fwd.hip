@@ -181,6 +181,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
     constexpr int KB = DK / 32;
     extern __shared__ __align__(16) char smem_[];
     lds_char* smem = (lds_char*)smem_;
+    poison_lds(smem, LS::BYTES);
+    poison_lds_done();
     lds_char* sXA = smem + LS::XA;
     lds_char* sXM = smem + LS::SLOTM;
     lds_char* sA = smem + LS::SLOTM;

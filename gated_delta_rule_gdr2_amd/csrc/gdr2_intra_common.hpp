@@ -310,10 +310,10 @@ __device__ __forceinline__ void row_exps(lds_char* sF, int ch0, const float (&f)
 }
 
 // XA = b*k*E1, XM = q*E1, Y = k*E2 (E1, E2 from the lane's log-decays in their stored form
-// rep, see DecayRep) for channel tile rows of this lane, into swizzled LDS
-// tiles [CH][DK]; with OUTS also Qg = q*exp(gam) as a swizzled tile [CH][DK] and
-// Kd = k*exp(gam_C - gam) transposed, as a swizzled tile Kd^T [DK][CH], in global memory (exp(gam) = E1 * exp(gam_R0), exp(gam_C - gam) = E2 *
-// exp(gam_C - gam_Rend), the row-uniform factors taken from rx).
+// rep, see DecayRep) for channel tile rows of this lane, into swizzled LDS tiles [CH][DK];
+// with OUTS also Qg = q*exp(gam) [CH][DK] and Kd = k*exp(gam_C - gam) transposed, Kd^T
+// [DK][CH], as fragment images in global memory (exp(gam) = E1 * exp(gam_R0),
+// exp(gam_C - gam) = E2 * exp(gam_C - gam_Rend), the row-uniform factors taken from rx).
 template <class OT, int DK, bool OUTS>
 __device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], const float (&kv)[4][4],
                                                     const float (&bv)[4][4], int ch0, const float (&rep)[4][4],

@@ -34,6 +34,9 @@ __global__ __launch_bounds__(128) void k_step(Args a) {
     constexpr int NI = DK / 8;  // state rows per lane
     __shared__ float sk[2][4][DK];             // per token: k, b*k, q, exp(g)
     __shared__ float sv[2][2][STEP_COLS];      // per token: v, w of the slice
+    poison_lds((lds_char*)sk, sizeof(sk));
+    poison_lds((lds_char*)sv, sizeof(sv));
+    poison_lds_done();
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, cq = l & 7, rg = l >> 3;
     const int NJ = DV / STEP_COLS;
     const int s = blockIdx.x / NJ, js = blockIdx.x % NJ;
