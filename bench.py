@@ -23,6 +23,15 @@ cpu_baseline     : the fp64 oracle (test infrastructure, untuned) timed on the h
                    passes over the first B*H sequences at full length until about
                    10 s have elapsed.
 
+    python bench.py --all-configs [--table PATH]
+
+times every workload of gated_delta_rule_gdr2_amd.inputs.WORKLOADS (the forward-only ones
+as gdr2_fwd steps, the training ones as fwd+bwd steps), each right after a 512 MiB write
+that evicts the Infinity Cache and also back to back, next to one oracle pass over a
+sample of its sequences at full length, with the GPU's normwise relative error against
+that pass per output tensor; one JSON line per workload, and with --table a markdown
+table at PATH.
+
     python bench.py --summarize-profile DIR
 
 reads the rocprofv3 output of a profiling run (DIR/trace, DIR/pmc_FETCH_SIZE,
@@ -102,13 +111,20 @@ def measured_traffic(workload, kernel):
     return None if k is None else k["fetch_bytes"] + k["write_bytes"]
 
 
-def algorithmic_flops(wl, C=64):
+def algorithmic_flops(wl, C=64, backward=True):
     """Chunkwise flops (triangular products at half cost, no recompute)."""
     th = wl.B * wl.T * wl.H
     d = wl.DK
     fwd = C * (3 * wl.DK + 2 * wl.DV) + 6 * wl.DK * wl.DV
     bwd = 14 * C * d + 12 * wl.DK * wl.DV
-    return th * (fwd + bwd)
+    return th * (fwd + (bwd if backward else 0))
+
+
+def forward_algorithmic_bytes(wl, esz):
+    """Operator-level bytes of one forward call: inputs, o and the final state (+ h0)."""
+    th = wl.B * wl.T * wl.H
+    state = wl.B * wl.H * wl.DK * wl.DV * 4
+    return th * (4 * wl.DK + 2 * wl.DV + wl.DV) * esz + state * (2 if wl.h0_std > 0 else 1)
 
 
 class HipEvents:
@@ -442,6 +458,147 @@ def gate_logits_measurement(torch, g2, wl, K, stream):
             "ms_per_step_separate_torch_passes": res["separate_torch_passes"]}
 
 
+CONFIG_ORDER = ("fwd_f32_b1h2t256d64", "fwd_bf16_b1h16t2048d128_h0", "fwdbwd_bf16_b2h16t4096d128",
+                "fwdbwd_bf16_b2h16t4096d128_tied", "fwdbwd_bf16_b8h16t2048d128_g05",
+                "fwdbwd_bf16_b1h16t16384d128_h0")
+
+
+def _normwise(gpu, ref):
+    import numpy as np
+    den = float(np.linalg.norm(ref))
+    return float(np.linalg.norm(gpu - ref)) / (den if den > 0 else 1.0)
+
+
+def measure_config(torch, g2, wl, K, W, stream, hip, with_oracle=True):
+    """One workload: cache-evicted and back-to-back step times, step roofline, and one oracle
+    pass over min(cores, B*H) of its sequences at full length with the GPU's error against it."""
+    import numpy as np
+    from gated_delta_rule_gdr2_amd.inputs import make_inputs
+    host = make_inputs(wl)
+    x = {k: (None if v is None else v.cuda()) for k, v in host.items()}
+    B, T, H, DK, DV = wl.B, wl.T, wl.H, wl.DK, wl.DV
+    esz = 2 if wl.dtype == "bf16" else 4
+    names = ("q", "k", "v", "g", "b", "w")
+    train = wl.backward
+    ws = g2.workspace(B, T, H, DK, DV, x["q"].dtype, train, "cuda")
+    o = torch.empty(B, T, H, DV, dtype=x["q"].dtype, device="cuda")
+    grads = {n: torch.empty_like(x[n[1:]]) for n in ("dq", "dk", "dv", "dg", "db", "dw")} if train else None
+    res = {}
+
+    def step():
+        _, ht, _ = g2.gdr2_fwd(*(x[n] for n in names), x["h0"], save_for_bwd=train, ws=ws, o=o, stream=stream)
+        res["ht"] = ht
+        if train:
+            res["grads"] = g2.gdr2_bwd(*(x[n] for n in names), x["h0"], x["do"], ws=ws, fwd_saved=True,
+                                       grads=grads, need_dh0=x["h0"] is not None, stream=stream)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t0) / K * 1e3
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ev = hip.create(2 * K)
+    for i in range(K):
+        flush.fill_(i & 255)
+        hip.record(ev[2 * i], stream)
+        step()
+        hip.record(ev[2 * i + 1], stream)
+    torch.cuda.synchronize()
+    cold_ms = sorted(hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(K))[K // 2]
+    hip.destroy(ev)
+    del flush
+    nbytes = step_algorithmic_bytes(wl, esz) if train else forward_algorithmic_bytes(wl, esz)
+    flops = algorithmic_flops(wl, backward=train)
+    peak_tf = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    t_hbm, t_mfma = nbytes / (HBM_PEAK_GBS * 1e9) * 1e3, flops / (peak_tf * 1e12) * 1e3
+    out = {"workload": wl.name, "path": "fwd+bwd" if train else "fwd", "dtype": wl.dtype,
+           "B": B, "H": H, "T": T, "d_k": DK, "d_v": DV, "h0": x["h0"] is not None, "tied": wl.tied,
+           "ms_cache_evicted": cold_ms, "ms_back_to_back": warm_ms,
+           "tokens_per_s": B * T / (cold_ms * 1e-3), "tokens_per_s_back_to_back": B * T / (warm_ms * 1e-3),
+           "roofline": {"bound": "hbm" if t_hbm >= t_mfma else "mfma", "algorithmic_bytes": nbytes,
+                        "algorithmic_flops": flops, "t_roofline_ms": max(t_hbm, t_mfma),
+                        "frac": max(t_hbm, t_mfma) / cold_ms}}
+    if with_oracle:
+        import oracle
+        cores = oracle.num_threads()
+        n = min(B * H, cores)
+        sel = [(q // H, q % H) for q in range(n)]
+
+        def take(t, state=False):
+            if t is None:
+                return None
+            a = t.float().cpu().double().numpy()
+            if state:
+                return np.concatenate([a[bb:bb + 1, hh:hh + 1] for bb, hh in sel], axis=1)
+            return np.concatenate([a[bb:bb + 1, :, hh:hh + 1] for bb, hh in sel], axis=2)
+
+        args = [take(host[k]) for k in names]
+        h0 = take(host["h0"], True)
+        t0 = time.perf_counter()
+        ro, rht = oracle.fwd(*args, h0)
+        rg = oracle.bwd(*args, h0, take(host["do"])) if train else None
+        dt = time.perf_counter() - t0
+        err = {"o": _normwise(take(o), ro), "ht": _normwise(take(res["ht"], True), rht)}
+        if train:
+            for k in ("dq", "dk", "dv", "dg", "db", "dw"):
+                err[k] = _normwise(take(res["grads"][k]), rg[k])
+            if x["h0"] is not None:
+                err["dh0"] = _normwise(take(res["grads"]["dh0"], True), rg["dh0"])
+        out["parity_normwise_rel_err"] = err
+        out["parity_tolerance"] = 2e-2 if wl.dtype == "bf16" else 1e-5
+        out["cpu_baseline"] = {"value": n * T / H / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                               "seconds": dt, "sample": "one %s pass over %d of %d (batch, head) sequences at "
+                               "full length T=%d, fp64; tokens counted as sequences*T/H"
+                               % ("fwd+bwd" if train else "fwd", n, B * H, T)}
+    del x, ws, o, grads
+    torch.cuda.empty_cache()
+    return out
+
+
+def write_table(rows, path, digest):
+    lines = ["# Every workload on one MI355X", "",
+             "Kernel source digest: `%s`." % digest[:16],
+             "Produced by `python bench.py --all-configs --table PATH` (steps and warmup per row below).", "",
+             "| workload | path | ms (cache evicted) | ms (back to back) | tokens/s (evicted) | roofline | "
+             "frac | max normwise err (tol) | oracle tokens/s (cores, s) |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        e = r.get("parity_normwise_rel_err")
+        emax = "%.2e (%g)" % (max(e.values()), r["parity_tolerance"]) if e else "-"
+        cb = r.get("cpu_baseline")
+        cbs = "%.3g (%d, %.1f)" % (cb["value"], cb["cores"], cb["seconds"]) if cb else "-"
+        rf = r["roofline"]
+        lines.append("| %s | %s | %.4f | %.4f | %.4g | %s %.4f ms | %.3f | %s | %s |" % (
+            r["workload"], r["path"], r["ms_cache_evicted"], r["ms_back_to_back"], r["tokens_per_s"],
+            rf["bound"], rf["t_roofline_ms"], rf["frac"], emax, cbs))
+    lines += ["", "Per-tensor errors (normwise relative, GPU vs the fp64 oracle on the sampled sequences):", ""]
+    for r in rows:
+        e = r.get("parity_normwise_rel_err")
+        if e:
+            lines.append("- %s: %s" % (r["workload"], ", ".join("%s %.2e" % kv for kv in e.items())))
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def all_configs(torch, g2, K, W, table, with_oracle):
+    from gated_delta_rule_gdr2_amd.inputs import WORKLOADS
+    stream = torch.cuda.current_stream()
+    hip = HipEvents()
+    rows = []
+    for name in CONFIG_ORDER:
+        print("# %s" % name, file=sys.stderr, flush=True)
+        r = measure_config(torch, g2, WORKLOADS[name], K, W, stream, hip, with_oracle)
+        r.update(steps=K, warmup=W)
+        rows.append(r)
+        print(json.dumps(r), flush=True)
+    if table:
+        write_table(rows, table, source_digest())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -460,6 +617,9 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="time the step alone (no decode, gate-logit or chain-scan side measurements): "
                          "the run that rocprofv3 traces")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="time every workload (forward-only ones as forward steps), each next to an oracle pass")
+    ap.add_argument("--table", default=None, help="with --all-configs: write a markdown table here")
     ap.add_argument("--scan-sweep", action="store_true",
                     help="print fwd+bwd step times against the chain segment count (chunk-parallel scan) and exit")
     args = ap.parse_args()
@@ -485,6 +645,9 @@ def main():
 
     if args.scan_sweep:
         scan_sweep(torch, g2)
+        return
+    if args.all_configs:
+        all_configs(torch, g2, args.steps, args.warmup, args.table, not args.no_cpu_baseline)
         return
 
     wl = WORKLOADS[args.workload or HEADLINE]

@@ -1079,6 +1079,20 @@ static hipError_t launch_seg_scan(const Args& a, hipStream_t stream) {  // never
 }
 
 // ============================================================================ launchers
+// Value columns per main-chain workgroup: 16 (NC = 1) or 32 (NC = 2). A step's cost is set by
+// the operands its workgroup moves through its compute unit's memory path (about 60 KB per step
+// whatever the slice width). With at most one 16-column walk per compute unit the narrow slices
+// finish first (their steps carry less arithmetic); with two or more, walks queue on the compute
+// units and 32-column slices, which move the shared operands once for two column tiles, halve
+// the traffic and the number of walks.
+inline hipError_t chain_nc(long long walks16, int& nc) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    nc = (e == hipSuccess && walks16 >= 2LL * cus) ? 2 : 1;
+    return e;
+}
+
 template <class OT, int DK, int DV>
 hipError_t launch_fwd_chain_t(const Args& a, bool train, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     const unsigned S = (unsigned)(a.B * a.H), NJ1 = DV / 16, NJP = DK / 16;
@@ -1091,11 +1105,20 @@ hipError_t launch_fwd_chain_t(const Args& a, bool train, hipStream_t stream, hip
         if ((e = launch_seg_scan<DK, DV, false>(a, stream)) != hipSuccess) return e;
         start = nullptr;
     }
-    const dim3 grid(S * a.nseg * NJ1);
-    if (train)
-        hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 1, true>), grid, block, 0, stream, start, stop, 0, a);
-    else
-        hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 1, false>), grid, block, 0, stream, start, stop, 0, a);
+    int nc = 1;
+    if ((e = chain_nc((long long)S * a.nseg * NJ1, nc)) != hipSuccess) return e;
+    const dim3 grid(S * a.nseg * (NJ1 / nc));
+    if (nc == 2) {
+        if (train)
+            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 2, true>), grid, block, 0, stream, start, stop, 0, a);
+        else
+            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 2, false>), grid, block, 0, stream, start, stop, 0, a);
+    } else {
+        if (train)
+            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 1, true>), grid, block, 0, stream, start, stop, 0, a);
+        else
+            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 1, false>), grid, block, 0, stream, start, stop, 0, a);
+    }
     return hipGetLastError();
 }
 template <class OT, int DK, int DV>
@@ -1110,7 +1133,14 @@ hipError_t launch_bwd_chain_t(const Args& a, hipStream_t stream, hipEvent_t star
         if ((e = launch_seg_scan<DK, DV, true>(a, stream)) != hipSuccess) return e;
         start = nullptr;
     }
-    hipExtLaunchKernelGGL((k_bwd_chain<OT, DK, DV, 1>), dim3(S * a.nseg * NJ1), block, 0, stream, start, stop, 0, a);
+    int nc = 1;
+    if ((e = chain_nc((long long)S * a.nseg * NJ1, nc)) != hipSuccess) return e;
+    if (nc == 2)
+        hipExtLaunchKernelGGL((k_bwd_chain<OT, DK, DV, 2>), dim3(S * a.nseg * (NJ1 / 2)), block, 0, stream, start,
+                              stop, 0, a);
+    else
+        hipExtLaunchKernelGGL((k_bwd_chain<OT, DK, DV, 1>), dim3(S * a.nseg * NJ1), block, 0, stream, start, stop, 0,
+                              a);
     return hipGetLastError();
 }
 
