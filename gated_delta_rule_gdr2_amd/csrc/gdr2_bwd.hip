@@ -269,11 +269,17 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     }
     undump_store<OT, DV, NTHR>(rdl, sDL);
     undump_store<OT, DV, NTHR>(rdy, sDY);
-    for (int idx = tid; idx < CH * CH; idx += NTHR) {  // zero the upper blocks of dA, dM
-        const int r = idx / CH, cc = idx % CH;
-        if ((cc >> 4) > (r >> 4)) {
-            lds_store<OT>(sDA + swz<OT, CH>(r, cc) * (int)sizeof(OT), to_ot<OT>(0.f));
-            lds_store<OT>(sDM + swz<OT, CH>(r, cc) * (int)sizeof(OT), to_ot<OT>(0.f));
+    {  // zero the upper blocks of dA, dM, a 16-byte chunk per store (no chunk spans two blocks)
+        constexpr int EPC = 16 / (int)sizeof(OT), CPR = CH / EPC;  // elements per chunk, chunks per row
+        static_assert(16 % EPC == 0 && CH * CPR % NTHR == 0, "the chunks split evenly over the threads");
+#pragma unroll
+        for (int u = 0; u < CH * CPR / NTHR; ++u) {
+            const int idx = tid + NTHR * u, r = idx / CPR, c0 = EPC * (idx % CPR);
+            if ((c0 >> 4) > (r >> 4)) {
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                lds_store<f32x4>(sDA + swz<OT, CH>(r, c0) * (int)sizeof(OT), z);
+                lds_store<f32x4>(sDM + swz<OT, CH>(r, c0) * (int)sizeof(OT), z);
+            }
         }
     }
     sync_lds();  // LDS only: the later loads stay in flight
@@ -392,7 +398,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     }
     sync_lds();  // dO, Delta, dY are dead; their slots take the key/query factors
 
-    // ---- phase 3b: XA = b*k*E1, XM = q*E1, Y = k*E2 into LDS
+    // ---- phase 3b: XA = b*k*E1, XM = q*E1, Y = k*E2 into LDS; E1 and E2 are kept for the finals
+    float e1f[CPW][4][4], e2f[CPW][4][4];
 #pragma unroll
     for (int ac = 0; ac < CPW; ++ac) {
         if (wv + NW * ac >= DK / 16) break;
@@ -401,7 +408,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         rows4(vQ, ch0, qv);
         rows4(vK, ch0, kv);
         rows4(vB, ch0, bv);  // (activated in phase 1 when the gates came as logits)
-        scaled_factors_from<OT, DK, false>(qv, kv, bv, ch0, gam[ac], sXA, sXM, sY, nullptr, nullptr, nullptr);
+        block_factors<OT>(gam[ac], e1f[ac], e2f[ac]);
+        scaled_factors<OT, DK, false>(qv, kv, bv, ch0, e1f[ac], e2f[ac], sXA, sXM, sY, nullptr, nullptr, nullptr);
     }
     sync_lds();
 
@@ -480,18 +488,14 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         rows4(vB, ch0, bv);
         // First the token-side sums in place, without the diagonal of dM: Pq -> dq, Pb -> the
         // K_b gradient times exp(gam) (gbk), Pk -> the Khat part of dk, PkS -> the Kd part.
-        {
-            float e1[4][4], e2[4][4];
-            block_factors<OT>(gam[ac], e1, e2);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < 4; ++t) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    Pq[ac][t][i] = e1[t][i] * Pq[ac][t][i];
-                    Pb[ac][t][i] = e1[t][i] * Pb[ac][t][i];
-                    Pk[ac][t][i] = e2[t][i] * Pk[ac][t][i];
-                    PkS[ac][t][i] = e2[t][i] * PkS[ac][t][i];
-                }
+            for (int i = 0; i < 4; ++i) {
+                Pq[ac][t][i] = e1f[ac][t][i] * Pq[ac][t][i];
+                Pb[ac][t][i] = e1f[ac][t][i] * Pb[ac][t][i];
+                Pk[ac][t][i] = e2f[ac][t][i] * Pk[ac][t][i];
+                PkS[ac][t][i] = e2f[ac][t][i] * PkS[ac][t][i];
             }
         }
         if (slow) {

@@ -315,10 +315,10 @@ __device__ __forceinline__ void row_exps(lds_char* sF, int ch0, const float (&f)
 // [DK][CH], as fragment images in global memory (exp(gam) = E1 * exp(gam_R0),
 // exp(gam_C - gam) = E2 * exp(gam_C - gam_Rend), the row-uniform factors taken from rx).
 template <class OT, int DK, bool OUTS>
-__device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], const float (&kv)[4][4],
-                                                    const float (&bv)[4][4], int ch0, const float (&rep)[4][4],
-                                                    lds_char* sXA, lds_char* sXM, lds_char* sY, OT* qg_out,
-                                                    OT* kd_out, const RowExp* rx) {
+__device__ __forceinline__ void scaled_factors(const float (&qv)[4][4], const float (&kv)[4][4],
+                                               const float (&bv)[4][4], int ch0, const float (&e1v)[4][4],
+                                               const float (&e2v)[4][4], lds_char* sXA, lds_char* sXM, lds_char* sY,
+                                               OT* qg_out, OT* kd_out, const RowExp* rx) {
     const int li = lane_id() & 15;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -326,8 +326,7 @@ __device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], con
         float xa[4], xm[4], y[4], qg[4], kd[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float e1, e2;
-            DecayRep<OT>::e12(rep[t][i], e1, e2);
+            const float e1 = e1v[t][i], e2 = e2v[t][i];
             xa[i] = bv[t][i] * kv[t][i] * e1;
             xm[i] = qv[t][i] * e1;
             y[i] = kv[t][i] * e2;
@@ -346,6 +345,16 @@ __device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], con
             for (int i = 0; i < 4; ++i) kd_out[fimg<OT, CH>(ch0 + i, r)] = to_ot<OT>(kd[i]);  // Kd^T [DK][CH]
         }
     }
+}
+// ... with E1, E2 formed here from the lane's log-decays
+template <class OT, int DK, bool OUTS>
+__device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], const float (&kv)[4][4],
+                                                    const float (&bv)[4][4], int ch0, const float (&rep)[4][4],
+                                                    lds_char* sXA, lds_char* sXM, lds_char* sY, OT* qg_out,
+                                                    OT* kd_out, const RowExp* rx) {
+    float e1[4][4], e2[4][4];
+    block_factors<OT>(rep, e1, e2);
+    scaled_factors<OT, DK, OUTS>(qv, kv, bv, ch0, e1, e2, sXA, sXM, sY, qg_out, kd_out, rx);
 }
 
 // X = w * v into a swizzled LDS tile [CH][DV] at columns ch0 .. ch0 + 3
