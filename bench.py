@@ -562,7 +562,9 @@ def measure_config(torch, g2, wl, K, W, stream, hip, with_oracle=True):
 def write_table(rows, path, digest):
     lines = ["# Every workload on one MI355X", "",
              "Kernel source digest: `%s`." % digest[:16],
-             "Produced by `python bench.py --all-configs --table PATH` (steps and warmup per row below).", "",
+             "Produced by `python bench.py --all-configs --steps %d --warmup %d --table PATH`; each time is the "
+             "median over the steps, each after a 512 MiB write that evicts the Infinity Cache (\"cache evicted\"), "
+             "and the mean of the same number of calls back to back." % (rows[0]["steps"], rows[0]["warmup"]), "",
              "| workload | path | ms (cache evicted) | ms (back to back) | tokens/s (evicted) | roofline | "
              "frac | max normwise err (tol) | oracle tokens/s (cores, s) |",
              "|---|---|---|---|---|---|---|---|---|"]
@@ -570,7 +572,7 @@ def write_table(rows, path, digest):
         e = r.get("parity_normwise_rel_err")
         emax = "%.2e (%g)" % (max(e.values()), r["parity_tolerance"]) if e else "-"
         cb = r.get("cpu_baseline")
-        cbs = "%.3g (%d, %.1f)" % (cb["value"], cb["cores"], cb["seconds"]) if cb else "-"
+        cbs = "%.3g (%d, %.3g)" % (cb["value"], cb["cores"], cb["seconds"]) if cb else "-"
         rf = r["roofline"]
         lines.append("| %s | %s | %.4f | %.4f | %.4g | %s %.4f ms | %.3f | %s | %s |" % (
             r["workload"], r["path"], r["ms_cache_evicted"], r["ms_back_to_back"], r["tokens_per_s"],
