@@ -409,7 +409,7 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         rows4(vK, ch0, kv);
         rows4(vB, ch0, bv);  // (activated in phase 1 when the gates came as logits)
         block_factors<OT>(gam[ac], e1f[ac], e2f[ac]);
-        scaled_factors<OT, DK, false>(qv, kv, bv, ch0, e1f[ac], e2f[ac], sXA, sXM, sY, nullptr, nullptr, nullptr);
+        scaled_factors<OT, DK, false>(qv, kv, bv, ch0, e1f[ac], e2f[ac], sXA, sXM, sY, nullptr, nullptr);
     }
     sync_lds();
 

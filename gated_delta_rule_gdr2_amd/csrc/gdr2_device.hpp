@@ -536,6 +536,18 @@ struct LImg {  // fragment image in LDS
     const lds_char* p;
     __device__ __forceinline__ int off(int r, int c) const { return fimg<XT, K>(r, c) * (int)sizeof(XT); }
 };
+// A row-K fragment (lane (li, lq): X[row0 + li][k0 + 8 lq + e]) stored into a fragment image
+// in global memory: one contiguous kilobyte per piece.
+template <class OT, int K>
+__device__ __forceinline__ void store_frag_img(OT* m, int row0, int k0, const typename Frag<OT>::type& f) {
+    const int l = lane_id(), li = l & 15, lq = l >> 4;
+    if constexpr (sizeof(OT) == 2) {
+        *(bf16x8*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq)) = f;
+    } else {
+        *(f32x4*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq)) = __builtin_shufflevector(f, f, 0, 1, 2, 3);
+        *(f32x4*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq + 4)) = __builtin_shufflevector(f, f, 4, 5, 6, 7);
+    }
+}
 // Row-K fragment (as lfrag_rowk8) read straight from a fragment image in global memory.
 template <class OT, int K>
 __device__ __forceinline__ typename Frag<OT>::type gfrag_img(const OT* m, int row0, int k0) {

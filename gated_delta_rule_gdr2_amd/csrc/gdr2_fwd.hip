@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
                 cvt_rows16<OT>(rk[ai], hq, nvalid, kv);
                 cvt_rows16<OT>(rb[ai], hq, nvalid, bv);
                 if (ACT) activate_rows<OT, GATE_B>(bv, nvalid, a.g_scale, a.b_scale);
-                scaled_factors_from<OT, DK, true>(qv, kv, bv, ch0, rep, sXA, sXM, sY, qg_out, kd_out, &rx);
+                scaled_factors_from<OT, DK, true>(qv, kv, bv, ch0, rep, sXA, sXM, sY, qg_out, &rx);
             }
         }
 #pragma unroll
@@ -278,9 +278,21 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
     sync_lds();
     const bool slow = (lds_load<int>(smem + LS::FLAG) | lds_load<int>(smem + LS::FLAG + 4) |
                        lds_load<int>(smem + LS::FLAG + 8) | lds_load<int>(smem + LS::FLAG + 12)) != 0;
+    const LSwz<OT, DK> vXA{sXA}, vXM{sXM}, vY{sY};
+
+    // ---- Kd^T = (k * exp(gam_C - gam))^T out to global as a fragment image, read from the Y
+    // tile (Y = k * E2) by transposing reads, each lane's 8 tokens in one 16-token block R
+    // whose factor exp(gam_C - gam_Rend) it applies; one contiguous kilobyte per fragment.
+    for (int f = wv; f < (DK / 16) * (CH / 32); f += 4) {
+        const int kt = f / (CH / 32), tb = f % (CH / 32);
+        FT fr = lfrag_colk8<OT>(vY, 16 * kt, 32 * tb);  // lane (li, lq): Y[32 tb + 8 lq + e][16 kt + li]
+        const float sc = lds_load<float>(sF + ((F_ECE + (32 * tb + 8 * lq) / 16) * DK + 16 * kt + li) * 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fr[e] = to_ot<OT>(to_f(fr[e]) * sc);
+        store_frag_img<OT, CH>(kd_out, 16 * kt, 32 * tb, fr);
+    }
 
     // ---- phase 2a: M = lower(Qg Khat^T), computed as M^T tiles, out to global
-    const LSwz<OT, DK> vXA{sXA}, vXM{sXM}, vY{sY};
     const LSwz<OT, DV> vX{sX};
     for (int p = wv; p < NPAIR; p += 4) {
         int R, I;
