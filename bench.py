@@ -379,11 +379,13 @@ def scan_workloads():
             replace(long_wl, H=1, name="fwdbwd_bf16_b1h1t16384d128_h0"), WORKLOADS["fwdbwd_bf16_b2h16t4096d128"]]
 
 
-def scan_sweep(torch, g2, K=10):
+def scan_sweep(torch, g2, K=10, table=None):
     """Chunk-parallel scan: fwd+bwd step time against the segment count on the long-sequence
-    workload, the same with 4 and 1 heads, and the training shape. One JSON line each."""
+    workload, the same with 4 and 1 heads, and the training shape. One JSON line each, and
+    with `table` a markdown table there."""
     from gated_delta_rule_gdr2_amd.inputs import make_inputs
     stream = torch.cuda.current_stream()
+    rows = []
     for wl in scan_workloads():
         x = {k: (None if v is None else v.cuda()) for k, v in make_inputs(wl).items()}
         auto = next(s for s in range(1, 33) if g2.gdr2_seg_workspace_bytes(
@@ -392,8 +394,25 @@ def scan_sweep(torch, g2, K=10):
         for segments in (1, 2, 4, 8, 16, 32):
             r = seg_step_ms(torch, g2, wl, segments, K, stream, x)
             r.update({"workload": wl.name, "automatic_segments": auto})
+            rows.append(r)
             print(json.dumps(r), flush=True)
         del x
+    if table:
+        lines = ["# Chunk-parallel scan: fwd+bwd step time against the chain segment count", "",
+                 "Kernel source digest: `%s`." % source_digest()[:16],
+                 "Command (MI355X, one GPU): `python bench.py --scan-sweep --table PATH`", "",
+                 "Each line: median of %d fwd+bwd steps (`gdr2_fwd_seg(save_for_bwd=1)` + "
+                 "`gdr2_bwd_seg(fwd_saved=1)`), bf16, d_k = d_v = 128, stage times from the library's HIP "
+                 "events on the launch stream (the chain stages include the summary and scan kernels). "
+                 "`auto` = the count `gdr2_fwd` / `gdr2_bwd` pick for the shape." % K, "",
+                 "| workload | segments | step ms | fwd_intra | fwd chain stage | bwd chain stage | bwd_intra | auto |",
+                 "|---|---|---|---|---|---|---|---|"]
+        for r in rows:
+            lines.append("| %s | %d | %.3f | %.3f | %.3f | %.3f | %.3f | %d |" % (
+                r["workload"], r["segments"], r["ms_per_step"], r["fwd_intra"], r["fwd_chain"], r["bwd_chain"],
+                r["bwd_intra"], r["automatic_segments"]))
+        with open(table, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
 
 
 def chain_scan_measurement(torch, g2, K, stream):
@@ -621,7 +640,7 @@ def main():
                          "the run that rocprofv3 traces")
     ap.add_argument("--all-configs", action="store_true",
                     help="time every workload (forward-only ones as forward steps), each next to an oracle pass")
-    ap.add_argument("--table", default=None, help="with --all-configs: write a markdown table here")
+    ap.add_argument("--table", default=None, help="with --all-configs or --scan-sweep: write a markdown table here")
     ap.add_argument("--scan-sweep", action="store_true",
                     help="print fwd+bwd step times against the chain segment count (chunk-parallel scan) and exit")
     args = ap.parse_args()
@@ -646,7 +665,7 @@ def main():
     from gated_delta_rule_gdr2_amd.inputs import HEADLINE, WORKLOADS, make_inputs
 
     if args.scan_sweep:
-        scan_sweep(torch, g2)
+        scan_sweep(torch, g2, table=args.table)
         return
     if args.all_configs:
         all_configs(torch, g2, args.steps, args.warmup, args.table, not args.no_cpu_baseline)

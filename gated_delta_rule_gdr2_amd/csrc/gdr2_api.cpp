@@ -40,17 +40,22 @@ void seg_plan(int T, int segments, int& nseg, int& seg_len) {
 }
 
 // The segment count gdr2_fwd / gdr2_bwd use. The chains run one workgroup per (sequence,
-// 16 value columns) and their throughput is set by the operand traffic of all walks
-// together, which the scan roughly triples, so it pays only when the walks are too few
-// to fill the 256 compute units: up to 128 chain workgroups, 256 / (workgroups)
-// segments, at most 8, each of at least 8 chunks.
+// 16 value columns) and a step's cost is set by the operands each walk moves through its
+// compute unit, which the scan roughly triples (summaries, transitions, the second walk),
+// so it pays only when the walks are too few to fill the 256 compute units: up to 128
+// chain walks, 512 / (walks) segments (the main walks then use 32-column slices), at most
+// 8, each of at least 16 chunks (shorter segments spend more on the summaries than they
+// save). Measured at d = 128: T = 16384 fwd+bwd, 16 heads best with 4 segments (1.12 ms
+// against 1.22 with one), 4 heads with 4-8 (0.46-0.47 against 0.73), one head with 8
+// (0.30 against 0.63); the forward alone at 16 heads, T = 2048, is faster with 2 segments
+// of 16 chunks than with 4 of 8 (0.080 against 0.100 ms).
 int auto_segments(int B, int T, int H, int dv) {
     const long long wgs = (long long)B * H * (dv / 16);
     const int NT = (T + 63) / 64;
     if (wgs < 1 || wgs > 128) return 1;
-    int n = (int)(256 / wgs);
+    int n = (int)(512 / wgs);
     if (n > 8) n = 8;
-    if (n > NT / 8) n = NT / 8;
+    if (n > NT / 16) n = NT / 16;
     return n < 1 ? 1 : n;
 }
 

@@ -110,7 +110,7 @@ int gdr2_bwd(const void* q, const void* k, const void* v, const void* g, const v
  * Results equal the one-walk chains up to rounding order. The work grows (about 3x the
  * chain's), so it pays only when the sequences are too few to fill the GPU: gdr2_fwd,
  * gdr2_bwd and their _logits variants use it by themselves when B * H * dv / 16 <= 128,
- * with 256 / (B * H * dv / 16) segments, at most 8, of at least 8 chunks each (their
+ * with 512 / (B * H * dv / 16) segments, at most 8, of at least 16 chunks each (their
  * workspace sizes include it), and walk the chains whole otherwise; segments = 1 here
  * forces one walk. Workspace: gdr2_seg_workspace_bytes (with
  * save_for_bwd = 1 for the backward; a gdr2_bwd_seg(..., fwd_saved = 1) needs the

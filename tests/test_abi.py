@@ -245,8 +245,8 @@ def test_segment_entry_points_validate(lib):
 
 def test_automatic_segments(lib):
     """The plain entry points size (and run) the chunk-parallel scan by themselves only
-    when the chain workgroups (B * H * dv / 16) are at most 128: 256 / workgroups
-    segments, at most 8, of at least 8 chunks each."""
+    when the chain walks (B * H * dv / 16) are at most 128: 512 / walks segments, at
+    most 8, of at least 16 chunks each."""
     BF = g2.DTYPE_BF16
 
     def auto(B, T, H, dv):
@@ -255,13 +255,14 @@ def test_automatic_segments(lib):
         return hits[0]
 
     assert auto(2, 4096, 16, 128) == 1       # 256 workgroups
-    assert auto(1, 16384, 16, 128) == 2      # 128
-    assert auto(1, 2048, 16, 128) == 2       # 128, 32 chunks
+    assert auto(1, 16384, 16, 128) == 4      # 128
+    assert auto(1, 2048, 16, 128) == 2       # 128, 32 chunks: segments of 16
     assert auto(8, 2048, 16, 128) == 1       # 1024
     assert auto(1, 16384, 4, 128) == 8       # 32
     assert auto(1, 16384, 2, 64) == 8        # 8
-    assert auto(1, 4096, 1, 128) == 8        # 64 chunks
-    assert auto(1, 1024, 1, 128) == 2        # 16 chunks: segments of 8
+    assert auto(1, 4096, 1, 128) == 4        # 64 chunks: segments of 16
+    assert auto(1, 2048, 1, 128) == 2        # 32 chunks
+    assert auto(1, 1024, 1, 128) == 1        # 16 chunks
     assert auto(1, 500, 1, 128) == 1         # 8 chunks
 
 

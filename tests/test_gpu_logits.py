@@ -201,7 +201,7 @@ def test_logits_with_automatic_segments():
     themselves (as gdr2_fwd / gdr2_bwd do), with the gates activated in the kernels."""
     wl = small(DK=128, DV=128, T=4100, dtype="bf16", B=1, H=1, h0_std=0.05, seed=43, b_scale=2.0, g_scale=0.3)
     assert g2.gdr2_fwd_workspace_bytes(1, 4100, 1, 128, 128, 64, g2.DTYPE_BF16, True) == \
-        g2.gdr2_seg_workspace_bytes(1, 4100, 1, 128, 128, 64, 8, g2.DTYPE_BF16, True)
+        g2.gdr2_seg_workspace_bytes(1, 4100, 1, 128, 128, 64, 4, g2.DTYPE_BF16, True)  # 4 segments
     inp = make_inputs(wl, gates="logits")
     args = gpu_args(inp)
     h0, do = inp["h0"].cuda(), inp["do"].cuda()

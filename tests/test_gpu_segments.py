@@ -170,11 +170,11 @@ def test_segmented_long_sequence_full_size():
 
 def test_plain_entry_points_segment_few_sequences():
     """gdr2_fwd / gdr2_bwd cut the chains by themselves when the sequences are few: one
-    sequence of 65 chunks takes 8 segments, bitwise the same as gdr2_fwd_seg(8), and
+    sequence of 65 chunks takes 4 segments, bitwise the same as gdr2_fwd_seg(4), and
     matches the oracle."""
     wl = small(DK=128, DV=128, T=4100, dtype="bf16", B=1, H=1, h0_std=0.05, seed=29)
     assert g2.gdr2_fwd_workspace_bytes(1, 4100, 1, 128, 128, 64, g2.DTYPE_BF16, True) == \
-        g2.gdr2_seg_workspace_bytes(1, 4100, 1, 128, 128, 64, 8, g2.DTYPE_BF16, True)
+        g2.gdr2_seg_workspace_bytes(1, 4100, 1, 128, 128, 64, 4, g2.DTYPE_BF16, True)
     inp = make_inputs(wl)
     x = {k: v.cuda() for k, v in inp.items()}
     args = [x[n] for n in NAMES] + [x["h0"]]
@@ -183,7 +183,7 @@ def test_plain_entry_points_segment_few_sequences():
     torch.cuda.synchronize()
     plain = {"o": o, "ht": ht}
     plain.update(gr)
-    seg = run_seg(x, 8)
+    seg = run_seg(x, 4)
     for key in ["o", "ht"] + GRADS + ["dh0"]:
         assert torch.equal(plain[key], seg[key]), key
     ref = oracle_all(inp, None)
