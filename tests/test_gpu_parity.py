@@ -340,10 +340,15 @@ def test_mixed_strong_and_weak_decay(dtype, DK, DV, T):
 
 
 MANY_SHORT = [
-    # many sequences of two chunks, the second ragged: large grids (4096 chain workgroups for
-    # the first), every sequence's last chunk partial, random h0 and dht
+    # many sequences of two or three chunks, the last ragged: large grids, every sequence's
+    # last chunk partial, random h0 and dht. With 512 or more 16-column chain walks the chains
+    # run 32-column slices (all but the 8 x 8 fp32 case); every d_k / d_v and both dtypes.
     dict(DK=128, DV=128, T=65, dtype="bf16", B=16, H=16, h0_std=0.05),
     dict(DK=64, DV=64, T=70, dtype="f32", B=8, H=8, h0_std=0.05),
+    dict(DK=64, DV=64, T=70, dtype="f32", B=8, H=16, h0_std=0.05),
+    dict(DK=64, DV=64, T=130, dtype="bf16", B=8, H=16, h0_std=0.05),
+    dict(DK=128, DV=64, T=100, dtype="bf16", B=8, H=16),
+    dict(DK=64, DV=128, T=100, dtype="bf16", B=4, H=16, h0_std=0.05),
 ]
 
 
