@@ -392,8 +392,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             dww[e] = to_ot<OT>(to_f(dy[e]) * to_f(rv[i][e]) * dwdz);
         }
         if (r < nvalid) {
-            *(RW*)((OT*)a.dv + rowk0 * DV + (size_t)r * rsv + ch) = dvv;
-            *(RW*)((OT*)a.dw + rowk0 * DV + (size_t)r * rsv + ch) = dww;
+            __builtin_nontemporal_store(dvv, (RW*)((OT*)a.dv + rowk0 * DV + (size_t)r * rsv + ch));
+            __builtin_nontemporal_store(dww, (RW*)((OT*)a.dw + rowk0 * DV + (size_t)r * rsv + ch));
         }
     }
     sync_lds();  // dO, Delta, dY are dead; their slots take the key/query factors

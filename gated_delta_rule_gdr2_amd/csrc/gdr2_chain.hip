@@ -160,14 +160,18 @@ __device__ __forceinline__ void stage_rows(lds_char* stage, const f32x4& s0, con
 }
 // ... into a [DK][DV] state in fragment-major layout (fmaj_off), where each piece is
 // contiguous and a wave's pieces form whole 512-byte runs
-template <class OT, int DV>
+template <class OT, int DV, bool NT = false>
 __device__ __forceinline__ void store_rows(OT* dst, int row0, int j, const f32x4 (&pend)[RowStore<OT>::PER_LANE]) {
     using R = RowStore<OT>;
     const int l = lane_id();
 #pragma unroll
     for (int k = 0; k < R::PER_LANE; ++k) {
         const int p = l + 64 * k, row = p / R::PPR, col = (p % R::PPR) * R::EPP;
-        *(f32x4*)(dst + fmaj_off<DV>(row0 + row, 16 * j + col)) = pend[k];
+        f32x4* q = (f32x4*)(dst + fmaj_off<DV>(row0 + row, 16 * j + col));
+        if (NT)
+            __builtin_nontemporal_store(pend[k], q);
+        else
+            *q = pend[k];
     }
 }
 
@@ -692,10 +696,10 @@ __device__ __forceinline__ void bwd_flush(const Args& a, int s, int j, BwdPend<O
 #pragma unroll
     for (int ch = 0; ch < NC; ++ch) {
         const int jt = NC * j + ch;
-        store_rows<OT, DV>((OT*)(a.ws + L.o_ds) + cid * L.ds, 32 * wv, jt, pd.st[ch]);
+        store_rows<OT, DV, true>((OT*)(a.ws + L.o_ds) + cid * L.ds, 32 * wv, jt, pd.st[ch]);
         OT* dy = (OT*)(a.ws + L.o_dy) + cid * L.dy + jt * 4 * 256;
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) store_tile<OT>(dy + (wv * TPW + u) * 256, pd.Y[u][ch]);
+        for (int u = 0; u < TPW; ++u) store_tile<OT, true>(dy + (wv * TPW + u) * 256, pd.Y[u][ch]);
     }
 }
 

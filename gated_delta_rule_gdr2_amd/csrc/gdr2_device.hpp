@@ -180,6 +180,23 @@ __device__ __forceinline__ void st4(float* p, const float in[4]) {
     *(f32x4*)p = v;
 }
 
+// Non-temporal variants, for results that another kernel reads later (the per-chunk
+// operands the forward intra-chunk kernel leaves for the chains, the backward chain's
+// outputs, the gradients): measured on MI355X, the hint speeds up the kernels that come
+// after (at the 4096-token training shape the forward chain that reads the operands takes
+// about 10 % less time, the whole step about 5 %), while the forward chain's own outputs
+// are faster with plain stores.
+__device__ __forceinline__ void st4_nt(bf16* p, const float in[4]) {
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (bf16)in[i];
+    __builtin_nontemporal_store(v, (bf16x4*)p);
+}
+__device__ __forceinline__ void st4_nt(float* p, const float in[4]) {
+    f32x4 v = {in[0], in[1], in[2], in[3]};
+    __builtin_nontemporal_store(v, (f32x4*)p);
+}
+
 // ----------------------------------------------------------------------------- fragment loads
 // "rowk": lane (li, lq) reads X[row0 + li][k0 + kmap(lq, e)] -- contiguous along K
 // (two runs of four). X is row-major with leading dimension ld (elements).
@@ -547,15 +564,16 @@ struct LImg {  // fragment image in LDS
     __device__ __forceinline__ int off(int r, int c) const { return fimg<XT, K>(r, c) * (int)sizeof(XT); }
 };
 // A row-K fragment (lane (li, lq): X[row0 + li][k0 + 8 lq + e]) stored into a fragment image
-// in global memory: one contiguous kilobyte per piece.
+// in global memory: one contiguous kilobyte per piece (non-temporal, see st4_nt).
 template <class OT, int K>
 __device__ __forceinline__ void store_frag_img(OT* m, int row0, int k0, const typename Frag<OT>::type& f) {
     const int l = lane_id(), li = l & 15, lq = l >> 4;
     if constexpr (sizeof(OT) == 2) {
-        *(bf16x8*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq)) = f;
+        __builtin_nontemporal_store(f, (bf16x8*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq)));
     } else {
-        *(f32x4*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq)) = __builtin_shufflevector(f, f, 0, 1, 2, 3);
-        *(f32x4*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq + 4)) = __builtin_shufflevector(f, f, 4, 5, 6, 7);
+        const f32x4 x0 = __builtin_shufflevector(f, f, 0, 1, 2, 3), x1 = __builtin_shufflevector(f, f, 4, 5, 6, 7);
+        __builtin_nontemporal_store(x0, (f32x4*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq)));
+        __builtin_nontemporal_store(x1, (f32x4*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq + 4)));
     }
 }
 // Row-K fragment (as lfrag_rowk8) read straight from a fragment image in global memory.
@@ -570,11 +588,14 @@ __device__ __forceinline__ typename Frag<OT>::type gfrag_img(const OT* m, int ro
         return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 }
-// accumulator tile dump: 64 lanes x 4 elements
-template <class OT>
+// accumulator tile dump: 64 lanes x 4 elements (NT: non-temporal, see st4_nt)
+template <class OT, bool NT = false>
 __device__ __forceinline__ void store_tile(OT* base, const f32x4& d) {
     float t[4] = {d[0], d[1], d[2], d[3]};
-    st4(base + lane_id() * 4, t);
+    if (NT)
+        st4_nt(base + lane_id() * 4, t);
+    else
+        st4(base + lane_id() * 4, t);
 }
 template <class OT>
 __device__ __forceinline__ f32x4 load_tile(const OT* base) {

@@ -306,13 +306,13 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
         float v[4];  // lane holds M[16R + li][16I + 4lq + i]
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = (R == I && 4 * lq + i > li) ? 0.f : acc[i];
-        st4(m_out + fimg<OT, CH>(16 * R + li, 16 * I + 4 * lq), v);
+        st4_nt(m_out + fimg<OT, CH>(16 * R + li, 16 * I + 4 * lq), v);
     }
     for (int u = wv; u < 6; u += 4) {
         int R, I;
         upper_ri(u, R, I);
         const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        st4(m_out + fimg<OT, CH>(16 * R + li, 16 * I + 4 * lq), z);
+        st4_nt(m_out + fimg<OT, CH>(16 * R + li, 16 * I + 4 * lq), z);
     }
     sync_lds();  // XM is dead from here on; its slot becomes A
 
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) mma(acc, aT[kb], lfrag_colk<OT, OT>(vX, 16 * j, 32 * kb));
-            store_tile<OT>(u_out + (j * 4 + tt) * 256, acc);
+            store_tile<OT, true>(u_out + (j * 4 + tt) * 256, acc);
         }
 #pragma unroll
         for (int at = 0; at < DK / 16; ++at) {
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vXA, 16 * at, 32 * kb), aT[kb]);  // XA holds K_b
             float v[4] = {acc[0], acc[1], acc[2], acc[3]};  // Wm[16tt + li][16at + 4lq + i]
-            st4(wm_out + fimg<OT, DK>(16 * tt + li, 16 * at + 4 * lq), v);
+            st4_nt(wm_out + fimg<OT, DK>(16 * tt + li, 16 * at + 4 * lq), v);
         }
     }
     if (TRAIN) {  // T for the backward chain
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
             const int r = idx / 16, c4 = 4 * (idx % 16);
             float v[4];
             lds_get4<float>(sT + swz<float, CH>(r, c4) * 4, v);
-            st4(t_out + swz<OT, CH>(r, c4), v);
+            st4_nt(t_out + swz<OT, CH>(r, c4), v);
         }
     }
 }

@@ -335,7 +335,7 @@ __device__ __forceinline__ void scaled_factors(const float (&qv)[4][4], const fl
         lds_put4<OT>(sXA + o, xa);
         lds_put4<OT>(sXM + o, xm);
         lds_put4<OT>(sY + o, y);
-        if constexpr (OUTS) st4(qg_out + fimg<OT, DK>(r, ch0), qg);
+        if constexpr (OUTS) st4_nt(qg_out + fimg<OT, DK>(r, ch0), qg);
     }
 }
 // ... with E1, E2 formed here from the lane's log-decays
@@ -392,7 +392,8 @@ __device__ __forceinline__ void dma_rows(const OT* base, size_t rs, int nvalid, 
 }
 // Rows 0 .. nvalid - 1 of a swizzled LDS tile [CH][RL] out to a row-major tensor (row
 // stride rs elements), 16 bytes per lane with consecutive lanes on consecutive chunks
-// of a row, so every request is a whole cache line (all threads of the workgroup).
+// of a row, so every request is a whole cache line (all threads of the workgroup);
+// non-temporal stores (see st4_nt).
 template <class OT, int RL, int NTHR>
 __device__ __forceinline__ void store_rows_tiles(const lds_char* tile, OT* dst, size_t rs, int nvalid) {
     constexpr int EPC = 16 / (int)sizeof(OT);
@@ -402,7 +403,7 @@ __device__ __forceinline__ void store_rows_tiles(const lds_char* tile, OT* dst, 
         const int u = (int)threadIdx.x + NTHR * i, row = u / NCH, pos = u % NCH;
         if ((CH * NCH % NTHR == 0 || u < CH * NCH) && row < nvalid) {
             const f32x4 x = lds_load<f32x4>(tile + u * 16);
-            *(f32x4*)(dst + (size_t)row * rs + (pos ^ swz_f<OT, RL>(row)) * EPC) = x;
+            __builtin_nontemporal_store(x, (f32x4*)(dst + (size_t)row * rs + (pos ^ swz_f<OT, RL>(row)) * EPC));
         }
     }
 }

@@ -108,8 +108,11 @@ __global__ __launch_bounds__(128) void k_step(Args a) {
             st4((OT*)a.o + (((size_t)bidx * a.T + t) * a.H + h) * DV + col, ov);
         }
     }
+    // the state goes back with non-temporal stores: it is not read again within the call,
+    // and on this path they stream to HBM faster (a 512 MB state updated in place: 0.177
+    // against 0.217 ms per call; non-temporal loads, by contrast, are slower)
 #pragma unroll
-    for (int i = 0; i < NI; ++i) *(f32x4*)(hs + (size_t)(rg + 8 * i) * DV) = S[i];
+    for (int i = 0; i < NI; ++i) __builtin_nontemporal_store(S[i], (f32x4*)(hs + (size_t)(rg + 8 * i) * DV));
 }
 
 template <class OT, int DK, int DV>
