@@ -121,7 +121,7 @@ __device__ __forceinline__ void undump_tiles(const OT* src, lds_char* dst) {
 
 constexpr int BWD_NW = 8;  // waves per workgroup of the backward intra-chunk kernel
 
-template <class OT, int DK, int DV, bool ACT>
+template <class OT, int DK, int DV, bool ACT, bool NT>
 __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     using LS = BwdLds<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
@@ -392,8 +392,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
             dww[e] = to_ot<OT>(to_f(dy[e]) * to_f(rv[i][e]) * dwdz);
         }
         if (r < nvalid) {
-            __builtin_nontemporal_store(dvv, (RW*)((OT*)a.dv + rowk0 * DV + (size_t)r * rsv + ch));
-            __builtin_nontemporal_store(dww, (RW*)((OT*)a.dw + rowk0 * DV + (size_t)r * rsv + ch));
+            store_out<NT>((RW*)((OT*)a.dv + rowk0 * DV + (size_t)r * rsv + ch), dvv);
+            store_out<NT>((RW*)((OT*)a.dw + rowk0 * DV + (size_t)r * rsv + ch), dww);
         }
     }
     sync_lds();  // dO, Delta, dY are dead; their slots take the key/query factors
@@ -617,10 +617,10 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     sync_lds();
 
     // ---- dq, dk, db, dg out of the staged tiles in whole rows
-    store_rows_tiles<OT, DK, NTHR>(sQ, (OT*)a.dq + rowk0 * DK, rsk, nvalid);
-    store_rows_tiles<OT, DK, NTHR>(sK, (OT*)a.dk + rowk0 * DK, rsk, nvalid);
-    store_rows_tiles<OT, DK, NTHR>(sB, (OT*)a.db + rowk0 * DK, rsk, nvalid);
-    store_rows_tiles<OT, DK, NTHR>(sG, (OT*)a.dg + rowk0 * DK, rsk, nvalid);
+    store_rows_tiles<OT, DK, NTHR, NT>(sQ, (OT*)a.dq + rowk0 * DK, rsk, nvalid);
+    store_rows_tiles<OT, DK, NTHR, NT>(sK, (OT*)a.dk + rowk0 * DK, rsk, nvalid);
+    store_rows_tiles<OT, DK, NTHR, NT>(sB, (OT*)a.db + rowk0 * DK, rsk, nvalid);
+    store_rows_tiles<OT, DK, NTHR, NT>(sG, (OT*)a.dg + rowk0 * DK, rsk, nvalid);
 }
 
 size_t bwd_intra_lds_bytes(int DK, int DV, int esz) {
@@ -635,7 +635,8 @@ size_t bwd_intra_lds_bytes(int DK, int DV, int esz) {
 template <class OT, int DK, int DV>
 static hipError_t launch_bwd_t(const Args& a, hipStream_t stream) {
     const size_t lds = BwdLds<OT, DK, DV>::BYTES;
-    auto intra = a.act ? k_bwd_intra<OT, DK, DV, true> : k_bwd_intra<OT, DK, DV, false>;
+    auto intra = a.nt_out ? (a.act ? k_bwd_intra<OT, DK, DV, true, true> : k_bwd_intra<OT, DK, DV, false, true>)
+                          : (a.act ? k_bwd_intra<OT, DK, DV, true, false> : k_bwd_intra<OT, DK, DV, false, false>);
     hipError_t e = hipFuncSetAttribute((const void*)intra, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     // stage events: 0 at the start of the chain, 1 at its end, 2 at the end of the intra-chunk kernel

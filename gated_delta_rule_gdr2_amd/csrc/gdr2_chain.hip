@@ -160,18 +160,14 @@ __device__ __forceinline__ void stage_rows(lds_char* stage, const f32x4& s0, con
 }
 // ... into a [DK][DV] state in fragment-major layout (fmaj_off), where each piece is
 // contiguous and a wave's pieces form whole 512-byte runs
-template <class OT, int DV, bool NT = false>
+template <class OT, int DV, bool NTS = false>
 __device__ __forceinline__ void store_rows(OT* dst, int row0, int j, const f32x4 (&pend)[RowStore<OT>::PER_LANE]) {
     using R = RowStore<OT>;
     const int l = lane_id();
 #pragma unroll
     for (int k = 0; k < R::PER_LANE; ++k) {
         const int p = l + 64 * k, row = p / R::PPR, col = (p % R::PPR) * R::EPP;
-        f32x4* q = (f32x4*)(dst + fmaj_off<DV>(row0 + row, 16 * j + col));
-        if (NT)
-            __builtin_nontemporal_store(pend[k], q);
-        else
-            *q = pend[k];
+        store_out<NTS>((f32x4*)(dst + fmaj_off<DV>(row0 + row, 16 * j + col)), pend[k]);
     }
 }
 
@@ -686,7 +682,7 @@ struct BwdPend {
     int c;
 };
 
-template <class OT, int DK, int DV, int NW, int NC>
+template <class OT, int DK, int DV, int NW, int NC, bool NTS>
 __device__ __forceinline__ void bwd_flush(const Args& a, int s, int j, BwdPend<OT, NW, NC>& pd) {
     if (pd.c < 0) return;
     constexpr int TPW = BwdPend<OT, NW, NC>::TPW;
@@ -696,10 +692,10 @@ __device__ __forceinline__ void bwd_flush(const Args& a, int s, int j, BwdPend<O
 #pragma unroll
     for (int ch = 0; ch < NC; ++ch) {
         const int jt = NC * j + ch;
-        store_rows<OT, DV, true>((OT*)(a.ws + L.o_ds) + cid * L.ds, 32 * wv, jt, pd.st[ch]);
+        store_rows<OT, DV, NTS>((OT*)(a.ws + L.o_ds) + cid * L.ds, 32 * wv, jt, pd.st[ch]);
         OT* dy = (OT*)(a.ws + L.o_dy) + cid * L.dy + jt * 4 * 256;
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) store_tile<OT, true>(dy + (wv * TPW + u) * 256, pd.Y[u][ch]);
+        for (int u = 0; u < TPW; ++u) store_tile<OT, NTS>(dy + (wv * TPW + u) * 256, pd.Y[u][ch]);
     }
 }
 
@@ -812,7 +808,7 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4 (&dS0
     pd.c = c;
 }
 
-template <class OT, int DK, int DV, int NW, int NC, bool DBUF, bool SUM>
+template <class OT, int DK, int DV, int NW, int NC, bool DBUF, bool SUM, bool NTS = false>
 __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, const WalkSpec& w, lds_char* b0, lds_char* b1,
                                          lds_char* xs, lds_char* stage_base, lds_char* pfslot) {
     using B = BwdChainBuf<OT, DK, DV, NC>;
@@ -911,10 +907,10 @@ __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, const Walk
     pd.c = -1;
     for (int n = 0; n < NT; ++n) {
         sync_lds();  // A_n
-        bwd_flush<OT, DK, DV, NW, NC>(a, s, j, pd);
+        bwd_flush<OT, DK, DV, NW, NC, NTS>(a, s, j, pd);
         bwd_step<OT, DK, DV, NW, NC, SUM>(last - n, (DBUF && (n & 1)) ? b1 : b0, dS0, dS1, stage, xs, pd);
     }
-    bwd_flush<OT, DK, DV, NW, NC>(a, s, j, pd);
+    bwd_flush<OT, DK, DV, NW, NC, NTS>(a, s, j, pd);
     if (w.end) {
 #pragma unroll
         for (int ch = 0; ch < NC; ++ch) {
@@ -936,7 +932,7 @@ struct BwdChainLds {
     static constexpr bool DBUF = 2 * BwdChainBuf<OT, DK, DV, NC>::BYTES + XBYTES + SBYTES + 256 <= LDS_LIMIT;
 };
 
-template <class OT, int DK, int DV, int NC>
+template <class OT, int DK, int DV, int NC, bool NTS>
 __global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_bwd_chain(Args a) {
     using B = BwdChainBuf<OT, DK, DV, NC>;
     using LZ = BwdChainLds<OT, DK, DV, NC, true>;
@@ -970,7 +966,7 @@ __global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_bwd_chain(Args a) {
     w.ld_end = DV;
     w.col = 16 * NC * j;
     w.noU = false;
-    bwd_walk<OT, DK, DV, NW, NC, DBUF, false>(a, s, j, w, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch,
+    bwd_walk<OT, DK, DV, NW, NC, DBUF, false, NTS>(a, s, j, w, (lds_char*)buf0, (lds_char*)buf1, (lds_char*)xch,
                                               (lds_char*)stage, (lds_char*)pfslot);
 }
 
@@ -1139,12 +1135,18 @@ hipError_t launch_bwd_chain_t(const Args& a, hipStream_t stream, hipEvent_t star
     }
     int nc = 1;
     if ((e = chain_nc((long long)S * a.nseg * NJ1, nc)) != hipSuccess) return e;
-    if (nc == 2)
-        hipExtLaunchKernelGGL((k_bwd_chain<OT, DK, DV, 2>), dim3(S * a.nseg * (NJ1 / 2)), block, 0, stream, start,
-                              stop, 0, a);
-    else
-        hipExtLaunchKernelGGL((k_bwd_chain<OT, DK, DV, 1>), dim3(S * a.nseg * NJ1), block, 0, stream, start, stop, 0,
-                              a);
+    const dim3 grid(S * a.nseg * (NJ1 / nc));
+    if (nc == 2) {
+        if (a.nt_out)
+            hipExtLaunchKernelGGL((k_bwd_chain<OT, DK, DV, 2, true>), grid, block, 0, stream, start, stop, 0, a);
+        else
+            hipExtLaunchKernelGGL((k_bwd_chain<OT, DK, DV, 2, false>), grid, block, 0, stream, start, stop, 0, a);
+    } else {
+        if (a.nt_out)
+            hipExtLaunchKernelGGL((k_bwd_chain<OT, DK, DV, 1, true>), grid, block, 0, stream, start, stop, 0, a);
+        else
+            hipExtLaunchKernelGGL((k_bwd_chain<OT, DK, DV, 1, false>), grid, block, 0, stream, start, stop, 0, a);
+    }
     return hipGetLastError();
 }
 

@@ -182,10 +182,12 @@ __device__ __forceinline__ void st4(float* p, const float in[4]) {
 
 // Non-temporal variants, for results that another kernel reads later (the per-chunk
 // operands the forward intra-chunk kernel leaves for the chains, the backward chain's
-// outputs, the gradients): measured on MI355X, the hint speeds up the kernels that come
-// after (at the 4096-token training shape the forward chain that reads the operands takes
-// about 10 % less time, the whole step about 5 %), while the forward chain's own outputs
-// are faster with plain stores.
+// outputs, the gradients), used when the problem's data is large next to the Infinity
+// Cache (Args::nt_out). Measured on MI355X: at the 4096-token training shape (176 MB of
+// per-chunk operands) the hint speeds up the kernels that come after -- the forward chain
+// that reads the operands takes about 10 % less time, the whole step about 5 % -- while at
+// 2048 tokens x 16 heads forward-only (37 MB, which the cache holds) plain stores are 11 %
+// faster. The forward chain's own outputs are faster with plain stores at every size.
 __device__ __forceinline__ void st4_nt(bf16* p, const float in[4]) {
     bf16x4 v;
 #pragma unroll
@@ -195,6 +197,22 @@ __device__ __forceinline__ void st4_nt(bf16* p, const float in[4]) {
 __device__ __forceinline__ void st4_nt(float* p, const float in[4]) {
     f32x4 v = {in[0], in[1], in[2], in[3]};
     __builtin_nontemporal_store(v, (f32x4*)p);
+}
+// NT is a compile-time choice (the kernels are instantiated both ways): with a run-time
+// branch the compiler merges the two stores into one and drops the non-temporal hint.
+template <bool NT, class OT>
+__device__ __forceinline__ void st4_out(OT* p, const float in[4]) {
+    if constexpr (NT)
+        st4_nt(p, in);
+    else
+        st4(p, in);
+}
+template <bool NT, class T>
+__device__ __forceinline__ void store_out(T* p, const T& v) {
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
 }
 
 // ----------------------------------------------------------------------------- fragment loads
@@ -564,16 +582,16 @@ struct LImg {  // fragment image in LDS
     __device__ __forceinline__ int off(int r, int c) const { return fimg<XT, K>(r, c) * (int)sizeof(XT); }
 };
 // A row-K fragment (lane (li, lq): X[row0 + li][k0 + 8 lq + e]) stored into a fragment image
-// in global memory: one contiguous kilobyte per piece (non-temporal, see st4_nt).
-template <class OT, int K>
+// in global memory: one contiguous kilobyte per piece (NT: non-temporal, see st4_nt).
+template <class OT, int K, bool NT>
 __device__ __forceinline__ void store_frag_img(OT* m, int row0, int k0, const typename Frag<OT>::type& f) {
     const int l = lane_id(), li = l & 15, lq = l >> 4;
     if constexpr (sizeof(OT) == 2) {
-        __builtin_nontemporal_store(f, (bf16x8*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq)));
+        store_out<NT>((bf16x8*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq)), f);
     } else {
         const f32x4 x0 = __builtin_shufflevector(f, f, 0, 1, 2, 3), x1 = __builtin_shufflevector(f, f, 4, 5, 6, 7);
-        __builtin_nontemporal_store(x0, (f32x4*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq)));
-        __builtin_nontemporal_store(x1, (f32x4*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq + 4)));
+        store_out<NT>((f32x4*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq)), x0);
+        store_out<NT>((f32x4*)(m + fimg<OT, K>(row0 + li, k0 + 8 * lq + 4)), x1);
     }
 }
 // Row-K fragment (as lfrag_rowk8) read straight from a fragment image in global memory.
@@ -592,10 +610,7 @@ __device__ __forceinline__ typename Frag<OT>::type gfrag_img(const OT* m, int ro
 template <class OT, bool NT = false>
 __device__ __forceinline__ void store_tile(OT* base, const f32x4& d) {
     float t[4] = {d[0], d[1], d[2], d[3]};
-    if (NT)
-        st4_nt(base + lane_id() * 4, t);
-    else
-        st4(base + lane_id() * 4, t);
+    st4_out<NT>(base + lane_id() * 4, t);
 }
 template <class OT>
 __device__ __forceinline__ f32x4 load_tile(const OT* base) {

@@ -22,6 +22,8 @@
 // query factors, T over the key factors once each is dead) so that two
 // workgroups fit on one compute unit. With gates passed as logits (ACT) the gates are
 // activated in phase 1, as they are converted to fp32; nothing else changes.
+#include <type_traits>
+
 #include "gdr2_intra_common.hpp"
 #include "gdr2_kernels.hpp"
 
@@ -174,7 +176,7 @@ __device__ __forceinline__ void upper_ri(int u, int& R, int& I) {
     I = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
 }
 
-template <class OT, int DK, int DV, bool TRAIN, bool ACT>
+template <class OT, int DK, int DV, bool TRAIN, bool ACT, bool NT>
 __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
     using LS = FwdLds<OT, DK, DV>;
     using FT = typename Frag<OT>::type;
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
                 cvt_rows16<OT>(rk[ai], hq, nvalid, kv);
                 cvt_rows16<OT>(rb[ai], hq, nvalid, bv);
                 if (ACT) activate_rows<OT, GATE_B>(bv, nvalid, a.g_scale, a.b_scale);
-                scaled_factors_from<OT, DK, true>(qv, kv, bv, ch0, rep, sXA, sXM, sY, qg_out, &rx);
+                scaled_factors_from<OT, DK, true, NT>(qv, kv, bv, ch0, rep, sXA, sXM, sY, qg_out, &rx);
             }
         }
 #pragma unroll
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
         const float sc = lds_load<float>(sF + ((F_ECE + (32 * tb + 8 * lq) / 16) * DK + 16 * kt + li) * 4);
 #pragma unroll
         for (int e = 0; e < 8; ++e) fr[e] = to_ot<OT>(to_f(fr[e]) * sc);
-        store_frag_img<OT, CH>(kd_out, 16 * kt, 32 * tb, fr);
+        store_frag_img<OT, CH, NT>(kd_out, 16 * kt, 32 * tb, fr);
     }
 
     // ---- phase 2a: M = lower(Qg Khat^T), computed as M^T tiles, out to global
@@ -306,13 +308,13 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
         float v[4];  // lane holds M[16R + li][16I + 4lq + i]
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = (R == I && 4 * lq + i > li) ? 0.f : acc[i];
-        st4_nt(m_out + fimg<OT, CH>(16 * R + li, 16 * I + 4 * lq), v);
+        st4_out<NT>(m_out + fimg<OT, CH>(16 * R + li, 16 * I + 4 * lq), v);
     }
     for (int u = wv; u < 6; u += 4) {
         int R, I;
         upper_ri(u, R, I);
         const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        st4_nt(m_out + fimg<OT, CH>(16 * R + li, 16 * I + 4 * lq), z);
+        st4_out<NT>(m_out + fimg<OT, CH>(16 * R + li, 16 * I + 4 * lq), z);
     }
     sync_lds();  // XM is dead from here on; its slot becomes A
 
@@ -388,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) mma(acc, aT[kb], lfrag_colk<OT, OT>(vX, 16 * j, 32 * kb));
-            store_tile<OT, true>(u_out + (j * 4 + tt) * 256, acc);
+            store_tile<OT, NT>(u_out + (j * 4 + tt) * 256, acc);
         }
 #pragma unroll
         for (int at = 0; at < DK / 16; ++at) {
@@ -396,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) mma(acc, lfrag_colk<OT, OT>(vXA, 16 * at, 32 * kb), aT[kb]);  // XA holds K_b
             float v[4] = {acc[0], acc[1], acc[2], acc[3]};  // Wm[16tt + li][16at + 4lq + i]
-            st4_nt(wm_out + fimg<OT, DK>(16 * tt + li, 16 * at + 4 * lq), v);
+            st4_out<NT>(wm_out + fimg<OT, DK>(16 * tt + li, 16 * at + 4 * lq), v);
         }
     }
     if (TRAIN) {  // T for the backward chain
@@ -405,7 +407,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
             const int r = idx / 16, c4 = 4 * (idx % 16);
             float v[4];
             lds_get4<float>(sT + swz<float, CH>(r, c4) * 4, v);
-            st4_nt(t_out + swz<OT, CH>(r, c4), v);
+            st4_out<NT>(t_out + swz<OT, CH>(r, c4), v);
         }
     }
 }
@@ -422,8 +424,12 @@ size_t fwd_intra_lds_bytes(int DK, int DV, int esz) {
 template <class OT, int DK, int DV>
 static hipError_t launch_fwd_t(const Args& a, bool train, hipStream_t stream) {
     const size_t lds = FwdLds<OT, DK, DV>::BYTES;
-    auto intra = a.act ? (train ? k_fwd_intra<OT, DK, DV, true, true> : k_fwd_intra<OT, DK, DV, false, true>)
-                       : (train ? k_fwd_intra<OT, DK, DV, true, false> : k_fwd_intra<OT, DK, DV, false, false>);
+    auto pick = [&](auto nt) {
+        constexpr bool NT = decltype(nt)::value;
+        return a.act ? (train ? k_fwd_intra<OT, DK, DV, true, true, NT> : k_fwd_intra<OT, DK, DV, false, true, NT>)
+                     : (train ? k_fwd_intra<OT, DK, DV, true, false, NT> : k_fwd_intra<OT, DK, DV, false, false, NT>);
+    };
+    auto intra = a.nt_out ? pick(std::true_type{}) : pick(std::false_type{});
     hipError_t e = hipFuncSetAttribute((const void*)intra, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     // stage events: 0 at the start of the intra-chunk kernel, 1 at its end, 2 at the end of the chain

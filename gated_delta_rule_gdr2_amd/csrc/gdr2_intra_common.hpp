@@ -313,7 +313,7 @@ __device__ __forceinline__ void row_exps(lds_char* sF, int ch0, const float (&f)
 // rep, see DecayRep) for channel tile rows of this lane, into swizzled LDS tiles [CH][DK];
 // with OUTS also Qg = q*exp(gam) [CH][DK] as a fragment image in global memory
 // (exp(gam) = E1 * exp(gam_R0), the row-uniform factor taken from rx).
-template <class OT, int DK, bool OUTS>
+template <class OT, int DK, bool OUTS, bool NT = false>
 __device__ __forceinline__ void scaled_factors(const float (&qv)[4][4], const float (&kv)[4][4],
                                                const float (&bv)[4][4], int ch0, const float (&e1v)[4][4],
                                                const float (&e2v)[4][4], lds_char* sXA, lds_char* sXM, lds_char* sY,
@@ -335,18 +335,18 @@ __device__ __forceinline__ void scaled_factors(const float (&qv)[4][4], const fl
         lds_put4<OT>(sXA + o, xa);
         lds_put4<OT>(sXM + o, xm);
         lds_put4<OT>(sY + o, y);
-        if constexpr (OUTS) st4_nt(qg_out + fimg<OT, DK>(r, ch0), qg);
+        if constexpr (OUTS) st4_out<NT>(qg_out + fimg<OT, DK>(r, ch0), qg);
     }
 }
 // ... with E1, E2 formed here from the lane's log-decays
-template <class OT, int DK, bool OUTS>
+template <class OT, int DK, bool OUTS, bool NT = false>
 __device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], const float (&kv)[4][4],
                                                     const float (&bv)[4][4], int ch0, const float (&rep)[4][4],
                                                     lds_char* sXA, lds_char* sXM, lds_char* sY, OT* qg_out,
                                                     const RowExp* rx) {
     float e1[4][4], e2[4][4];
     block_factors<OT>(rep, e1, e2);
-    scaled_factors<OT, DK, OUTS>(qv, kv, bv, ch0, e1, e2, sXA, sXM, sY, qg_out, rx);
+    scaled_factors<OT, DK, OUTS, NT>(qv, kv, bv, ch0, e1, e2, sXA, sXM, sY, qg_out, rx);
 }
 
 // X = w * v into a swizzled LDS tile [CH][DV] at columns ch0 .. ch0 + 3
@@ -393,8 +393,8 @@ __device__ __forceinline__ void dma_rows(const OT* base, size_t rs, int nvalid, 
 // Rows 0 .. nvalid - 1 of a swizzled LDS tile [CH][RL] out to a row-major tensor (row
 // stride rs elements), 16 bytes per lane with consecutive lanes on consecutive chunks
 // of a row, so every request is a whole cache line (all threads of the workgroup);
-// non-temporal stores (see st4_nt).
-template <class OT, int RL, int NTHR>
+// NT: non-temporal stores (see st4_nt).
+template <class OT, int RL, int NTHR, bool NT>
 __device__ __forceinline__ void store_rows_tiles(const lds_char* tile, OT* dst, size_t rs, int nvalid) {
     constexpr int EPC = 16 / (int)sizeof(OT);
     constexpr int NCH = RL / EPC;
@@ -403,7 +403,7 @@ __device__ __forceinline__ void store_rows_tiles(const lds_char* tile, OT* dst, 
         const int u = (int)threadIdx.x + NTHR * i, row = u / NCH, pos = u % NCH;
         if ((CH * NCH % NTHR == 0 || u < CH * NCH) && row < nvalid) {
             const f32x4 x = lds_load<f32x4>(tile + u * 16);
-            __builtin_nontemporal_store(x, (f32x4*)(dst + (size_t)row * rs + (pos ^ swz_f<OT, RL>(row)) * EPC));
+            store_out<NT>((f32x4*)(dst + (size_t)row * rs + (pos ^ swz_f<OT, RL>(row)) * EPC), x);
         }
     }
 }

@@ -24,6 +24,11 @@ struct Args {
     // writes the gradients with respect to the logits into dg, db, dw
     int act;
     float g_scale, b_scale;
+    // 1: results that a later kernel reads (the chains' per-chunk operands, the backward
+    // chain's outputs, the gradients, the decode state) go out with non-temporal stores; the
+    // library sets it for problems whose data is large next to the 256 MB Infinity Cache, and
+    // the launchers pick the kernel instantiation that matches
+    int nt_out;
     char* ws;           // workspace base
     Layout L;
     int B, T, H, NT;

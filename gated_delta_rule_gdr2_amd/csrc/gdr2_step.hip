@@ -29,7 +29,7 @@ __device__ __forceinline__ f32x4 xor_sum_rows(f32x4 x) {  // sum over lanes l ^ 
     return x;
 }
 
-template <class OT, int DK, int DV, bool ACT>
+template <class OT, int DK, int DV, bool ACT, bool NT>
 __global__ __launch_bounds__(128) void k_step(Args a) {
     constexpr int NI = DK / 8;  // state rows per lane
     __shared__ float sk[2][4][DK];             // per token: k, b*k, q, exp(g)
@@ -108,20 +108,28 @@ __global__ __launch_bounds__(128) void k_step(Args a) {
             st4((OT*)a.o + (((size_t)bidx * a.T + t) * a.H + h) * DV + col, ov);
         }
     }
-    // the state goes back with non-temporal stores: it is not read again within the call,
-    // and on this path they stream to HBM faster (a 512 MB state updated in place: 0.177
-    // against 0.217 ms per call; non-temporal loads, by contrast, are slower)
+    // a large state goes back with non-temporal stores: it is not read again within the call,
+    // and they stream to HBM faster (a 512 MB state updated in place: 0.177 against 0.217 ms
+    // per call; non-temporal loads, by contrast, are slower); a state the Infinity Cache can
+    // hold stays cached for the next call
 #pragma unroll
-    for (int i = 0; i < NI; ++i) __builtin_nontemporal_store(S[i], (f32x4*)(hs + (size_t)(rg + 8 * i) * DV));
+    for (int i = 0; i < NI; ++i) store_out<NT>((f32x4*)(hs + (size_t)(rg + 8 * i) * DV), S[i]);
 }
 
 template <class OT, int DK, int DV>
 static hipError_t launch_step_t(const Args& a, hipStream_t stream) {
     const dim3 grid((unsigned)(a.B * a.H * (DV / STEP_COLS)));
-    if (a.act)
-        hipLaunchKernelGGL((k_step<OT, DK, DV, true>), grid, dim3(128), 0, stream, a);
-    else
-        hipLaunchKernelGGL((k_step<OT, DK, DV, false>), grid, dim3(128), 0, stream, a);
+    if (a.nt_out) {
+        if (a.act)
+            hipLaunchKernelGGL((k_step<OT, DK, DV, true, true>), grid, dim3(128), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_step<OT, DK, DV, false, true>), grid, dim3(128), 0, stream, a);
+    } else {
+        if (a.act)
+            hipLaunchKernelGGL((k_step<OT, DK, DV, true, false>), grid, dim3(128), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_step<OT, DK, DV, false, false>), grid, dim3(128), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
