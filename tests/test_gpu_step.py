@@ -77,3 +77,33 @@ def test_step_continues_across_calls_and_matches_the_chunkwise_forward():
     assert torch.equal(torch.cat([o1, o2], 1), o_all) and torch.equal(s_part, s_all)
     assert err(np64(o_all), np64(oc), "fro") <= 2e-2
     assert err(np64(s_all), np64(hc), "fro") <= 2e-2
+
+
+def test_step_large_state_streaming_stores():
+    """A state of 128 MiB or more (here 512 sequences x 16 heads, d = 128: 512 MiB) takes the
+    instantiation that writes it back with non-temporal stores. Its o and state must match the
+    oracle on sampled (sequence, head) pairs, the last included, and equal bit for bit what the
+    plain-store instantiation gives for the same sequences in a small batch."""
+    B, H, D = 512, 16, 128
+    wl = small(DK=D, DV=D, T=1, dtype="bf16", B=B, H=H, backward=False, h0_std=0.0)
+    inp = make_inputs(wl)
+    names = ["q", "k", "v", "g", "b", "w"]
+    x = {n: inp[n].cuda() for n in names}
+    gen = torch.Generator(device="cuda").manual_seed(23)
+    state = torch.randn(B, H, D, D, device="cuda", generator=gen) * 0.05
+    rows = [0, 137, B - 1]
+    start = state[rows].clone()
+    o = g2.gdr2_step(*(x[n] for n in names), state)
+    # the same sequences as a 3-sequence batch (3 MiB of state: plain stores)
+    small_state = start.clone()
+    o_small = g2.gdr2_step(*(x[n][rows].contiguous() for n in names), small_state)
+    torch.cuda.synchronize()
+    assert torch.equal(o[rows], o_small) and torch.equal(state[rows], small_state)
+    for b, h in ((0, 0), (137, 5), (B - 1, H - 1)):
+        sl = lambda t: np64(t[b:b + 1, :, h:h + 1])
+        s0 = np64(start[rows.index(b), h])[None, None]
+        ro, rh = oracle.fwd(*(sl(inp[n]) for n in names), s0)
+        eo = err(np64(o[b:b + 1, :, h:h + 1]), ro, "fro")
+        eh = err(np64(state[b, h])[None, None], rh, "fro")
+        print("b %d h %d: o fro err %.3e, state fro err %.3e" % (b, h, eo, eh))
+        assert eo <= 2e-2 and eh <= 2e-2
