@@ -240,6 +240,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
 #pragma unroll
         for (int ai = 0; ai < NA; ++ai) {
             if (wv + 4 * ai >= NGK) break;
+            RT qgp[4];  // Q_g of this lane's W channels, rows 16 t + li, stored once both quarters are in
 #pragma unroll
             for (int hq = 0; hq < W / 4; ++hq) {
                 const int ch0 = GC * (wv + 4 * ai) + W * lq + 4 * hq;
@@ -258,8 +259,18 @@ __global__ __launch_bounds__(256, 2) void k_fwd_intra(Args a) {
                 cvt_rows16<OT>(rk[ai], hq, nvalid, kv);
                 cvt_rows16<OT>(rb[ai], hq, nvalid, bv);
                 if (ACT) activate_rows<OT, GATE_B>(bv, nvalid, a.g_scale, a.b_scale);
-                scaled_factors_from<OT, DK, true, NT>(qv, kv, bv, ch0, rep, sXA, sXM, sY, qg_out, &rx);
+                float qg[4][4];
+                scaled_factors_from<OT, DK, true>(qv, kv, bv, ch0, rep, sXA, sXM, sY, qg, &rx);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) qgp[t][4 * hq + i] = to_ot<OT>(qg[t][i]);
             }
+            // whole 16-byte pieces: with non-temporal stores, two 8-byte halves written apart
+            // would each go to memory as a partial line
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                store_out<NT>((RT*)(qg_out + fimg<OT, DK>(16 * t + li, GC * (wv + 4 * ai) + W * lq)), qgp[t]);
         }
 #pragma unroll
         for (int ji = 0; ji < NJ; ++ji) {

@@ -311,42 +311,41 @@ __device__ __forceinline__ void row_exps(lds_char* sF, int ch0, const float (&f)
 
 // XA = b*k*E1, XM = q*E1, Y = k*E2 (E1, E2 from the lane's log-decays in their stored form
 // rep, see DecayRep) for channel tile rows of this lane, into swizzled LDS tiles [CH][DK];
-// with OUTS also Qg = q*exp(gam) [CH][DK] as a fragment image in global memory
-// (exp(gam) = E1 * exp(gam_R0), the row-uniform factor taken from rx).
-template <class OT, int DK, bool OUTS, bool NT = false>
+// with OUTS also Qg = q*exp(gam) of the same positions into qgv (exp(gam) = E1 * exp(gam_R0),
+// the row-uniform factor taken from rx).
+template <class OT, int DK, bool OUTS>
 __device__ __forceinline__ void scaled_factors(const float (&qv)[4][4], const float (&kv)[4][4],
                                                const float (&bv)[4][4], int ch0, const float (&e1v)[4][4],
                                                const float (&e2v)[4][4], lds_char* sXA, lds_char* sXM, lds_char* sY,
-                                               OT* qg_out, const RowExp* rx) {
+                                               float (*qgv)[4], const RowExp* rx) {
     const int li = lane_id() & 15;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int r = 16 * t + li;
-        float xa[4], xm[4], y[4], qg[4];
+        float xa[4], xm[4], y[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float e1 = e1v[t][i], e2 = e2v[t][i];
             xa[i] = bv[t][i] * kv[t][i] * e1;
             xm[i] = qv[t][i] * e1;
             y[i] = kv[t][i] * e2;
-            if constexpr (OUTS) qg[i] = xm[i] * rx_er0(*rx, t, i);
+            if constexpr (OUTS) qgv[t][i] = xm[i] * rx_er0(*rx, t, i);
         }
         const int o = swz<OT, DK>(r, ch0) * (int)sizeof(OT);
         lds_put4<OT>(sXA + o, xa);
         lds_put4<OT>(sXM + o, xm);
         lds_put4<OT>(sY + o, y);
-        if constexpr (OUTS) st4_out<NT>(qg_out + fimg<OT, DK>(r, ch0), qg);
     }
 }
 // ... with E1, E2 formed here from the lane's log-decays
-template <class OT, int DK, bool OUTS, bool NT = false>
+template <class OT, int DK, bool OUTS>
 __device__ __forceinline__ void scaled_factors_from(const float (&qv)[4][4], const float (&kv)[4][4],
                                                     const float (&bv)[4][4], int ch0, const float (&rep)[4][4],
-                                                    lds_char* sXA, lds_char* sXM, lds_char* sY, OT* qg_out,
+                                                    lds_char* sXA, lds_char* sXM, lds_char* sY, float (*qgv)[4],
                                                     const RowExp* rx) {
     float e1[4][4], e2[4][4];
     block_factors<OT>(rep, e1, e2);
-    scaled_factors<OT, DK, OUTS, NT>(qv, kv, bv, ch0, e1, e2, sXA, sXM, sY, qg_out, rx);
+    scaled_factors<OT, DK, OUTS>(qv, kv, bv, ch0, e1, e2, sXA, sXM, sY, qgv, rx);
 }
 
 // X = w * v into a swizzled LDS tile [CH][DV] at columns ch0 .. ch0 + 3
