@@ -204,7 +204,7 @@ __device__ __forceinline__ typename Frag<OT>::type get_k8(const lds_char* frag) 
 
 constexpr int LDS_LIMIT = 160 * 1024;
 
-constexpr int PFD = 4;  // L2 prefetch distance in chunk steps
+constexpr int PFD = 2;  // L2 prefetch distance in chunk steps
 
 // L2 prefetch of one chunk's operands: the lines of a list of regions are numbered
 // 0 .. LINES - 1 in order; workgroup j of NJ, producer pi touches lines
