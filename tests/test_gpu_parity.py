@@ -211,6 +211,22 @@ def test_recompute_backward_full_size():
             keys=["dq", "dk", "dv", "dg", "db", "dw"])
 
 
+def test_fp32_at_a_streaming_store_size():
+    """fp32 at d = 64 with a training workspace past the library's 128 MiB threshold (B2 H16
+    T2048 with h0: 163 MiB), so every kernel runs its non-temporal-store instantiation, which
+    the small fp32 cases never reach: sampled sequences, the last included, against the
+    oracle at the fp32 tolerance."""
+    wl = small(name="f32_stream", DK=64, DV=64, T=2048, dtype="f32", B=2, H=16, backward=True, seed=91,
+               h0_std=0.1)
+    assert g2.gdr2_fwd_workspace_bytes(wl.B, wl.T, wl.H, wl.DK, wl.DV, dtype=g2.DTYPE_F32,
+                                       save_for_bwd=True) >= 128 << 20
+    inp = make_inputs(wl)
+    gpu = run_gpu(inp, True)
+    sel = sample_sequences(wl)
+    ref = run_oracle(inp, True, sel=sel)
+    compare(gpu, ref, wl.dtype, True, sel=sel, has_h0=True)
+
+
 def test_state_size_matches_the_pages():
     """262,144 state floats per layer for H = 16, d_k = d_v = 128 (LIT-802 takeaway 3)."""
     wl = WORKLOADS["fwd_bf16_b1h16t2048d128_h0"]
