@@ -162,9 +162,9 @@ def workspace(B, T, H, dk, dv, dtype, train, device="cuda", segments=None):
             gdr2_fwd_workspace_bytes(B, T, H, dk, dv, 64, dt, False)
     else:
         n = gdr2_seg_workspace_bytes(B, T, H, dk, dv, 64, segments, dt, train)
-    if n == 0:
+    if n == 0 and B * T * H > 0:
         raise ValueError("unsupported shape/dtype for gdr2: B=%d T=%d H=%d dk=%d dv=%d" % (B, T, H, dk, dv))
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)  # empty for a call without tokens
 
 
 def gdr2_fwd(q, k, v, g, b, w, h0=None, *, chunk=64, save_for_bwd=False, ws=None, o=None,

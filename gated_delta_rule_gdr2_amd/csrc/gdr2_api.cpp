@@ -21,13 +21,26 @@ int esize(int dtype) { return dtype == GDR2_DTYPE_BF16 ? 2 : 4; }
 bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_shape(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
-    if (B < 1 || T < 1 || H < 1) return GDR2_ERR_SHAPE;
+    if (B < 0 || T < 0 || H < 0) return GDR2_ERR_SHAPE;
     if (!supported(dk, dv, chunk, dtype)) return GDR2_ERR_UNSUPPORTED;
     // element counts must fit comfortably in 64-bit offsets and the grid in 32 bits
     const long long NT = (T + 63) / 64;
     const long long nc = (long long)B * H * NT;
     if (nc > 0x7fffffffLL || (long long)B * T * H > (1LL << 40)) return GDR2_ERR_SHAPE;
     return GDR2_OK;
+}
+
+// No tokens (B, T or H zero): the token tensors are empty and their pointers may be null;
+// the calls only pass the state through (see pass_state).
+bool no_tokens(int B, int T, int H) { return (long long)B * T * H == 0; }
+
+// The result of a call without tokens: the end state of a recurrence over no tokens is its
+// start state (h_T = h0, and zero without h0), and so is the gradient that reaches the start
+// (dh0 = dht, and zero without dht). dst (B * H * dk * dv floats) may be null: nothing to do.
+int pass_state(float* dst, const float* src, int B, int H, int dk, int dv, void* stream) {
+    const long long n = (long long)B * H * dk * dv;
+    if (!dst || n == 0) return GDR2_OK;
+    return gdr2::launch_state_pass(dst, src, n, (hipStream_t)stream) == hipSuccess ? GDR2_OK : GDR2_ERR_HIP;
 }
 
 // Segments of the state chains: `segments` requested (>= 1) -> chunks per segment and
@@ -96,7 +109,7 @@ extern "C" {
 
 size_t gdr2_seg_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int segments, int dtype,
                                 int save_for_bwd) {
-    if (check_shape(B, T, H, dk, dv, chunk, dtype) != GDR2_OK || segments < 1) return 0;
+    if (check_shape(B, T, H, dk, dv, chunk, dtype) != GDR2_OK || segments < 1 || no_tokens(B, T, H)) return 0;
     gdr2::Layout L = layout_for(B, T, H, dk, dv, dtype, segments, save_for_bwd != 0);
     return save_for_bwd ? L.train_bytes : L.fwd_infer_bytes;
 }
@@ -120,11 +133,11 @@ namespace {
 int fwd_check(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
               const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, int chunk, int dtype,
               int save_for_bwd, int act, float g_scale, float b_scale, int& segments, size_t& need) {
-    if (!q || !k || !v || !g || !b || !w || !o) return GDR2_ERR_NULL;
-    if (act && !scales_ok(g_scale, b_scale)) return GDR2_ERR_VALUE;
-    if (segments < 0) return GDR2_ERR_VALUE;  // 0: the automatic count
     int st = check_shape(B, T, H, dk, dv, chunk, dtype);
     if (st != GDR2_OK) return st;
+    if (!no_tokens(B, T, H) && (!q || !k || !v || !g || !b || !w || !o)) return GDR2_ERR_NULL;
+    if (act && !scales_ok(g_scale, b_scale)) return GDR2_ERR_VALUE;
+    if (segments < 0) return GDR2_ERR_VALUE;  // 0: the automatic count
     if (segments == 0) segments = auto_segments(B, T, H, dv);
     const void* ptrs[] = {q, k, v, g, b, w, h0, o, ht};
     for (const void* p : ptrs)
@@ -142,6 +155,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* g, const v
                        b_scale, segments, need);
     if (st != GDR2_OK) return st;
     if (workspace && !aligned(workspace)) return GDR2_ERR_ALIGN;
+    if (no_tokens(B, T, H)) return pass_state(ht, h0, B, H, dk, dv, stream);
     if (!workspace || workspace_bytes < need) return GDR2_ERR_WORKSPACE;
 
     gdr2::Args a = {};
@@ -159,16 +173,18 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* g, const v
              void* db, void* dw, float* dh0, int B, int T, int H, int dk, int dv, int chunk, int dtype,
              int fwd_saved, void* workspace, size_t workspace_bytes, void* stream,
              void* const* stage_events, int act, float g_scale, float b_scale, int segments) {
-    if (!q || !k || !v || !g || !b || !w || !dout || !dq || !dk_ || !dv_ || !dg || !db || !dw)
+    int st = check_shape(B, T, H, dk, dv, chunk, dtype);
+    if (st != GDR2_OK) return st;
+    if (!no_tokens(B, T, H) &&
+        (!q || !k || !v || !g || !b || !w || !dout || !dq || !dk_ || !dv_ || !dg || !db || !dw))
         return GDR2_ERR_NULL;
     if (act && !scales_ok(g_scale, b_scale)) return GDR2_ERR_VALUE;
     if (segments < 0) return GDR2_ERR_VALUE;  // 0: the automatic count
-    int st = check_shape(B, T, H, dk, dv, chunk, dtype);
-    if (st != GDR2_OK) return st;
     if (segments == 0) segments = auto_segments(B, T, H, dv);
     const void* ptrs[] = {q, k, v, g, b, w, h0, dout, dht, dq, dk_, dv_, dg, db, dw, dh0, workspace};
     for (const void* p : ptrs)
         if (p && !aligned(p)) return GDR2_ERR_ALIGN;
+    if (no_tokens(B, T, H)) return pass_state(dh0, dht, B, H, dk, dv, stream);
     const size_t need = gdr2_seg_workspace_bytes(B, T, H, dk, dv, chunk, segments, dtype, 1);
     if (!workspace || workspace_bytes < need) return GDR2_ERR_WORKSPACE;
 
@@ -196,13 +212,15 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* g, const v
 int step_impl(const void* q, const void* k, const void* v, const void* g, const void* b, const void* w,
               float* state, void* o, int B, int T, int H, int dk, int dv, int dtype, void* stream, int act,
               float g_scale, float b_scale) {
-    if (!q || !k || !v || !g || !b || !w || !state || !o) return GDR2_ERR_NULL;
-    if (act && !scales_ok(g_scale, b_scale)) return GDR2_ERR_VALUE;
     int st = check_shape(B, T, H, dk, dv, 64, dtype);
     if (st != GDR2_OK) return st;
+    const bool none = no_tokens(B, T, H);
+    if (!none && (!q || !k || !v || !g || !b || !w || !state || !o)) return GDR2_ERR_NULL;
+    if (act && !scales_ok(g_scale, b_scale)) return GDR2_ERR_VALUE;
     const void* ptrs[] = {q, k, v, g, b, w, state, o};
     for (const void* p : ptrs)
-        if (!aligned(p)) return GDR2_ERR_ALIGN;
+        if (p && !aligned(p)) return GDR2_ERR_ALIGN;
+    if (none) return GDR2_OK;  // no tokens: the state stays as it is
     gdr2::Args a = {};
     a.q = q; a.k = k; a.v = v; a.g = g; a.b = b; a.w = w;
     a.o = o; a.state = state;
@@ -306,7 +324,7 @@ const char* gdr2_strerror(int status) {
     switch (status) {
         case GDR2_OK: return "ok";
         case GDR2_ERR_NULL: return "a required pointer is NULL";
-        case GDR2_ERR_SHAPE: return "invalid shape (B, T and H must be >= 1; sizes must fit)";
+        case GDR2_ERR_SHAPE: return "invalid shape (B, T and H must be >= 0; sizes must fit)";
         case GDR2_ERR_UNSUPPORTED: return "unsupported dk/dv/chunk/dtype combination";
         case GDR2_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case GDR2_ERR_WORKSPACE: return "workspace is NULL or too small";

@@ -55,6 +55,9 @@ hipError_t launch_bwd_chain_t(const Args& a, hipStream_t stream, hipEvent_t star
 hipError_t launch_fwd(const Args& a, bool bf16, bool train, hipStream_t stream);
 hipError_t launch_bwd(const Args& a, bool bf16, hipStream_t stream);
 hipError_t launch_step(const Args& a, bool bf16, hipStream_t stream);
+// dst[0 .. n) = src[0 .. n), or zeros when src is null (n a multiple of 4, both 16-byte
+// aligned): the state a call without tokens passes through.
+hipError_t launch_state_pass(float* dst, const float* src, long long n, hipStream_t stream);
 size_t fwd_intra_lds_bytes(int DK, int DV, int esz);
 
 // The forward entry point's host validation (all but the workspace; *need = the workspace

@@ -53,8 +53,8 @@ extern "C" int gdr2_fwd_noalloc(const void* q, const void* k, const void* v, con
     const int st = gdr2::fwd_validate(q, k, v, g, b, w, h0, o, ht, B, T, H, dk, dv, chunk, dtype, &need);
     if (st != GDR2_OK) return st;
     if (need > GDR2_NOALLOC_SCRATCH_BYTES) return GDR2_ERR_SCRATCH;
-    void* ws = nullptr;
-    if (scratch_address(&ws) != hipSuccess) return GDR2_ERR_HIP;
+    void* ws = nullptr;  // a call without tokens needs no workspace
+    if (need > 0 && scratch_address(&ws) != hipSuccess) return GDR2_ERR_HIP;
     return gdr2::fwd_with_workspace(q, k, v, g, b, w, h0, o, ht, B, T, H, dk, dv, chunk, dtype, ws,
                                     GDR2_NOALLOC_SCRATCH_BYTES, stream);
 }

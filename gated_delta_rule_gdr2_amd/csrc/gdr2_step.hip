@@ -133,6 +133,22 @@ static hipError_t launch_step_t(const Args& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// A call without tokens: the state passes through unchanged (or starts at zero), a plain
+// vectorised copy -- a kernel rather than a memset or copy command, so that a caller may
+// capture the call in a HIP graph.
+__global__ __launch_bounds__(256) void k_state_pass(f32x4* dst, const f32x4* src, long long n4) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256)
+        dst[i] = src ? src[i] : z;
+}
+
+hipError_t launch_state_pass(float* dst, const float* src, long long n, hipStream_t stream) {
+    const long long n4 = n / 4, blocks = (n4 + 255) / 256;
+    const dim3 grid((unsigned)(blocks < 1024 ? blocks : 1024));
+    hipLaunchKernelGGL(k_state_pass, grid, dim3(256), 0, stream, (f32x4*)dst, (const f32x4*)src, n4);
+    return hipGetLastError();
+}
+
 hipError_t launch_step(const Args& a, bool bf16_, hipStream_t stream) {
     const int DK = a.L.DK, DV = a.L.DV;
     if (bf16_) {

@@ -23,8 +23,15 @@
  *   v, w, o, dout and dv, dw      : [B][T][H][dv]
  *   h0, ht, dht, dh0              : [B][H][dk][dv], always fp32
  * Supported: dtype BF16 with dk, dv in {64, 128}; dtype F32 with dk = dv = 64;
- * chunk = 64; any T >= 1 (a partial last chunk is padded with zero tokens,
+ * chunk = 64; any T >= 0 (a partial last chunk is padded with zero tokens,
  * which leave the recurrence unchanged).
+ *
+ * Calls without tokens (B, T or H zero): the token tensors are empty, their pointers
+ * may be NULL, and no workspace is needed (the size functions return 0, a NULL
+ * workspace is accepted). A recurrence over no tokens ends where it starts, so
+ * gdr2_fwd writes ht = h0 (zeros when h0 is NULL) and gdr2_bwd writes dh0 = dht
+ * (zeros when dht is NULL), when ht / dh0 are given and B * H > 0; gdr2_step leaves
+ * the state as it is. Nothing else is enqueued.
  *
  * Ownership: the caller owns every buffer, including the workspace. All device
  * pointers must stay valid until the stream has passed the enqueued work. The
@@ -57,7 +64,7 @@ enum gdr2_dtype { GDR2_DTYPE_F32 = 0, GDR2_DTYPE_BF16 = 1 };
 enum gdr2_status {
     GDR2_OK = 0,
     GDR2_ERR_NULL = -1,        /* a required pointer is NULL */
-    GDR2_ERR_SHAPE = -2,       /* B, T or H < 1, or sizes overflow */
+    GDR2_ERR_SHAPE = -2,       /* B, T or H negative, or sizes overflow */
     GDR2_ERR_UNSUPPORTED = -3, /* dk/dv/chunk/dtype combination not built */
     GDR2_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
     GDR2_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
@@ -68,7 +75,7 @@ enum gdr2_status {
 
 /* Bytes of workspace gdr2_fwd needs. save_for_bwd = 1 sizes it for a later
  * gdr2_bwd(..., fwd_saved = 1) on the same buffer. Returns 0 for unsupported
- * or invalid arguments. */
+ * or invalid arguments, and for calls without tokens, which need none. */
 size_t gdr2_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype,
                                 int save_for_bwd);
 

@@ -62,7 +62,12 @@ def test_workspace_sizes(lib):
     assert g2.gdr2_fwd_workspace_bytes(1, 64, 1, 96, 64, 64, BF, False) == 0
     assert g2.gdr2_fwd_workspace_bytes(1, 64, 1, 64, 64, 32, BF, False) == 0
     assert g2.gdr2_fwd_workspace_bytes(1, 64, 1, 128, 128, 64, g2.DTYPE_F32, False) == 0
+    assert g2.gdr2_fwd_workspace_bytes(-1, 64, 1, 64, 64, 64, BF, False) == 0
+    # no tokens -> no workspace
     assert g2.gdr2_fwd_workspace_bytes(0, 64, 1, 64, 64, 64, BF, False) == 0
+    assert g2.gdr2_fwd_workspace_bytes(1, 0, 1, 64, 64, 64, BF, True) == 0
+    assert g2.gdr2_bwd_workspace_bytes(1, 64, 0, 64, 64, 64, BF) == 0
+    assert g2.gdr2_seg_workspace_bytes(1, 0, 1, 64, 64, 64, 2, BF, 1) == 0
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
@@ -102,8 +107,9 @@ def test_bwd_rejects_null_required_pointers(lib):
 
 
 def test_shape_and_support_errors(lib):
-    assert fwd(lib, B=0) == ERR_SHAPE
-    assert fwd(lib, T=0) == ERR_SHAPE
+    assert fwd(lib, B=-1) == ERR_SHAPE
+    assert fwd(lib, T=-1) == ERR_SHAPE
+    assert bwd(lib, T=-64) == ERR_SHAPE
     assert fwd(lib, H=-1) == ERR_SHAPE
     assert fwd(lib, dk=96) == ERR_UNSUP
     assert fwd(lib, dv=32) == ERR_UNSUP
@@ -111,6 +117,26 @@ def test_shape_and_support_errors(lib):
     assert fwd(lib, dtype=7) == ERR_UNSUP
     assert fwd(lib, dk=128, dv=128, dtype=g2.DTYPE_F32) == ERR_UNSUP
     assert bwd(lib, dk=48) == ERR_UNSUP
+
+
+def test_calls_without_tokens(lib):
+    """B, T or H zero: the token tensors are empty (NULL pointers allowed) and no workspace is
+    needed. With no state to pass through (ht / dh0 NULL, or B * H = 0) the calls succeed
+    without any HIP call, so they run here; state pass-through is a GPU test."""
+    none6 = [0] * 6
+    assert fwd(lib, none6 + [0, 0, 0], T=0, ws=0, ws_bytes=0) == OK
+    assert fwd(lib, none6 + [FAKE, 0, 0], T=0, ws=0, ws_bytes=0, save=1) == OK
+    assert fwd(lib, none6 + [FAKE, 0, FAKE], B=0, ws=0, ws_bytes=0) == OK  # B * H = 0: no state
+    assert fwd(lib, none6 + [FAKE, 0, FAKE], H=0, ws=0, ws_bytes=0) == OK
+    assert bwd(lib, [0] * 16, T=0, ws=0, ws_bytes=0) == OK
+    assert bwd(lib, [0] * 15 + [FAKE], B=0, ws=0, ws_bytes=0, saved=0) == OK
+    assert step(lib, [0] * 8, T=0) == OK
+    assert step(lib, [0] * 6 + [FAKE, 0], B=0) == OK
+    # the other checks still apply
+    assert fwd(lib, none6 + [0, 0, 0], T=0, dk=96) == ERR_UNSUP
+    assert fwd(lib, none6 + [FAKE + 4, 0, 0], T=0) == ERR_ALIGN
+    assert bwd(lib, [0] * 16, T=0, dtype=g2.DTYPE_F32, dk=128, dv=128) == ERR_UNSUP
+    assert fwd_logits(lib, none6 + [0, 0, 0], gs=-1.0, T=0) == ERR_VALUE
 
 
 def test_alignment_errors(lib):
@@ -153,8 +179,8 @@ def test_step_rejects_bad_arguments(lib):
         assert step(lib, p) == ERR_NULL, i
         p[i] = FAKE + 4
         assert step(lib, p) == ERR_ALIGN, i
-    assert step(lib, B=0) == ERR_SHAPE
-    assert step(lib, T=0) == ERR_SHAPE
+    assert step(lib, B=-1) == ERR_SHAPE
+    assert step(lib, T=-1) == ERR_SHAPE
     assert step(lib, dk=96) == ERR_UNSUP
     assert step(lib, dk=128, dv=128, dtype=g2.DTYPE_F32) == ERR_UNSUP
 
@@ -200,7 +226,7 @@ def test_logit_entry_points_validate_like_the_plain_ones(lib):
     p = [FAKE] * 16
     p[14] = 0  # dzw
     assert bwd_logits(lib, p) == ERR_NULL
-    assert bwd_logits(lib, B=0) == ERR_SHAPE
+    assert bwd_logits(lib, B=-1) == ERR_SHAPE
     p = [FAKE] * 8
     p[6] = 0  # state
     assert step_logits(lib, p) == ERR_NULL
@@ -291,7 +317,9 @@ def test_noalloc_validates_like_the_forward_and_rejects_oversized_calls(lib):
         p = [FAKE] * 9
         p[idx if idx < 6 else 7] = 0
         assert noalloc(lib, p) == ERR_NULL
-    assert noalloc(lib, B=0) == ERR_SHAPE
+    assert noalloc(lib, B=-1) == ERR_SHAPE
+    # no tokens (B * H = 0, so no state either): nothing to do, no scratch looked up
+    assert noalloc(lib, [0] * 9, B=0) == OK
     assert noalloc(lib, dk=96) == ERR_UNSUP
     assert noalloc(lib, dtype=g2.DTYPE_F32, dk=128, dv=128) == ERR_UNSUP
     p = [FAKE] * 9
