@@ -35,6 +35,12 @@
 //                 phase 1 (b, and d g / d z_g, go back into the staged tiles), w where
 //                 it is read, and multiplies dg, db, dw by the activations' derivatives
 //                 before they are stored (gradients with respect to the logits).
+//                 NT (large workspaces): the gradients go out with non-temporal stores,
+//                 and the saved S, dS', Delta and dY -- read here for the last time --
+//                 come in with non-temporal loads, so that they do not displace the
+//                 inputs from the Infinity Cache (measured at the headline shape: the
+//                 backward itself unchanged, the next forward intra-chunk kernel over
+//                 the same inputs 0.091 -> 0.085 ms).
 #include "gdr2_intra_common.hpp"
 #include "gdr2_kernels.hpp"
 
@@ -69,11 +75,11 @@ struct Undump {
     static constexpr int NU = (DV / 16) * 4 * 64 / NTHR;
     static_assert((DV / 16) * 4 * 64 % NTHR == 0, "tile dump divides evenly over the threads");
 };
-template <class OT, int DV, int NTHR>
+template <class OT, int DV, int NTHR, bool NT>
 __device__ __forceinline__ void undump_load(const OT* src, typename Raw4<OT>::type (&raw)[Undump<OT, DV, NTHR>::NU]) {
 #pragma unroll
     for (int u = 0; u < Undump<OT, DV, NTHR>::NU; ++u)
-        raw[u] = *(const typename Raw4<OT>::type*)(src + (size_t)(threadIdx.x + NTHR * u) * 4);
+        raw[u] = load_in<NT>((const typename Raw4<OT>::type*)(src + (size_t)(threadIdx.x + NTHR * u) * 4));
 }
 template <class OT, int DV, int NTHR>
 __device__ __forceinline__ void undump_store(const typename Raw4<OT>::type (&raw)[Undump<OT, DV, NTHR>::NU],
@@ -187,8 +193,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     // first, so the wait below covers them alone and the later loads stay in flight
     // through phases 1 and 2. Each of these loads is one instruction (8 or 16 bytes).
     __builtin_amdgcn_sched_barrier(0);
-    undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_delta) + cid * L.delta, rdl);
-    undump_load<OT, DV, NTHR>((const OT*)(a.ws + L.o_dy) + cid * L.dy, rdy);
+    undump_load<OT, DV, NTHR, NT>((const OT*)(a.ws + L.o_delta) + cid * L.delta, rdl);
+    undump_load<OT, DV, NTHR, NT>((const OT*)(a.ws + L.o_dy) + cid * L.dy, rdy);
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
         const int pc = tid + NTHR * i, r = pc / NCV, rr = r < nvalid ? r : nvalid - 1;
@@ -200,8 +206,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         const int at = wv < DK / 16 ? wv : 0;
 #pragma unroll
         for (int kb = 0; kb < KV; ++kb) {
-            Sf[0][kb] = frag_fmaj<OT, DV>(Sg, at, kb);
-            dSf[0][kb] = frag_fmaj<OT, DV>(dSg, at, kb);
+            Sf[0][kb] = frag_fmaj<OT, DV, NT>(Sg, at, kb);
+            dSf[0][kb] = frag_fmaj<OT, DV, NT>(dSg, at, kb);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -340,8 +346,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
         if (!EARLY_S) {
 #pragma unroll
             for (int kb = 0; kb < KV; ++kb) {
-                Sf[ac][kb] = frag_fmaj<OT, DV>(Sg, at, kb);
-                dSf[ac][kb] = frag_fmaj<OT, DV>(dSg, at, kb);
+                Sf[ac][kb] = frag_fmaj<OT, DV, NT>(Sg, at, kb);
+                dSf[ac][kb] = frag_fmaj<OT, DV, NT>(dSg, at, kb);
             }
         }
         // lane (li, lq) element i: sum over v of S[16at + 4lq + i][v] dS'[16at + li][v], so the

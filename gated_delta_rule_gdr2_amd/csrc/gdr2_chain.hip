@@ -368,7 +368,10 @@ struct FwdPend {
     int c;                                 // chunk, -1 = nothing pending
 };
 
-template <class OT, int DK, int DV, bool TRAIN, bool OUT, int NW, int NC>
+// TRAIN: 0 inference; 1 training (the chunk start states S and Delta are saved for the
+// backward); 2 training with S and Delta written by non-temporal stores (large workspaces:
+// they are read only by the backward intra-chunk kernel, much later).
+template <class OT, int DK, int DV, int TRAIN, bool OUT, int NW, int NC>
 __device__ __forceinline__ void fwd_flush(const Args& a, int s, int j, FwdPend<OT, NW, NC>& pd) {
     if (pd.c < 0) return;
     constexpr int TPW = FwdPend<OT, NW, NC>::TPW;
@@ -379,10 +382,10 @@ __device__ __forceinline__ void fwd_flush(const Args& a, int s, int j, FwdPend<O
     for (int ch = 0; ch < NC; ++ch) {
         const int jt = NC * j + ch;  // 16-column tile of the value axis
         if (TRAIN) {
-            store_rows<OT, DV>((OT*)(a.ws + L.o_s) + cid * L.s, 32 * wv, jt, pd.st[ch]);
+            store_rows<OT, DV, TRAIN == 2>((OT*)(a.ws + L.o_s) + cid * L.s, 32 * wv, jt, pd.st[ch]);
             OT* dl = (OT*)(a.ws + L.o_delta) + cid * L.delta + jt * 4 * 256;
 #pragma unroll
-            for (int u = 0; u < TPW; ++u) store_tile<OT>(dl + (wv * TPW + u) * 256, pd.D[u][ch]);
+            for (int u = 0; u < TPW; ++u) store_tile<OT, TRAIN == 2>(dl + (wv * TPW + u) * 256, pd.D[u][ch]);
         }
         if (OUT) {
             const int bidx = s / a.H, h = s % a.H;
@@ -403,7 +406,7 @@ __device__ __forceinline__ void fwd_flush(const Args& a, int s, int j, FwdPend<O
 // step and, spread over its own work, the loads of the next step's operands (chunk ncid)
 // into nxt. Exchange slots: state fragment (key block kb, column tile ch) at kb * NC + ch,
 // Delta fragment (token block tb, column tile ch) at NW * NC + tb * NC + ch.
-template <class OT, int DK, int DV, bool TRAIN, bool OUT, int NW, int NC>
+template <class OT, int DK, int DV, int TRAIN, bool OUT, int NW, int NC>
 __device__ __forceinline__ void fwd_step(const Args& a, int s, int j, int c, const FwdOps<OT, DK, NC>& op,
                                          FwdOps<OT, DK, NC>& nxt, long long ncid, bool noU, f32x4 (&S0)[NC],
                                          f32x4 (&S1)[NC], lds_char* stage, lds_char* xs, FwdPend<OT, NW, NC>& pd) {
@@ -491,7 +494,7 @@ __device__ __forceinline__ void fwd_step(const Args& a, int s, int j, int c, con
     pd.c = c;
 }
 
-template <class OT, int DK, int DV, bool TRAIN, bool OUT, int NW, int NC>
+template <class OT, int DK, int DV, int TRAIN, bool OUT, int NW, int NC>
 __device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, const WalkSpec& w, lds_char* xs,
                                          lds_char* stage_base, lds_char* pfslot) {
     constexpr int NJ = DV / (16 * NC);  // workgroups per sequence (value slices)
@@ -594,7 +597,7 @@ __device__ __forceinline__ void fwd_walk(const Args& a, int s, int j, const Walk
     }
 }
 
-template <class OT, int DK, int DV, int NC, bool TRAIN>
+template <class OT, int DK, int DV, int NC, int TRAIN>
 __global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_fwd_chain(Args a) {
     constexpr int NW = DK / 32, NJ = DV / (16 * NC);
     __shared__ __align__(16) char xch[Xch<OT>::bytes(NW, NC)];
@@ -657,7 +660,7 @@ __global__ __launch_bounds__(64 * (DK / 32 + NP)) void k_fwd_chain_sum(Args a) {
     w.ld_end = trans ? DK : DV;
     w.col = 16 * (trans ? j - NJ : j);
     w.noU = trans;
-    fwd_walk<OT, DK, DV, false, false, NW, 1>(a, s, j, w, (lds_char*)xch, nullptr, (lds_char*)pfslot);
+    fwd_walk<OT, DK, DV, 0, false, NW, 1>(a, s, j, w, (lds_char*)xch, nullptr, (lds_char*)pfslot);
 }
 
 // ============================================================================ backward chain
@@ -1108,16 +1111,23 @@ hipError_t launch_fwd_chain_t(const Args& a, bool train, hipStream_t stream, hip
     int nc = 1;
     if ((e = chain_nc((long long)S * a.nseg * NJ1, nc)) != hipSuccess) return e;
     const dim3 grid(S * a.nseg * (NJ1 / nc));
+    // the non-temporal choice is a template parameter: behind a run-time branch the
+    // compiler merges the two kinds of store and drops the hint
+    const int mode = train ? (a.nt_out ? 2 : 1) : 0;
     if (nc == 2) {
-        if (train)
-            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 2, true>), grid, block, 0, stream, start, stop, 0, a);
+        if (mode == 2)
+            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 2, 2>), grid, block, 0, stream, start, stop, 0, a);
+        else if (mode == 1)
+            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 2, 1>), grid, block, 0, stream, start, stop, 0, a);
         else
-            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 2, false>), grid, block, 0, stream, start, stop, 0, a);
+            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 2, 0>), grid, block, 0, stream, start, stop, 0, a);
     } else {
-        if (train)
-            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 1, true>), grid, block, 0, stream, start, stop, 0, a);
+        if (mode == 2)
+            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 1, 2>), grid, block, 0, stream, start, stop, 0, a);
+        else if (mode == 1)
+            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 1, 1>), grid, block, 0, stream, start, stop, 0, a);
         else
-            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 1, false>), grid, block, 0, stream, start, stop, 0, a);
+            hipExtLaunchKernelGGL((k_fwd_chain<OT, DK, DV, 1, 0>), grid, block, 0, stream, start, stop, 0, a);
     }
     return hipGetLastError();
 }

@@ -214,6 +214,15 @@ __device__ __forceinline__ void store_out(T* p, const T& v) {
     else
         *p = v;
 }
+// Load with the non-temporal hint as a compile-time choice, for data that nothing reads
+// after this load (it then does not displace other data from the caches).
+template <bool NT, class T>
+__device__ __forceinline__ T load_in(const T* p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
 
 // ----------------------------------------------------------------------------- fragment loads
 // "rowk": lane (li, lq) reads X[row0 + li][k0 + kmap(lq, e)] -- contiguous along K
@@ -239,13 +248,14 @@ template <int DV>
 __device__ __forceinline__ size_t fmaj_off(int r, int c) {
     return ((size_t)((r >> 4) * (DV / 32) + (c >> 5)) * 64 + ((c >> 3) & 3) * 16 + (r & 15)) * 8 + (c & 7);
 }
-template <class OT, int DV>
+// (NT: a non-temporal load, for data read for the last time)
+template <class OT, int DV, bool NT = false>
 __device__ __forceinline__ typename Frag<OT>::type frag_fmaj(const OT* X, int at, int kb) {
     const OT* p = X + ((size_t)(at * (DV / 32) + kb) * 64 + lane_id()) * 8;
     if constexpr (sizeof(OT) == 2) {
-        return *(const bf16x8*)p;
+        return load_in<NT>((const bf16x8*)p);
     } else {
-        f32x4 x0 = *(const f32x4*)p, x1 = *(const f32x4*)(p + 4);
+        f32x4 x0 = load_in<NT>((const f32x4*)p), x1 = load_in<NT>((const f32x4*)(p + 4));
         return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 }
