@@ -215,7 +215,8 @@ int step_impl(const void* q, const void* k, const void* v, const void* g, const 
     int st = check_shape(B, T, H, dk, dv, 64, dtype);
     if (st != GDR2_OK) return st;
     const bool none = no_tokens(B, T, H);
-    if (!none && (!q || !k || !v || !g || !b || !w || !state || !o)) return GDR2_ERR_NULL;
+    if (!none && (!q || !k || !v || !g || !b || !w || !o)) return GDR2_ERR_NULL;
+    if ((long long)B * H > 0 && !state) return GDR2_ERR_NULL;  // the state is not a token tensor
     if (act && !scales_ok(g_scale, b_scale)) return GDR2_ERR_VALUE;
     const void* ptrs[] = {q, k, v, g, b, w, state, o};
     for (const void* p : ptrs)

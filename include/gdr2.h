@@ -31,7 +31,8 @@
  * workspace is accepted). A recurrence over no tokens ends where it starts, so
  * gdr2_fwd writes ht = h0 (zeros when h0 is NULL) and gdr2_bwd writes dh0 = dht
  * (zeros when dht is NULL), when ht / dh0 are given and B * H > 0; gdr2_step leaves
- * the state as it is. Nothing else is enqueued.
+ * the state as it is (the state pointer is still required when B * H > 0). Nothing
+ * else is enqueued.
  *
  * Ownership: the caller owns every buffer, including the workspace. All device
  * pointers must stay valid until the stream has passed the enqueued work. The

@@ -130,8 +130,9 @@ def test_calls_without_tokens(lib):
     assert fwd(lib, none6 + [FAKE, 0, FAKE], H=0, ws=0, ws_bytes=0) == OK
     assert bwd(lib, [0] * 16, T=0, ws=0, ws_bytes=0) == OK
     assert bwd(lib, [0] * 15 + [FAKE], B=0, ws=0, ws_bytes=0, saved=0) == OK
-    assert step(lib, [0] * 8, T=0) == OK
-    assert step(lib, [0] * 6 + [FAKE, 0], B=0) == OK
+    assert step(lib, [0] * 6 + [FAKE, 0], T=0) == OK
+    assert step(lib, [0] * 8, T=0) == ERR_NULL  # the state is required whenever B * H > 0
+    assert step(lib, [0] * 8, B=0) == OK
     # the other checks still apply
     assert fwd(lib, none6 + [0, 0, 0], T=0, dk=96) == ERR_UNSUP
     assert fwd(lib, none6 + [FAKE + 4, 0, 0], T=0) == ERR_ALIGN
