@@ -127,6 +127,46 @@ __device__ __forceinline__ void undump_tiles(const OT* src, lds_char* dst) {
 
 constexpr int BWD_NW = 8;  // waves per workgroup of the backward intra-chunk kernel
 
+// L2 warm-up for the next round. One workgroup per compute unit and chunk means that the
+// loads of a chunk (about 200 KB at d = 128) are the compute unit's only memory traffic for
+// the first quarter of the chunk's time and none is in flight afterwards. During this
+// chunk's phase 2, every lane reads one 4-byte word of up to NI cache lines of the rows the
+// chunk at blockIdx + a.l2_ahead will stage by DMA (g, q, k, b, dO: 80 KB at d = 128) --
+// the chunk the same XCD runs next -- so that they come from L2 when that workgroup starts
+// (the other 128 KB it reads would not fit in L2 beside them: measured slower). The words
+// are kept in registers and consumed by an empty asm statement at the end of the kernel.
+template <class OT, int DK, int DV, int NTHR>
+struct L2Warm {
+    static constexpr int LPRK = DK * (int)sizeof(OT) / 128, LPRV = DV * (int)sizeof(OT) / 128;  // lines per row
+    static constexpr int NL = 4 * CH * LPRK + CH * LPRV;
+    static constexpr int NI = (NL + NTHR - 1) / NTHR;
+};
+template <class OT, int DK, int DV, int NTHR>
+__device__ __forceinline__ void l2_warm_next(const Args& a, long long cid, uint32_t (&word)[L2Warm<OT, DK, DV, NTHR>::NI]) {
+    using W = L2Warm<OT, DK, DV, NTHR>;
+#pragma unroll
+    for (int i = 0; i < W::NI; ++i) word[i] = 0;
+    const long long cid2 = cid + a.l2_ahead;
+    if (a.l2_ahead <= 0 || cid2 >= a.NC) return;
+    const int s2 = (int)(cid2 / a.NT), c2 = (int)(cid2 % a.NT);
+    const int nv2 = min(CH, a.T - c2 * CH);
+    const size_t r0 = ((size_t)(s2 / a.H) * a.T + (size_t)c2 * CH) * a.H + s2 % a.H;  // token row of its row 0
+#pragma unroll
+    for (int i = 0; i < W::NI; ++i) {
+        const int v = threadIdx.x + NTHR * i;  // line v: tensor, row, line in the row
+        const char* p = nullptr;
+        if (v < 4 * CH * W::LPRK) {
+            const int t = v / (CH * W::LPRK), r = v % (CH * W::LPRK) / W::LPRK, ln = v % W::LPRK;
+            const void* base = t == 0 ? a.g : t == 1 ? a.q : t == 2 ? a.k : a.b;
+            if (r < nv2) p = (const char*)((const OT*)base + (r0 + (size_t)r * a.H) * DK) + ln * 128;
+        } else if (v < W::NL) {
+            const int u = v - 4 * CH * W::LPRK, r = u / W::LPRV, ln = u % W::LPRV;
+            if (r < nv2) p = (const char*)((const OT*)a.dout + (r0 + (size_t)r * a.H) * DV) + ln * 128;
+        }
+        if (p) word[i] = *(const uint32_t*)p;
+    }
+}
+
 template <class OT, int DK, int DV, bool ACT, bool NT>
 __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     using LS = BwdLds<OT, DK, DV>;
@@ -298,6 +338,10 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     if (slow)
         for (int e = tid; e < NBLK * DK; e += NTHR)
             lds_store<float>(sF + ((F_S + pair_id(e / DK, e / DK)) * DK + e % DK) * 4, 0.f);
+
+    uint32_t warm[L2Warm<OT, DK, DV, NTHR>::NI];
+    l2_warm_next<OT, DK, DV, NTHR>(a, cid, warm);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- phase 2: dA = -strict_lower(dY Delta^T), dM = lower(dO Delta^T)
     // The diagonal of M, q_r . k_r, does not depend on the decay; its gradient is
@@ -627,6 +671,8 @@ __global__ __launch_bounds__(64 * BWD_NW) void k_bwd_intra(Args a) {
     store_rows_tiles<OT, DK, NTHR, NT>(sK, (OT*)a.dk + rowk0 * DK, rsk, nvalid);
     store_rows_tiles<OT, DK, NTHR, NT>(sB, (OT*)a.db + rowk0 * DK, rsk, nvalid);
     store_rows_tiles<OT, DK, NTHR, NT>(sG, (OT*)a.dg + rowk0 * DK, rsk, nvalid);
+#pragma unroll
+    for (int i = 0; i < L2Warm<OT, DK, DV, NTHR>::NI; ++i) asm volatile("" ::"v"(warm[i]));  // the warm-up loads stay
 }
 
 size_t bwd_intra_lds_bytes(int DK, int DV, int esz) {
@@ -645,10 +691,18 @@ static hipError_t launch_bwd_t(const Args& a, hipStream_t stream) {
                           : (a.act ? k_bwd_intra<OT, DK, DV, true, false> : k_bwd_intra<OT, DK, DV, false, false>);
     hipError_t e = hipFuncSetAttribute((const void*)intra, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
+    // the next round of workgroups starts (compute units x workgroups per unit) chunks later
+    int dev = 0, cus = 0, per_cu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)intra, 64 * BWD_NW, lds)) != hipSuccess)
+        return e;
+    Args ai = a;
+    ai.l2_ahead = (long long)cus * (per_cu > 0 ? per_cu : 1);
     // stage events: 0 at the start of the chain, 1 at its end, 2 at the end of the intra-chunk kernel
     if ((e = launch_bwd_chain_t<OT, DK, DV>(a, stream, stage_event(a, 0), stage_event(a, 1))) != hipSuccess) return e;
     hipExtLaunchKernelGGL(intra, dim3((unsigned)a.NC), dim3(64 * BWD_NW), lds, stream, nullptr, stage_event(a, 2),
-                          0, a);
+                          0, ai);
     return hipGetLastError();
 }
 

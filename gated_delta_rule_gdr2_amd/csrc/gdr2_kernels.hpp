@@ -34,6 +34,11 @@ struct Args {
     int B, T, H, NT;
     int nseg, seg_len;  // state chains: segments per sequence and chunks per segment (nseg = 1: one walk)
     long long NC;       // B * H * NT chunks
+    // k_bwd_intra: the workgroups of one round are one per compute unit, so the chunk that
+    // runs next on this workgroup's XCD (workgroups go to the XCDs round-robin) is
+    // blockIdx + l2_ahead with l2_ahead = the compute unit count; its staged input rows are
+    // pulled into L2 during this chunk's work (0: no warm-up)
+    long long l2_ahead;
     hipEvent_t const* events;  // optional: per-stage timing events (see stage_event)
     int events_continue;       // 1: events[0] was recorded by the stages before (backward after a recompute)
 };
