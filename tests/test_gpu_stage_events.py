@@ -51,3 +51,33 @@ def test_stage_events_cover_the_stages(segments):
             assert torch.equal(gr[key], gr_re[key]), key
     finally:
         hip.destroy(evs)
+
+
+def test_stage_events_with_null_slots():
+    """Elements of the event array may be NULL: only the given boundaries carry events (how
+    bench.py times the dominant kernel alone). Here only the backward intra-chunk stage's two
+    boundaries (elements 1 and 2 of the backward's array) have events; the interval is
+    positive and no longer than the whole call timed outside, and the results are unchanged."""
+    wl = small(DK=128, DV=128, T=700, dtype="bf16", B=2, H=2, h0_std=0.05, seed=52)
+    x = {k: (None if v is None else v.cuda()) for k, v in make_inputs(wl).items()}
+    args = [x[n] for n in NAMES] + [x["h0"]]
+    hip = HipEvents()
+    evs = hip.create(4)
+    arr = (ctypes.c_void_p * 3)(None, evs[0], evs[1])
+    stream = torch.cuda.current_stream()
+    try:
+        o, ht, ws = g2.gdr2_fwd(*args, save_for_bwd=True, stream=stream)
+        ref = {k: v.clone() for k, v in g2.gdr2_bwd(*args, x["do"], ws=ws, fwd_saved=True, stream=stream).items()
+               if v is not None}
+        hip.record(evs[2], stream)
+        gr = g2.gdr2_bwd(*args, x["do"], ws=ws, fwd_saved=True, stream=stream,
+                         stage_events=ctypes.cast(arr, ctypes.c_void_p))
+        hip.record(evs[3], stream)
+        torch.cuda.synchronize()
+        intra, whole = hip.elapsed_ms(evs[0], evs[1]), hip.elapsed_ms(evs[2], evs[3])
+        print("intra stage %.4f ms of %.4f ms" % (intra, whole), flush=True)
+        assert 0 < intra <= whole
+        for key, v in ref.items():
+            assert torch.equal(gr[key], v), key
+    finally:
+        hip.destroy(evs)
