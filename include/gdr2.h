@@ -182,7 +182,8 @@ int gdr2_step_logits(const void* q, const void* k, const void* v, const void* zg
 
 /* stage_events (gdr2_fwd and gdr2_bwd, and their _logits and _seg variants): NULL, or
  * an array of hipEvent_t for per-stage timing on `stream`: element 0 marks the start of
- * the first stage and element i the end of the i-th. The events are attached to the
+ * the first stage and element i the end of the i-th (a NULL element: no event at that
+ * boundary). The events are attached to the
  * stages' kernel launches (start of the first kernel, end of the last), so timing puts no
  * extra commands between the kernels; a stage's interval therefore includes the launch
  * gap before its first kernel.
