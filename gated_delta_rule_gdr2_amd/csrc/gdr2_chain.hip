@@ -29,12 +29,14 @@
 // the operands of the chunk PFD steps ahead into L2. Backward: the operands are read
 // transposed (K = token), which the LDS transposing reads provide, so the producer waves
 // stream them into LDS with asynchronous global->LDS DMA, 16 bytes per lane, in two
-// parts: P1, what the compute waves read between barriers A and B, and P2, what they
-// read after B. With two buffers the part of a buffer a step has finished reading is
-// refilled for the chunk two steps ahead (P1 right after barrier B, P2 right after the
-// next A), so the copies run under the compute of the steps in between; with one buffer
-// (operand sets too large for two) each part is refilled for the next step as soon as it
-// is free. The backward producers also pull the operands of the chunk PFD steps ahead
+// parts, P1 and P2. With two buffers a chunk's whole operand set lands before the barrier
+// A that opens its step, the compute waves read all of it before barrier B (and form the
+// part of dS that does not depend on dDelta there), and the buffer is refilled for the
+// chunk two steps ahead right after B, so the copies run under the compute of the step in
+// between and no operand read is left between B and the next step. With one buffer
+// (operand sets too large for two) P1 is what the compute waves read between A and B and
+// P2 what they read after B, and each part is refilled for the next step as soon as it is
+// free. The backward producers also pull the operands of the chunk PFD steps ahead
 // into L2, with 4-byte DMAs (one cache line per lane) into a scratch word of LDS. In both
 // directions the NJ workgroups of a sequence, which share one XCD's L2, split the
 // prefetched lines between them.
@@ -232,31 +234,29 @@ constexpr int prefetch_count() { return (LINES + NJ * 64 * NP - 1) / (NJ * 64 * 
 template <bool DBUF, int N1, int N2, int NPF, class F1, class F2, class FP>
 __device__ __forceinline__ void produce(int NT, lds_char* b0, lds_char* b1, F1 P1, F2 P2, FP PF) {
     if (DBUF) {
+        // both parts of a chunk land before the barrier that opens its step, and the compute
+        // waves read all of a buffer before B_n, so the buffer of chunk n is refilled with
+        // chunk n + 2 right after B_n
         P1(0, b0);
         P2(0, b0);
         if (NT > 1) {
             P1(1, b1);
-            wait_vm<N1>();  // chunk 0 complete
+            P2(1, b1);
+            wait_vm<N1 + N2>();  // chunk 0 complete
         } else {
             wait_vm<0>();
         }
         for (int n = 0; n < NT; ++n) {
             lds_char* cur = (n & 1) ? b1 : b0;
-            lds_char* nxt = (n & 1) ? b0 : b1;
-            sync_lds();  // A_n: P1 of chunk n is in cur; step n - 1 is done with nxt's P2
-            if (n + 1 < NT) {
-                P2(n + 1, nxt);
-                PF(n + 1 + PFD);
-                wait_vm<N1 + N2 + NPF>();  // P2 of chunk n (older than P1(n + 1), P2(n + 1), PF)
-            } else {
-                wait_vm<0>();
-            }
-            sync_lds();  // B_n: step n is done with cur's P1
+            sync_lds();  // A_n: all of chunk n is in cur
+            PF(n + 1 + PFD);
+            sync_lds();  // B_n: step n is done with cur
             if (n + 2 < NT) {
                 P1(n + 2, cur);
-                wait_vm<N2 + NPF + N1>();  // P1 of chunk n + 1
-            } else if (n + 1 < NT) {
-                wait_vm<N2 + NPF>();
+                P2(n + 2, cur);
+                wait_vm<N1 + N2>();  // chunk n + 1 (and the prefetch) complete
+            } else {
+                wait_vm<0>();  // chunk n + 1, if any, and the prefetches complete
             }
         }
     } else {
@@ -706,7 +706,7 @@ __device__ __forceinline__ void bwd_flush(const Args& a, int s, int j, BwdPend<O
 // fragments of all waves are in the exchange and the chunk's P1 operands in buf).
 // Contains barrier B_n. SUM: a summary walk -- only the state gradient, no per-chunk
 // outputs. Exchange slots as in the forward.
-template <class OT, int DK, int DV, int NW, int NC, bool SUM>
+template <class OT, int DK, int DV, int NW, int NC, bool SUM, bool EARLY>
 __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4 (&dS0)[NC], f32x4 (&dS1)[NC],
                                          lds_char* stage, lds_char* xs, BwdPend<OT, NW, NC>& pd) {
     using B = BwdChainBuf<OT, DK, DV, NC>;
@@ -745,6 +745,24 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4 (&dS0
     }
     lds_get4<float>(buf + B::GC + (32 * wv + 4 * lq) * 4, g0);
     lds_get4<float>(buf + B::GC + (32 * wv + 16 + 4 * lq) * 4, g1);
+    // EARLY (double-buffered operands): the P2 operands are in the buffer already, so they are
+    // read here too, and the state-independent part of dS is formed before barrier B
+    FT QGf[2][2], WMf[2][2], Tf[TPW][2];
+    if constexpr (EARLY) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                QGf[h][kb] = lfrag_colk8<OT>(vQG, 32 * wv + 16 * h, 32 * kb);
+                WMf[h][kb] = lfrag_colk8<OT>(vWM, 32 * wv + 16 * h, 32 * kb);
+            }
+        if (!SUM) {
+#pragma unroll
+            for (int u = 0; u < TPW; ++u)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) Tf[u][kb] = lfrag_colk8<OT>(vT, 16 * (wv * TPW + u), 32 * kb);
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
     // dDelta = M^T dO + Kd dS' on this wave's token tiles, published for every wave
 #pragma unroll
@@ -760,40 +778,56 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4 (&dS0
             put_k8<OT>(xsD + ((t >> 1) * NC + ch) * FRAG, t & 1, dD);
         }
     }
-    sync_lds();  // B_n: all of dDelta is in the exchange; the P2 operands are in buf
-    FT dDB[2][NC], QGf[2][2], WMf[2][2], Tf[TPW][2];
+    // diag(exp gam_C) dS' + Qg^T dO on this wave's rows (the part of dS without dDelta)
+    f32x4 P0[NC], P1[NC];
+    auto state_part = [&]() {
+#pragma unroll
+        for (int ch = 0; ch < NC; ++ch) {
+            P0[ch] = f32x4{g0[0] * dS0[ch][0], g0[1] * dS0[ch][1], g0[2] * dS0[ch][2], g0[3] * dS0[ch][3]};
+            P1[ch] = f32x4{g1[0] * dS1[ch][0], g1[1] * dS1[ch][1], g1[2] * dS1[ch][2], g1[3] * dS1[ch][3]};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                mma(P0[ch], QGf[0][kb], dOB[kb][ch]);
+                mma(P1[ch], QGf[1][kb], dOB[kb][ch]);
+            }
+        }
+    };
+    if constexpr (EARLY) state_part();
+    sync_lds();  // B_n: all of dDelta is in the exchange (and, without EARLY, the P2 operands in buf)
+    FT dDB[2][NC];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int ch = 0; ch < NC; ++ch) dDB[kb][ch] = get_k8<OT>(xsD + (kb * NC + ch) * FRAG);
+        if constexpr (!EARLY) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {  // Qg^T and Wm^T rows (this wave's keys), K = token
-            QGf[h][kb] = lfrag_colk8<OT>(vQG, 32 * wv + 16 * h, 32 * kb);
-            WMf[h][kb] = lfrag_colk8<OT>(vWM, 32 * wv + 16 * h, 32 * kb);
+            for (int h = 0; h < 2; ++h) {  // Qg^T and Wm^T rows (this wave's keys), K = token
+                QGf[h][kb] = lfrag_colk8<OT>(vQG, 32 * wv + 16 * h, 32 * kb);
+                WMf[h][kb] = lfrag_colk8<OT>(vWM, 32 * wv + 16 * h, 32 * kb);
+            }
         }
     }
-    if (!SUM) {
+    if constexpr (!EARLY) {
+        if (!SUM) {
 #pragma unroll
-        for (int u = 0; u < TPW; ++u)
+            for (int u = 0; u < TPW; ++u)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) Tf[u][kb] = lfrag_colk8<OT>(vT, 16 * (wv * TPW + u), 32 * kb);
+                for (int kb = 0; kb < 2; ++kb) Tf[u][kb] = lfrag_colk8<OT>(vT, 16 * (wv * TPW + u), 32 * kb);
+        }
+        state_part();
     }
     // dS = diag(exp gam_C) dS' + Qg^T dO - Wm^T dDelta on this wave's rows, published for the
     // next step (every wave read the state-gradient fragments before B_n)
 #pragma unroll
     for (int ch = 0; ch < NC; ++ch) {
-        f32x4 p0 = {g0[0] * dS0[ch][0], g0[1] * dS0[ch][1], g0[2] * dS0[ch][2], g0[3] * dS0[ch][3]};
-        f32x4 p1 = {g1[0] * dS1[ch][0], g1[1] * dS1[ch][1], g1[2] * dS1[ch][2], g1[3] * dS1[ch][3]};
         f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = n0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             mma(n0, WMf[0][kb], dDB[kb][ch]);
             mma(n1, WMf[1][kb], dDB[kb][ch]);
-            mma(p0, QGf[0][kb], dOB[kb][ch]);
-            mma(p1, QGf[1][kb], dOB[kb][ch]);
         }
-        dS0[ch] = p0 - n0;
-        dS1[ch] = p1 - n1;
+        dS0[ch] = P0[ch] - n0;
+        dS1[ch] = P1[ch] - n1;
         put_k8<OT>(xsS + (wv * NC + ch) * FRAG, 0, dS0[ch]);
         put_k8<OT>(xsS + (wv * NC + ch) * FRAG, 1, dS1[ch]);
     }
@@ -911,7 +945,7 @@ __device__ __forceinline__ void bwd_walk(const Args& a, int s, int j, const Walk
     for (int n = 0; n < NT; ++n) {
         sync_lds();  // A_n
         bwd_flush<OT, DK, DV, NW, NC, NTS>(a, s, j, pd);
-        bwd_step<OT, DK, DV, NW, NC, SUM>(last - n, (DBUF && (n & 1)) ? b1 : b0, dS0, dS1, stage, xs, pd);
+        bwd_step<OT, DK, DV, NW, NC, SUM, DBUF>(last - n, (DBUF && (n & 1)) ? b1 : b0, dS0, dS1, stage, xs, pd);
     }
     bwd_flush<OT, DK, DV, NW, NC, NTS>(a, s, j, pd);
     if (w.end) {
