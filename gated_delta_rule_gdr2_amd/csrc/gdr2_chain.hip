@@ -30,10 +30,10 @@
 // transposed (K = token), which the LDS transposing reads provide, so the producer waves
 // stream them into LDS with asynchronous global->LDS DMA, 16 bytes per lane, in two
 // parts, P1 and P2. With two buffers a chunk's whole operand set lands before the barrier
-// A that opens its step, the compute waves read all of it before barrier B (and form the
-// part of dS that does not depend on dDelta there), and the buffer is refilled for the
-// chunk two steps ahead right after B, so the copies run under the compute of the step in
-// between and no operand read is left between B and the next step. With one buffer
+// A that opens its step, the compute waves read all of it before barrier B, and the
+// buffer is refilled for the chunk two steps ahead right after B, so the copies run under
+// the compute of the step in between and no operand read is left between B and the next
+// step. With one buffer
 // (operand sets too large for two) P1 is what the compute waves read between A and B and
 // P2 what they read after B, and each part is refilled for the next step as soon as it is
 // free. The backward producers also pull the operands of the chunk PFD steps ahead
@@ -746,7 +746,7 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4 (&dS0
     lds_get4<float>(buf + B::GC + (32 * wv + 4 * lq) * 4, g0);
     lds_get4<float>(buf + B::GC + (32 * wv + 16 + 4 * lq) * 4, g1);
     // EARLY (double-buffered operands): the P2 operands are in the buffer already, so they are
-    // read here too, and the state-independent part of dS is formed before barrier B
+    // read here too and no read of the buffer is left after barrier B
     FT QGf[2][2], WMf[2][2], Tf[TPW][2];
     if constexpr (EARLY) {
 #pragma unroll
@@ -792,7 +792,6 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4 (&dS0
             }
         }
     };
-    if constexpr (EARLY) state_part();
     sync_lds();  // B_n: all of dDelta is in the exchange (and, without EARLY, the P2 operands in buf)
     FT dDB[2][NC];
 #pragma unroll
@@ -814,8 +813,8 @@ __device__ __forceinline__ void bwd_step(int c, const lds_char* buf, f32x4 (&dS0
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) Tf[u][kb] = lfrag_colk8<OT>(vT, 16 * (wv * TPW + u), 32 * kb);
         }
-        state_part();
     }
+    state_part();
     // dS = diag(exp gam_C) dS' + Qg^T dO - Wm^T dDelta on this wave's rows, published for the
     // next step (every wave read the state-gradient fragments before B_n)
 #pragma unroll
